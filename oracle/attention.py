@@ -1,0 +1,181 @@
+"""fp64 materialised attention: forward (O, LSE) and analytic backward.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Sources, by page and section:
+
+* "Flex Attention and Triton, Supporting Long Context Training in SpecForge",
+  section *EAGLE3 Training*: attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V,
+  with the softmax taken in fp32 or better.
+* Same page, section *Flex Attention*: the EAGLE3 mask is the OR of a causal
+  part (query index minus a shift at least the key index, key index below the
+  batch's sequence length) and a suffix part (key index at least Q_LEN, key
+  index modulo Q_LEN below the sequence length, and key minus query index a
+  multiple of Q_LEN).  The mask does not depend on the head (H=1 broadcast) and
+  K/V heads are shared by groups of query heads (enable_gqa).
+* "Flash-attention training (the fused backward) - adoption playbook",
+  section *1. What exists*: the forward's saved state is O plus the per-row
+  logsumexp LSE; the backward produces dQ, dK, dV.  Section *6. Trap list*,
+  item 9: a query row with no allowed key has O = 0 and LSE = 0; item 8: a key
+  column no query may attend gets an exactly-zero gradient.
+* "CS336 - LLM Systems", *Flash Attention (Triton)* / *How it works*: the
+  fused kernel returns the same result as the explicit
+  Q K^T -> softmax -> P V chain; only memory traffic changes.
+
+Readings taken where the pages are silent (each listed in the design doc):
+  * scale defaults to 1/sqrt(D);
+  * LSE is the natural-log logsumexp of the *scaled* scores;
+  * CAUSAL with Sq != Skv is top-left aligned: key j allowed iff j <= i - shift;
+  * kv_valid[b] masks keys only, every query row is computed;
+  * GQA maps query head h to key/value head h // (Hq / Hkv).
+
+The backward is the gradient of  L = sum(O * dO)  (dO is the upstream
+gradient), derived from the softmax Jacobian:
+    dV = P^T dO,  dP = dO V^T,  Delta_i = sum_j P_ij dP_ij,
+    dS = P * (dP - Delta),  dQ = scale * dS K,  dK = scale * dS^T Q.
+"""
+import numpy as np
+
+FULL, CAUSAL, TTT = 0, 1, 2
+
+# Rows of S materialised at a time; only bounds RAM, never splits a row.
+_ROW_BLOCK = 1024
+
+
+def allowed(kind, Sq, Skv, shift=0, kv_valid=None, rows=None):
+    """Boolean [len(rows), Skv] matrix: may query i attend key j?
+
+    A literal transcription of the masks on the SpecForge page (*Flex
+    Attention* section): FULL is the padding mask alone, CAUSAL is the
+    ``causal_mask`` function, TTT is ``or_masks(causal_mask, suffix_mask)``
+    with Q_LEN = Sq.  ``kv_valid`` plays the role of ``seq_lengths[b]``.
+    """
+    i = (np.arange(Sq) if rows is None else np.asarray(rows))[:, None]
+    j = np.arange(Skv)[None, :]
+    n_valid = Skv if kv_valid is None else int(kv_valid)
+    padding = j < n_valid
+    if kind == FULL:
+        return np.broadcast_to(padding, (i.shape[0], Skv)).copy()
+    causal = (i - shift >= j) & padding
+    if kind == CAUSAL:
+        return causal
+    if kind == TTT:
+        q_len = Sq
+        suffix = (j >= q_len) & ((j % q_len) < n_valid) & (((j - i) % q_len) == 0)
+        return causal | suffix
+    raise ValueError(f"unknown mask kind {kind}")
+
+
+def allowed_pair_count(kind, Sq, Skv, shift=0, kv_valid=None):
+    """Number of allowed (i, j) pairs for one (batch, head): the unit in which
+    attention work is counted (4 D flop per pair forward, 10 D backward)."""
+    total = 0
+    for r0 in range(0, Sq, 4096):
+        rows = np.arange(r0, min(Sq, r0 + 4096))
+        total += int(allowed(kind, Sq, Skv, shift, kv_valid, rows).sum())
+    return total
+
+
+def _kv_valid_list(B, Skv, kv_valid):
+    if kv_valid is None:
+        return [Skv] * B
+    return [int(x) for x in np.asarray(kv_valid).reshape(-1)]
+
+
+def _check_shapes(q, k, v):
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    assert v.shape == k.shape and Bk == B and Dk == D
+    assert Hq % Hkv == 0, "GQA needs Hq to be a multiple of Hkv"
+    return B, Hq, Hkv, Sq, Skv, D
+
+
+def _row_softmax(S_masked):
+    """Softmax of masked score rows, plus the per-row natural logsumexp.
+
+    Rows with no allowed key give P = 0 and LSE = 0 (playbook trap 9).
+    """
+    nonempty = np.isfinite(S_masked).any(axis=1)
+    m = np.where(nonempty, S_masked.max(axis=1, initial=-np.inf), 0.0)
+    e = np.exp(S_masked - m[:, None])          # exp(-inf) = 0 for masked entries
+    e[~nonempty] = 0.0
+    z = e.sum(axis=1)
+    lse = np.where(nonempty, m + np.log(np.where(nonempty, z, 1.0)), 0.0)
+    P = np.where(nonempty[:, None], e / np.where(nonempty, z, 1.0)[:, None], 0.0)
+    return P, lse
+
+
+def attention_forward(q, k, v, kind=FULL, shift=0, kv_valid=None, scale=None,
+                      heads=None):
+    """O [B,Hq,Sq,D] and LSE [B,Hq,Sq] in float64.
+
+    ``heads`` optionally restricts the work to a list of query heads (the
+    other heads' outputs are left as NaN); used to time or check one GQA
+    group of a large configuration.
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
+    G = Hq // Hkv
+    s = 1.0 / np.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    kvv = _kv_valid_list(B, Skv, kv_valid)
+    hs = range(Hq) if heads is None else heads
+    O = np.full(q.shape, np.nan)
+    LSE = np.full((B, Hq, Sq), np.nan)
+    for b in range(B):
+        for r0 in range(0, Sq, _ROW_BLOCK):
+            rows = np.arange(r0, min(Sq, r0 + _ROW_BLOCK))
+            A = allowed(kind, Sq, Skv, shift, kvv[b], rows)
+            for h in hs:
+                g = h // G
+                S = s * (q[b, h, rows] @ k[b, g].T)
+                P, lse = _row_softmax(np.where(A, S, -np.inf))
+                O[b, h, rows] = P @ v[b, g]
+                LSE[b, h, rows] = lse
+    return O, LSE
+
+
+def attention_backward(q, k, v, do, kind=FULL, shift=0, kv_valid=None,
+                       scale=None, heads=None):
+    """dQ, dK, dV (float64) of L = sum(O * dO), plus Delta [B,Hq,Sq].
+
+    P is rebuilt from the scores, exactly as the definition states; dK and dV
+    of a key/value head sum the contributions of every query head in its
+    group.  With ``heads`` only those query heads contribute (to dK/dV as
+    well), and the other heads' dQ rows are NaN.
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
+    G = Hq // Hkv
+    s = 1.0 / np.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    kvv = _kv_valid_list(B, Skv, kv_valid)
+    hs = range(Hq) if heads is None else heads
+    dQ = np.full(q.shape, np.nan)
+    dK = np.zeros(k.shape)
+    dV = np.zeros(v.shape)
+    Delta = np.full((B, Hq, Sq), np.nan)
+    for b in range(B):
+        for r0 in range(0, Sq, _ROW_BLOCK):
+            rows = np.arange(r0, min(Sq, r0 + _ROW_BLOCK))
+            A = allowed(kind, Sq, Skv, shift, kvv[b], rows)
+            for h in hs:
+                g = h // G
+                S = s * (q[b, h, rows] @ k[b, g].T)
+                P, _ = _row_softmax(np.where(A, S, -np.inf))
+                dO = do[b, h, rows]
+                dV[b, g] += P.T @ dO
+                dP = dO @ v[b, g].T
+                delta = (P * dP).sum(axis=1)
+                dS = P * (dP - delta[:, None])
+                dQ[b, h, rows] = s * (dS @ k[b, g])
+                dK[b, g] += s * (dS.T @ q[b, h, rows])
+                Delta[b, h, rows] = delta
+    return dQ, dK, dV, Delta
+
+
+def attention_ref(q, k, v, do, kind=FULL, shift=0, kv_valid=None, scale=None,
+                  heads=None):
+    """Forward and backward together: dict with O, LSE, dQ, dK, dV, Delta."""
+    O, LSE = attention_forward(q, k, v, kind, shift, kv_valid, scale, heads)
+    dQ, dK, dV, Delta = attention_backward(q, k, v, do, kind, shift, kv_valid,
+                                           scale, heads)
+    return dict(O=O, LSE=LSE, dQ=dQ, dK=dK, dV=dV, Delta=Delta)

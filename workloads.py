@@ -1,0 +1,111 @@
+"""Seeded synthetic inputs and the named workloads of the attention path.
+
+Holds no attention arithmetic: it only names shapes and draws the random
+tensors that both the oracle (``oracle/``) and the HIP library are fed.
+
+Recipe (the same for every workload): ``torch.Generator('cpu')`` seeded with
+``seed`` draws Q, K, V, dO in that order with ``torch.randn`` in float32
+(i.i.d. N(0, 1)); bf16 workloads then round each to bfloat16 (round to
+nearest even).  The oracle receives exactly these values upcast to float64,
+so input rounding is never counted as kernel error.
+
+Shapes follow the pages' own workloads:
+  * tiny fp32 causal / full self-attention (a correctness case);
+  * the batch-8 d_model x seq_len grid of the CS336 Triton benchmark
+    (head count 16 and causal masking are this library's choice; the page
+    states neither);
+  * long-context (16K / 32K) GQA causal attention, the SpecForge setting;
+  * the EAGLE3 TTT call at draft step t = 2 (keys/values of steps 0, 1, 2
+    concatenated, Skv = 3 * Sq);
+  * diffusion-transformer full self-attention and cross-attention with padded
+    keys (1000 valid of 1024), the ggml playbook's real geometries.
+"""
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import torch
+
+FULL, CAUSAL, TTT = 0, 1, 2
+KIND_NAMES = {FULL: "full", CAUSAL: "causal", TTT: "ttt"}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Skv: int
+    D: int
+    kind: int
+    dtype: str = "bf16"            # "bf16" or "f32"
+    shift: int = 0
+    kv_valid: Optional[tuple] = None   # per-batch valid key count, None = all
+    scale: Optional[float] = None      # None -> 1/sqrt(D)
+
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def with_(self, **kw):
+        return replace(self, **kw)
+
+
+def tiny_fp32(kind=CAUSAL):
+    return Workload(f"tiny_fp32_{KIND_NAMES[kind]}", 1, 2, 2, 128, 128, 64,
+                    kind, dtype="f32")
+
+
+def grid(D, S):
+    return Workload(f"grid_D{D}_S{S}", 8, 16, 16, S, S, D, CAUSAL)
+
+
+def long_gqa(S=16384):
+    return Workload(f"long_gqa_S{S}", 1, 32, 4, S, S, 128, CAUSAL)
+
+
+def ttt(S=16384, step=2, shift=0):
+    return Workload(f"ttt_S{S}_t{step}", 1, 32, 4, S, (step + 1) * S, 128,
+                    TTT, shift=shift)
+
+
+def dit_self():
+    return Workload("dit_self_S8192", 2, 16, 16, 8192, 8192, 64, FULL)
+
+
+def dit_cross():
+    return Workload("dit_cross_S8192_kv1000of1024", 2, 16, 16, 8192, 1024, 64,
+                    FULL, kv_valid=(1000, 1000))
+
+
+HEADLINE = long_gqa(16384)
+
+
+def all_workloads():
+    ws = [tiny_fp32(CAUSAL), tiny_fp32(FULL)]
+    ws += [grid(D, S) for D in (16, 32, 64) for S in (256, 1024, 4096)]
+    ws += [long_gqa(16384), long_gqa(32768), ttt(16384, 2), dit_self(),
+           dit_cross()]
+    return ws
+
+
+def make_inputs(w: Workload, seed: int = 0, device="cpu"):
+    """Q, K, V, dO as [B, H, S, D] tensors of the workload's dtype.
+
+    Drawn on the CPU generator (so every device sees identical values), then
+    moved to ``device``.
+    """
+    g = torch.Generator("cpu").manual_seed(seed)
+    shapes = [(w.B, w.Hq, w.Sq, w.D), (w.B, w.Hkv, w.Skv, w.D),
+              (w.B, w.Hkv, w.Skv, w.D), (w.B, w.Hq, w.Sq, w.D)]
+    out = []
+    for shp in shapes:
+        x = torch.randn(shp, generator=g, dtype=torch.float32)
+        out.append(x.to(w.torch_dtype()).to(device))
+    return tuple(out)
+
+
+def kv_valid_tensor(w: Workload, device="cpu"):
+    if w.kv_valid is None:
+        return None
+    return torch.tensor(list(w.kv_valid), dtype=torch.int32, device=device)
