@@ -1,0 +1,173 @@
+"""MI355X (gfx950) fused training attention: forward, backward, autograd.
+
+Thin Python binding over ``libfa.so`` (include/fa.h).  Every step of the
+computation runs in the library's HIP kernels; PyTorch only provides device
+memory and the current stream.  The functions mirror the C entry points:
+
+    fa_fwd(q, k, v, ...)                     -> (o, lse)
+    fa_bwd(q, k, v, o, lse, dout, ...)       -> (dq, dk, dv)
+    fa_bwd_workspace_bytes(q, k, ...)        -> int
+    fa_last_error()                          -> str
+
+and ``attention(q, k, v, ...)`` is a drop-in ``torch.autograd.Function``
+that saves (O, LSE) for the backward.
+
+Tensors are logical [B, H, S, D] (any strides with unit stride in D): q is
+[B, Hq, Sq, D], k and v are [B, Hkv, Skv, D] with Hq a multiple of Hkv.
+Mask kinds: ``FULL``, ``CAUSAL`` (key j <= query i - causal_shift) and
+``TTT`` (EAGLE3 training-time test: Skv = n * Sq, causal over the step-0 keys
+plus the key at the query's own position in each later step).  ``kv_valid``
+is an optional int32 device tensor [B] of valid key counts.
+"""
+import math
+
+import torch
+
+from . import _lib
+from ._lib import (FAError, FA_BF16, FA_F32, FA_MASK_FULL, FA_MASK_CAUSAL,  # noqa: F401
+                   FA_MASK_TTT)
+
+FULL, CAUSAL, TTT = FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_TTT
+
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_last_error",
+           "attention", "FAError", "FULL", "CAUSAL", "TTT"]
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise FAError(_lib.FA_ERR_UNSUPPORTED, f"dtype {t.dtype} (expected bfloat16 or float32)")
+
+
+def _tensor(t):
+    if t.dim() != 4:
+        raise FAError(_lib.FA_ERR_INVALID_ARG, f"expected a 4-d [B, H, S, D] tensor, got {tuple(t.shape)}")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise FAError(_lib.FA_ERR_INVALID_ARG, "the D dimension must have unit stride")
+    return _lib.fa_tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _mask(kind, causal_shift, kv_valid):
+    ptr = None
+    if kv_valid is not None:
+        if kv_valid.dtype != torch.int32 or not kv_valid.is_contiguous():
+            raise FAError(_lib.FA_ERR_INVALID_ARG, "kv_valid must be a contiguous int32 tensor")
+        ptr = kv_valid.data_ptr()
+    return _lib.fa_mask_desc(int(kind), int(causal_shift), ptr)
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if t.is_cuda:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _shape(q, k):
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    return int(B), int(Hq), int(Hkv), int(Sq), int(Skv), int(D)
+
+
+def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None,
+           out=None, lse=None, stream=None):
+    """Forward attention.  Returns (O [B,Hq,Sq,D] in q's dtype, LSE [B,Hq,Sq] fp32)."""
+    B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    a = _lib.fa_fwd_args()
+    a.dtype = _dtype_code(q)
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
+    a.scale = 0.0 if scale is None else float(scale)
+    a.q, a.k, a.v, a.o = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
+    a.lse = lse.data_ptr()
+    a.mask = _mask(mask_kind, causal_shift, kv_valid)
+    for t in (k, v, out):
+        if t.dtype != q.dtype:
+            raise FAError(_lib.FA_ERR_INVALID_ARG, "q, k, v and out must share one dtype")
+    _lib.check(_lib.lib().fa_fwd(a, _stream(q, stream)))
+    return out, lse
+
+
+def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale):
+    B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
+    a = _lib.fa_bwd_args()
+    a.dtype = _dtype_code(q)
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
+    a.scale = 0.0 if scale is None else float(scale)
+    a.q, a.k, a.v, a.o, a.dout = (_tensor(t) for t in (q, k, v, o, dout))
+    a.lse = None if lse is None else lse.data_ptr()
+    if dq is not None:
+        a.dq, a.dk, a.dv = _tensor(dq), _tensor(dk), _tensor(dv)
+    a.mask = _mask(mask_kind, causal_shift, kv_valid)
+    return a
+
+
+def fa_bwd_workspace_bytes(q, k, *, mask_kind=FULL):
+    """Scratch bytes fa_bwd needs for these shapes (linear in Sq)."""
+    a = _lib.fa_bwd_args()
+    B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
+    a.dtype = _dtype_code(q)
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
+    a.mask = _lib.fa_mask_desc(int(mask_kind), 0, None)
+    return int(_lib.lib().fa_bwd_workspace_bytes(a))
+
+
+def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=None,
+           scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward attention.  Returns (dQ, dK, dV) in q's dtype."""
+    if dq is None:
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if dk is None:
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    if dv is None:
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale)
+    need = int(_lib.lib().fa_bwd_workspace_bytes(a))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr()
+    _lib.check(_lib.lib().fa_bwd(a, ws_ptr, workspace.numel() * workspace.element_size(),
+                                 _stream(q, stream)))
+    return dq, dk, dv
+
+
+def fa_last_error():
+    return _lib.last_error()
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, mask_kind, causal_shift, kv_valid, scale):
+        o, lse = fa_fwd(q, k, v, mask_kind=mask_kind, causal_shift=causal_shift,
+                        kv_valid=kv_valid, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.cfg = (mask_kind, causal_shift, kv_valid, scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        mask_kind, causal_shift, kv_valid, scale = ctx.cfg
+        if do.stride(-1) != 1:
+            do = do.contiguous()
+        dq, dk, dv = fa_bwd(q, k, v, o, lse, do, mask_kind=mask_kind,
+                            causal_shift=causal_shift, kv_valid=kv_valid, scale=scale)
+        return dq, dk, dv, None, None, None, None
+
+
+def attention(q, k, v, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None):
+    """Fused attention O = softmax(scale q k^T + mask) v, differentiable.
+
+    ``scale`` defaults to 1/sqrt(D).  Saves only O and LSE for the backward.
+    """
+    return _Attention.apply(q, k, v, mask_kind, causal_shift, kv_valid, scale)
+
+
+def default_scale(D):
+    return 1.0 / math.sqrt(D)

@@ -1,0 +1,260 @@
+// fa_api.cpp - the C ABI: argument validation, dispatch, error text.
+//
+// Everything is validated before the first launch; a failing call launches
+// nothing.  There is no fallback path: an unsupported request is an error
+// (the ggml flash-attn-training playbook, section 2, item 2, explains why a
+// silent fallback is worse than a hard error).
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_error;
+
+fa_status fail(fa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return s;
+}
+
+struct Shape {
+  int dtype, B, Hq, Hkv, Sq, Skv, D;
+};
+
+int elem_bytes(int dtype) { return dtype == FA_BF16 ? 2 : 4; }
+
+// Byte range [lo, hi) spanned by a [n0, n1, n2, D] strided tensor.
+struct Range {
+  uintptr_t lo, hi;
+  bool empty;
+};
+
+Range span(const fa_tensor& t, int n0, int n1, int n2, int D, int eb) {
+  Range r{0, 0, true};
+  if (n0 <= 0 || n1 <= 0 || n2 <= 0 || D <= 0) return r;
+  int64_t lo = 0, hi = 0;
+  const int64_t st[3] = {t.stride_b, t.stride_h, t.stride_s};
+  const int64_t n[3] = {n0, n1, n2};
+  for (int i = 0; i < 3; ++i) {
+    int64_t ext = st[i] * (n[i] - 1);
+    if (ext < 0) lo += ext; else hi += ext;
+  }
+  hi += D;
+  r.lo = reinterpret_cast<uintptr_t>(t.data) + lo * eb;
+  r.hi = reinterpret_cast<uintptr_t>(t.data) + hi * eb;
+  r.empty = false;
+  return r;
+}
+
+bool overlap(const Range& a, const Range& b) {
+  return !a.empty && !b.empty && a.lo < b.hi && b.lo < a.hi;
+}
+
+fa_status check_shape(const Shape& s, const fa_mask_desc& m) {
+  if (s.dtype != FA_BF16 && s.dtype != FA_F32)
+    return fail(FA_ERR_UNSUPPORTED, "unknown dtype %d (expected FA_BF16=0 or FA_F32=1)", s.dtype);
+  if (s.B < 0 || s.Sq < 0 || s.Skv < 0)
+    return fail(FA_ERR_INVALID_ARG, "negative size: B=%d Sq=%d Skv=%d", s.B, s.Sq, s.Skv);
+  if (s.Hq <= 0 || s.Hkv <= 0 || s.D <= 0)
+    return fail(FA_ERR_INVALID_ARG, "non-positive size: Hq=%d Hkv=%d D=%d", s.Hq, s.Hkv, s.D);
+  if (s.Hq % s.Hkv != 0)
+    return fail(FA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", s.Hq, s.Hkv);
+  if (s.D != 16 && s.D != 32 && s.D != 64 && s.D != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dim D=%d not in {16, 32, 64, 128}", s.D);
+  if (m.kind != FA_MASK_FULL && m.kind != FA_MASK_CAUSAL && m.kind != FA_MASK_TTT)
+    return fail(FA_ERR_UNSUPPORTED, "unknown mask kind %d", m.kind);
+  if (m.causal_shift < 0)
+    return fail(FA_ERR_INVALID_ARG, "negative causal_shift %d", m.causal_shift);
+  if (m.kind == FA_MASK_TTT) {
+    if (s.Sq <= 0 && s.Skv != 0)
+      return fail(FA_ERR_INVALID_ARG, "TTT mask needs Sq > 0 (Sq is the step length)");
+    if (s.Sq > 0 && s.Skv % s.Sq != 0)
+      return fail(FA_ERR_INVALID_ARG, "TTT mask needs Skv (%d) to be a multiple of Sq (%d)", s.Skv, s.Sq);
+  }
+  return FA_OK;
+}
+
+// Checks one tensor: non-null data (when non-empty), 16-byte alignment of the
+// base pointer and of every outer stride, and, for outputs, that no two
+// elements share an address.
+fa_status check_tensor(const char* name, const fa_tensor& t, int n0, int n1, int n2,
+                       int D, int eb, bool output) {
+  if (n0 == 0 || n2 == 0) return FA_OK;  // empty: never touched
+  if (t.data == nullptr) return fail(FA_ERR_INVALID_ARG, "%s: NULL data pointer", name);
+  if (reinterpret_cast<uintptr_t>(t.data) % 16 != 0)
+    return fail(FA_ERR_ALIGNMENT, "%s: base pointer %p is not 16-byte aligned", name, t.data);
+  const int64_t st[3] = {t.stride_b, t.stride_h, t.stride_s};
+  const int64_t n[3] = {n0, n1, n2};
+  for (int i = 0; i < 3; ++i) {
+    if (n[i] > 1 && (st[i] * eb) % 16 != 0)
+      return fail(FA_ERR_ALIGNMENT, "%s: stride %d (%lld elements) is not a multiple of 16 bytes",
+                  name, i, (long long)st[i]);
+  }
+  if (output) {
+    // No self-overlap: sort the outer dims by |stride|; each stride must
+    // cover the extent of everything below it.
+    struct Dim { int64_t n, st; };
+    Dim dims[3] = {{n[0], st[0]}, {n[1], st[1]}, {n[2], st[2]}};
+    std::sort(dims, dims + 3, [](const Dim& a, const Dim& b) {
+      return std::llabs(a.st) < std::llabs(b.st);
+    });
+    int64_t extent = D;
+    for (const Dim& d : dims) {
+      if (d.n <= 1) continue;
+      if (std::llabs(d.st) < extent)
+        return fail(FA_ERR_INVALID_ARG, "%s: output strides overlap (stride %lld < extent %lld)",
+                    name, (long long)d.st, (long long)extent);
+      extent = std::llabs(d.st) * d.n;
+    }
+  }
+  return FA_OK;
+}
+
+fa_status check_device() {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n <= 0)
+    return fail(FA_ERR_HIP, "no HIP device available (%s)",
+                e != hipSuccess ? hipGetErrorString(e) : "device count is 0");
+  return FA_OK;
+}
+
+fa::Tensor tensor(const fa_tensor& t) { return {t.data, t.stride_b, t.stride_h, t.stride_s}; }
+
+void fill_common(fa::Params& p, const Shape& s, float scale, const fa_mask_desc& m) {
+  p.B = s.B; p.Hq = s.Hq; p.Hkv = s.Hkv; p.G = s.Hq / s.Hkv;
+  p.Sq = s.Sq; p.Skv = s.Skv; p.D = s.D;
+  p.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)s.D);
+  p.scale_log2 = p.scale * 1.4426950408889634f;
+  p.mask.kind = m.kind;
+  p.mask.shift = m.causal_shift;
+  p.mask.kv_valid = m.kv_valid;
+}
+
+size_t delta_bytes(const Shape& s) {
+  size_t n = (size_t)std::max(s.B, 0) * (size_t)std::max(s.Hq, 0) * (size_t)std::max(s.Sq, 0) * 4;
+  return (n + 255) / 256 * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_last_error(void) { return g_error.c_str(); }
+
+fa_status fa_fwd(const fa_fwd_args* a, hipStream_t stream) {
+  if (!a) return fail(FA_ERR_INVALID_ARG, "fa_fwd: args is NULL");
+  Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
+  fa_status st = check_shape(s, a->mask);
+  if (st != FA_OK) return st;
+  const int eb = elem_bytes(s.dtype);
+  if ((st = check_tensor("q", a->q, s.B, s.Hq, s.Sq, s.D, eb, false))) return st;
+  if ((st = check_tensor("k", a->k, s.B, s.Hkv, s.Skv, s.D, eb, false))) return st;
+  if ((st = check_tensor("v", a->v, s.B, s.Hkv, s.Skv, s.D, eb, false))) return st;
+  if ((st = check_tensor("o", a->o, s.B, s.Hq, s.Sq, s.D, eb, true))) return st;
+  const bool rows = s.B > 0 && s.Sq > 0;
+  if (rows && a->lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse: NULL pointer");
+  if (rows && reinterpret_cast<uintptr_t>(a->lse) % 4 != 0)
+    return fail(FA_ERR_ALIGNMENT, "lse: pointer is not 4-byte aligned");
+  // outputs must not overlap inputs or each other
+  Range rq = span(a->q, s.B, s.Hq, s.Sq, s.D, eb), rk = span(a->k, s.B, s.Hkv, s.Skv, s.D, eb),
+        rv = span(a->v, s.B, s.Hkv, s.Skv, s.D, eb), ro = span(a->o, s.B, s.Hq, s.Sq, s.D, eb);
+  Range rl{reinterpret_cast<uintptr_t>(a->lse),
+           reinterpret_cast<uintptr_t>(a->lse) + (size_t)s.B * s.Hq * s.Sq * 4, !rows};
+  for (const Range* in : {&rq, &rk, &rv}) {
+    if (overlap(ro, *in)) return fail(FA_ERR_ALIAS, "o overlaps an input tensor");
+    if (overlap(rl, *in)) return fail(FA_ERR_ALIAS, "lse overlaps an input tensor");
+  }
+  if (overlap(ro, rl)) return fail(FA_ERR_ALIAS, "o overlaps lse");
+  if (a->mask.kv_valid && reinterpret_cast<uintptr_t>(a->mask.kv_valid) % 4 != 0)
+    return fail(FA_ERR_ALIGNMENT, "kv_valid: pointer is not 4-byte aligned");
+  if (!rows) return FA_OK;  // nothing to compute
+  if ((st = check_device())) return st;
+
+  fa::Params p{};
+  fill_common(p, s, a->scale, a->mask);
+  p.q = tensor(a->q); p.k = tensor(a->k); p.v = tensor(a->v); p.o = tensor(a->o);
+  p.lse = a->lse;
+  hipError_t e = s.dtype == FA_BF16 ? fa::launch_fwd_bf16(p, stream) : fa::launch_fwd_f32(p, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+size_t fa_bwd_workspace_bytes(const fa_bwd_args* a) {
+  if (!a) return 0;
+  Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
+  return delta_bytes(s);
+}
+
+fa_status fa_bwd(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!a) return fail(FA_ERR_INVALID_ARG, "fa_bwd: args is NULL");
+  Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
+  fa_status st = check_shape(s, a->mask);
+  if (st != FA_OK) return st;
+  const int eb = elem_bytes(s.dtype);
+  if ((st = check_tensor("q", a->q, s.B, s.Hq, s.Sq, s.D, eb, false))) return st;
+  if ((st = check_tensor("k", a->k, s.B, s.Hkv, s.Skv, s.D, eb, false))) return st;
+  if ((st = check_tensor("v", a->v, s.B, s.Hkv, s.Skv, s.D, eb, false))) return st;
+  if ((st = check_tensor("o", a->o, s.B, s.Hq, s.Sq, s.D, eb, false))) return st;
+  if ((st = check_tensor("dout", a->dout, s.B, s.Hq, s.Sq, s.D, eb, false))) return st;
+  if ((st = check_tensor("dq", a->dq, s.B, s.Hq, s.Sq, s.D, eb, true))) return st;
+  if ((st = check_tensor("dk", a->dk, s.B, s.Hkv, s.Skv, s.D, eb, true))) return st;
+  if ((st = check_tensor("dv", a->dv, s.B, s.Hkv, s.Skv, s.D, eb, true))) return st;
+  const bool rows = s.B > 0 && s.Sq > 0;
+  if (rows && a->lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse: NULL pointer");
+  if (rows && reinterpret_cast<uintptr_t>(a->lse) % 4 != 0)
+    return fail(FA_ERR_ALIGNMENT, "lse: pointer is not 4-byte aligned");
+  const size_t need = delta_bytes(s);
+  if (need > 0) {
+    if (ws == nullptr) return fail(FA_ERR_INVALID_ARG, "workspace: NULL pointer (%zu bytes needed)", need);
+    if (ws_bytes < need)
+      return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+      return fail(FA_ERR_ALIGNMENT, "workspace pointer %p is not 256-byte aligned", ws);
+  }
+  if (a->mask.kv_valid && reinterpret_cast<uintptr_t>(a->mask.kv_valid) % 4 != 0)
+    return fail(FA_ERR_ALIGNMENT, "kv_valid: pointer is not 4-byte aligned");
+
+  Range in[7] = {span(a->q, s.B, s.Hq, s.Sq, s.D, eb), span(a->k, s.B, s.Hkv, s.Skv, s.D, eb),
+                 span(a->v, s.B, s.Hkv, s.Skv, s.D, eb), span(a->o, s.B, s.Hq, s.Sq, s.D, eb),
+                 span(a->dout, s.B, s.Hq, s.Sq, s.D, eb),
+                 {reinterpret_cast<uintptr_t>(a->lse),
+                  reinterpret_cast<uintptr_t>(a->lse) + (size_t)s.B * s.Hq * s.Sq * 4, !rows},
+                 {0, 0, true}};
+  Range out[4] = {span(a->dq, s.B, s.Hq, s.Sq, s.D, eb), span(a->dk, s.B, s.Hkv, s.Skv, s.D, eb),
+                  span(a->dv, s.B, s.Hkv, s.Skv, s.D, eb),
+                  {reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + need, need == 0}};
+  const char* out_names[4] = {"dq", "dk", "dv", "workspace"};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(out[i], in[j])) return fail(FA_ERR_ALIAS, "%s overlaps an input tensor", out_names[i]);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out[j]))
+        return fail(FA_ERR_ALIAS, "%s overlaps %s", out_names[i], out_names[j]);
+  }
+  const bool keys = s.B > 0 && s.Skv > 0;
+  if (!rows && !keys) return FA_OK;
+  if ((st = check_device())) return st;
+
+  fa::Params p{};
+  fill_common(p, s, a->scale, a->mask);
+  p.q = tensor(a->q); p.k = tensor(a->k); p.v = tensor(a->v); p.o = tensor(a->o);
+  p.dout = tensor(a->dout); p.dq = tensor(a->dq); p.dk = tensor(a->dk); p.dv = tensor(a->dv);
+  p.lse_in = a->lse;
+  p.delta = static_cast<float*>(ws);
+  hipError_t e = s.dtype == FA_BF16 ? fa::launch_bwd_bf16(p, stream) : fa::launch_bwd_f32(p, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_bwd launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+}  // extern "C"

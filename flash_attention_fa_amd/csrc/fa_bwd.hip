@@ -1,0 +1,546 @@
+// fa_bwd.hip - bf16 backward attention for gfx950 (MFMA 32x32x16).
+//
+// Gradient of L = sum(O * dO) through O = softmax(s Q K^T + mask) V, with P
+// rebuilt from the saved LSE instead of being stored (CS336 "Flash Attention
+// (Triton)": the backward recomputes the weights from the logsumexp; the
+// ggml flash-attn-training playbook, section 1: a fused backward that is
+// bitwise deterministic, no floating-point atomics, fixed schedules):
+//   Delta_i = sum_d dO_id O_id                      (delta_kernel)
+//   P_ij    = exp(s q_i.k_j - LSE_i)  on allowed pairs, else 0
+//   dP_ij   = dO_i . v_j,   dS_ij = P_ij (dP_ij - Delta_i)
+//   dV_j    = sum_i P_ij dO_i                        (dkdv_kernel)
+//   dK_j    = s sum_i dS_ij q_i                      (dkdv_kernel)
+//   dQ_i    = s sum_j dS_ij k_j                      (dq_kernel)
+// dK/dV are owned by key tiles and dQ by query tiles, so every output element
+// is summed by exactly one workgroup in a fixed order: reruns are bitwise
+// identical.  Keys no query may attend get exact zeros.
+#include "fa_device.h"
+
+namespace fa {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Delta = rowsum(dO * O), fp32.  D/8 lanes per row, 16-byte loads.
+template <int D>
+__global__ void __launch_bounds__(256) delta_kernel(Params p) {
+  constexpr int LPR = D / 8;        // lanes per row
+  constexpr int RPB = 256 / LPR;    // rows per block
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (r < rows) {
+    const int i = (int)(r % p.Sq);
+    const int64_t bh = r / p.Sq;
+    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.o.ptr) + b * p.o.sb +
+                                                      h * p.o.sh + (int64_t)i * p.o.ss + 8 * c);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb +
+                                                      h * p.dout.sh + (int64_t)i * p.dout.ss + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)o[e] * (float)g[e];
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (r < rows && c == 0) p.delta[r] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: a workgroup owns NW*QB*32 query rows of one (batch, head) and streams
+// key tiles through LDS (as in the forward).  Transposed scores again: lane =
+// query column, so LSE and Delta are one scalar per lane.
+constexpr int DQ_TK = 64;
+
+template <int D>
+struct DqLds {
+  static constexpr int KSTR = D + 8;
+  static constexpr int VSTR = D + 8;
+  static constexpr int KTILE = DQ_TK * KSTR;
+  static constexpr int VTILE = DQ_TK * VSTR;
+  static constexpr int BYTES = 2 * (KTILE + VTILE) * 2;
+};
+
+template <int D, int QB, int NW>
+__global__ void __launch_bounds__(NW * 64)
+dq_kernel(Params p) {
+  constexpr int NT = NW * 64;
+  constexpr int TQ = NW * QB * 32;
+  constexpr int TK = DQ_TK;
+  constexpr int DC = D / 8;
+  constexpr int CHUNKS = TK * DC;
+  constexpr int PER_T = (CHUNKS + NT - 1) / NT;
+  constexpr int NDB = D >= 32 ? D / 32 : 1;
+  constexpr int NJ = D / 16;
+  using L = DqLds<D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* Ks = reinterpret_cast<bf16*>(smem);
+  bf16* Vs = Ks + 2 * L::KTILE;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int nq = (p.Sq + TQ - 1) / TQ;
+  int col, rank;
+  map_block(blockIdx.x, p.B * p.Hq, nq, col, rank);
+  const int b = col / p.Hq, h = col % p.Hq, hk = h / p.G;
+  const int qtile = p.mask.kind == MASK_FULL ? rank : nq - 1 - rank;
+  const MaskB m = resolve_mask(p, b);
+  const int qa = qtile * TQ, qb = min(p.Sq, qa + TQ);
+  const int wa = qa + wave * QB * 32, wb = min(p.Sq, wa + QB * 32);
+
+  const bf16* Qg = static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
+  const bf16* Gg = static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh;
+  const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
+  const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
+  const int64_t rowbase = ((int64_t)b * p.Hq + h) * p.Sq;
+
+  bf16x8 qreg[QB][NJ], greg[QB][NJ];
+  float lse2[QB], dlt[QB];
+#pragma unroll
+  for (int qb_ = 0; qb_ < QB; ++qb_) {
+    const int row = wa + qb_ * 32 + l32;
+    const bool ok = row < p.Sq;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      qreg[qb_][j] = ok ? *reinterpret_cast<const bf16x8*>(Qg + (int64_t)row * p.q.ss + 16 * j + 8 * hh)
+                        : bf16x8{};
+      greg[qb_][j] = ok ? *reinterpret_cast<const bf16x8*>(Gg + (int64_t)row * p.dout.ss + 16 * j + 8 * hh)
+                        : bf16x8{};
+    }
+    lse2[qb_] = ok ? p.lse_in[rowbase + row] * 1.4426950408889634f : 0.f;
+    dlt[qb_] = ok ? p.delta[rowbase + row] : 0.f;
+  }
+
+  f32x16 acc[QB][NDB];
+#pragma unroll
+  for (int qb_ = 0; qb_ < QB; ++qb_)
+#pragma unroll
+    for (int c = 0; c < NDB; ++c) acc[qb_][c] = f32x16{};
+
+  i32x4 kst[PER_T], vst[PER_T];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int c = tid + i * NT;
+      const int r = c / DC, c8 = c % DC;
+      const int key = t * TK + r;
+      if (c < CHUNKS && key_valid(m, key)) {
+        kst[i] = *reinterpret_cast<const i32x4*>(Kg + (int64_t)key * p.k.ss + 8 * c8);
+        vst[i] = *reinterpret_cast<const i32x4*>(Vg + (int64_t)key * p.v.ss + 8 * c8);
+      } else {
+        kst[i] = i32x4{};
+        vst[i] = i32x4{};
+      }
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int c = tid + i * NT;
+      if (c < CHUNKS) {
+        const int r = c / DC, c8 = c % DC;
+        lds_write16(Ks + buf * L::KTILE + r * L::KSTR + 8 * c8, kst[i]);
+        lds_write16(Vs + buf * L::VTILE + r * L::VSTR + 8 * c8, vst[i]);
+      }
+    }
+  };
+
+  TileWalk walk;
+  walk.start(m, qa, qb, TK);
+  int buf = 0;
+  if (walk.valid()) {
+    fetch(walk.t);
+    store(0);
+  }
+  __syncthreads();
+
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const bool d_lane_ok = D >= 32 || ((lane >> 4) & 1) == 0;
+
+  while (walk.valid()) {
+    const int t = walk.t;
+    TileWalk nxt = walk;
+    nxt.next(m, qa, qb, TK);
+    if (nxt.valid()) fetch(nxt.t);
+
+    const int k0 = t * TK;
+    const int state = tile_state(m, k0, TK, wa, wb);
+    if (state != TILE_SKIP) {
+      const bf16* Kt = Ks + buf * L::KTILE;
+      const bf16* Vt = Vs + buf * L::VTILE;
+      f32x16 s[QB][2], dp[QB][2];
+#pragma unroll
+      for (int qb_ = 0; qb_ < QB; ++qb_)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) { s[qb_][kb] = f32x16{}; dp[qb_][kb] = f32x16{}; }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 ak = lds_read8(Kt + (32 * kb + l32) * L::KSTR + 16 * j + 8 * hh);
+          const bf16x8 av = lds_read8(Vt + (32 * kb + l32) * L::VSTR + 16 * j + 8 * hh);
+#pragma unroll
+          for (int qb_ = 0; qb_ < QB; ++qb_) {
+            s[qb_][kb] = mfma32(ak, qreg[qb_][j], s[qb_][kb]);
+            dp[qb_][kb] = mfma32(av, greg[qb_][j], dp[qb_][kb]);
+          }
+        }
+      if (state == TILE_PART) {
+#pragma unroll
+        for (int qb_ = 0; qb_ < QB; ++qb_) {
+          const int qi = wa + qb_ * 32 + l32;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
+              if (!allowed(m, qi, key)) s[qb_][kb][i] = -INFINITY;
+            }
+        }
+      }
+      // dS^T = P^T (dP^T - Delta), rounded to bf16 for the dS K product.
+      bf16x8 dsb[QB][2][2];
+#pragma unroll
+      for (int qb_ = 0; qb_ < QB; ++qb_)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            float e[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int i = 8 * st + u;
+              const float pr = exp2_fast(s[qb_][kb][i] * p.scale_log2 - lse2[qb_]);
+              e[u] = pr * (dp[qb_][kb][i] - dlt[qb_]);
+            }
+            dsb[qb_][kb][st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
+          }
+      // dQ^T += K^T dS^T  (K^T straight from the row-major K tile).
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int kbase = 32 * kb + 16 * st + 4 * hh + tr_row;
+#pragma unroll
+          for (int c = 0; c < NDB; ++c) {
+            const int dcol = (D >= 32 ? 32 * c + tr_col : (tr_col & 15));
+            bf16x8 a = cat8(lds_read_tr4(Kt + kbase * L::KSTR + dcol),
+                            lds_read_tr4(Kt + (kbase + 8) * L::KSTR + dcol));
+            if (!d_lane_ok) a = bf16x8{};
+#pragma unroll
+            for (int qb_ = 0; qb_ < QB; ++qb_) acc[qb_][c] = mfma32(a, dsb[qb_][kb][st], acc[qb_][c]);
+          }
+        }
+    }
+    if (nxt.valid()) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    walk = nxt;
+  }
+
+  bf16* Dg = static_cast<bf16*>(const_cast<void*>(p.dq.ptr)) + b * p.dq.sb + h * p.dq.sh;
+#pragma unroll
+  for (int qb_ = 0; qb_ < QB; ++qb_) {
+    const int row = wa + qb_ * 32 + l32;
+    if (row < p.Sq) {
+#pragma unroll
+      for (int c = 0; c < NDB; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * c + 8 * g + 4 * hh;
+          if (d < D) {
+            const float sc = p.scale;
+            *reinterpret_cast<bf16x4*>(Dg + (int64_t)row * p.dq.ss + d) =
+                to_bf16x4(acc[qb_][c][4 * g] * sc, acc[qb_][c][4 * g + 1] * sc,
+                          acc[qb_][c][4 * g + 2] * sc, acc[qb_][c][4 * g + 3] * sc);
+          }
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV: a workgroup owns NW*KB*32 keys of one (batch, kv head) and streams
+// query tiles (Q, dO, LSE, Delta) of every query head of the group through
+// LDS, in a fixed order.  Scores in natural orientation, S = Q K^T, so each
+// lane owns one key column; P and dS feed dV^T = dO^T P and dK^T = Q^T dS
+// from registers, with dO^T and Q^T read transposed from the row-major tiles.
+constexpr int KV_TQ = 64;
+
+template <int D>
+struct KvLds {
+  static constexpr int STR = D + 8;
+  static constexpr int TILE = KV_TQ * STR;               // one Q or dO tile
+  static constexpr int STAGE = 2 * TILE * 2 + 2 * KV_TQ * 4;  // Q, dO, LSE, Delta
+  static constexpr int BYTES = 2 * STAGE;
+};
+
+template <int D, int KB, int NW>
+__global__ void __launch_bounds__(NW * 64)
+dkdv_kernel(Params p) {
+  constexpr int NT = NW * 64;
+  constexpr int TKW = NW * KB * 32;   // keys per workgroup
+  constexpr int TQ = KV_TQ;
+  constexpr int DC = D / 8;
+  constexpr int CHUNKS = TQ * DC;
+  constexpr int PER_T = (CHUNKS + NT - 1) / NT;
+  constexpr int NDB = D >= 32 ? D / 32 : 1;
+  constexpr int NJ = D / 16;
+  using L = KvLds<D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int nkt = (p.Skv + TKW - 1) / TKW;
+  int col, rank;
+  map_block(blockIdx.x, p.B * p.Hkv, nkt, col, rank);
+  const int b = col / p.Hkv, hk = col % p.Hkv;
+  const int ktile = rank;  // key tile 0 sees the most queries under causal masks
+  const MaskB m = resolve_mask(p, b);
+  const int ka = ktile * TKW, kbnd = min(p.Skv, ka + TKW);
+  const int kw = ka + wave * KB * 32, kwe = min(p.Skv, kw + KB * 32);
+
+  const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
+  const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
+
+  // K^T, V^T as B operands: lane (key = l32, hh) holds row key at d 16j+8hh.
+  bf16x8 kreg[KB][NJ], vreg[KB][NJ];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = kw + kb * 32 + l32;
+    const bool ok = key_valid(m, key);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      kreg[kb][j] = ok ? *reinterpret_cast<const bf16x8*>(Kg + (int64_t)key * p.k.ss + 16 * j + 8 * hh)
+                       : bf16x8{};
+      vreg[kb][j] = ok ? *reinterpret_cast<const bf16x8*>(Vg + (int64_t)key * p.v.ss + 16 * j + 8 * hh)
+                       : bf16x8{};
+    }
+  }
+  f32x16 dka[KB][NDB], dva[KB][NDB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int c = 0; c < NDB; ++c) { dka[kb][c] = f32x16{}; dva[kb][c] = f32x16{}; }
+
+  int qlo, qhi;
+  query_hull(m, ka, kbnd, qlo, qhi);
+  const int t_first = qlo < qhi ? qlo / TQ : 0;
+  const int t_last = qlo < qhi ? (qhi + TQ - 1) / TQ : 0;
+  const int ntile = t_last - t_first;
+  const int nsteps = ntile * p.G;   // (head, query tile) pairs, head-major
+
+  i32x4 qst[PER_T], gst[PER_T];
+  float lst = 0.f, dst = 0.f;
+  auto fetch = [&](int step) {
+    const int h = hk * p.G + step / ntile;
+    const int q0 = (t_first + step % ntile) * TQ;
+    const bf16* Qg = static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
+    const bf16* Gg = static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int c = tid + i * NT;
+      const int r = c / DC, c8 = c % DC;
+      const int row = q0 + r;
+      if (c < CHUNKS && row < p.Sq) {
+        qst[i] = *reinterpret_cast<const i32x4*>(Qg + (int64_t)row * p.q.ss + 8 * c8);
+        gst[i] = *reinterpret_cast<const i32x4*>(Gg + (int64_t)row * p.dout.ss + 8 * c8);
+      } else {
+        qst[i] = i32x4{};
+        gst[i] = i32x4{};
+      }
+    }
+    if (tid < TQ) {
+      const int row = q0 + tid;
+      const int64_t rb = ((int64_t)b * p.Hq + h) * p.Sq;
+      lst = row < p.Sq ? p.lse_in[rb + row] * 1.4426950408889634f : 0.f;
+      dst = row < p.Sq ? p.delta[rb + row] : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+    unsigned char* st = smem + buf * L::STAGE;
+    bf16* Qs = reinterpret_cast<bf16*>(st);
+    bf16* Gs = Qs + L::TILE;
+    float* Ls = reinterpret_cast<float*>(Gs + L::TILE);
+    float* Ds = Ls + TQ;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int c = tid + i * NT;
+      if (c < CHUNKS) {
+        const int r = c / DC, c8 = c % DC;
+        lds_write16(Qs + r * L::STR + 8 * c8, qst[i]);
+        lds_write16(Gs + r * L::STR + 8 * c8, gst[i]);
+      }
+    }
+    if (tid < TQ) { Ls[tid] = lst; Ds[tid] = dst; }
+  };
+
+  int buf = 0;
+  if (nsteps > 0) {
+    fetch(0);
+    store(0);
+  }
+  __syncthreads();
+
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const bool d_lane_ok = D >= 32 || ((lane >> 4) & 1) == 0;
+
+  for (int step = 0; step < nsteps; ++step) {
+    if (step + 1 < nsteps) fetch(step + 1);
+    const int q0 = (t_first + step % ntile) * TQ;
+    const unsigned char* stg = smem + buf * L::STAGE;
+    const bf16* Qs = reinterpret_cast<const bf16*>(stg);
+    const bf16* Gs = Qs + L::TILE;
+    const float* Ls = reinterpret_cast<const float*>(Gs + L::TILE);
+    const float* Ds = Ls + TQ;
+
+#pragma unroll
+    for (int qb = 0; qb < TQ / 32; ++qb) {
+      const int qa = q0 + 32 * qb;
+      const int state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + 32));
+      if (state == TILE_SKIP) continue;
+      f32x16 s[KB], dp[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bf16x8 aq = lds_read8(Qs + (32 * qb + l32) * L::STR + 16 * j + 8 * hh);
+        const bf16x8 ag = lds_read8(Gs + (32 * qb + l32) * L::STR + 16 * j + 8 * hh);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb] = mfma32(aq, kreg[kb][j], s[kb]);
+          dp[kb] = mfma32(ag, vreg[kb][j], dp[kb]);
+        }
+      }
+      // Per-register query rows: q = qa + 8*(i/4) + 4*hh + i%4.
+      float lrow[16], drow[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *FA_LDS(const f32x4, Ls + 32 * qb + 8 * g + 4 * hh);
+        const f32x4 d4 = *FA_LDS(const f32x4, Ds + 32 * qb + 8 * g + 4 * hh);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { lrow[4 * g + u] = l4[u]; drow[4 * g + u] = d4[u]; }
+      }
+      bf16x8 pb[KB][2], dsb[KB][2];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int key = kw + 32 * kb + l32;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          float pe[8], de[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = 8 * st + u;
+            float sv = s[kb][i];
+            if (state == TILE_PART) {
+              const int qi = qa + 8 * (i >> 2) + 4 * hh + (i & 3);
+              if (!allowed(m, qi, key)) sv = -INFINITY;
+            }
+            pe[u] = exp2_fast(sv * p.scale_log2 - lrow[i]);
+            de[u] = pe[u] * (dp[kb][i] - drow[i]);
+          }
+          pb[kb][st] = cat8(to_bf16x4(pe[0], pe[1], pe[2], pe[3]), to_bf16x4(pe[4], pe[5], pe[6], pe[7]));
+          dsb[kb][st] = cat8(to_bf16x4(de[0], de[1], de[2], de[3]), to_bf16x4(de[4], de[5], de[6], de[7]));
+        }
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dS  (q-contraction, 16 rows per MFMA).
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int rbase = 32 * qb + 16 * st + 4 * hh + tr_row;
+#pragma unroll
+        for (int c = 0; c < NDB; ++c) {
+          const int dcol = (D >= 32 ? 32 * c + tr_col : (tr_col & 15));
+          bf16x8 ag = cat8(lds_read_tr4(Gs + rbase * L::STR + dcol), lds_read_tr4(Gs + (rbase + 8) * L::STR + dcol));
+          bf16x8 aq = cat8(lds_read_tr4(Qs + rbase * L::STR + dcol), lds_read_tr4(Qs + (rbase + 8) * L::STR + dcol));
+          if (!d_lane_ok) { ag = bf16x8{}; aq = bf16x8{}; }
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            dva[kb][c] = mfma32(ag, pb[kb][st], dva[kb][c]);
+            dka[kb][c] = mfma32(aq, dsb[kb][st], dka[kb][c]);
+          }
+        }
+      }
+    }
+    if (step + 1 < nsteps) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // dK = s * dK^T^T, dV = dV^T^T; lane (key, hh) holds d = 32c + 8g + 4hh + u.
+  bf16* DKg = static_cast<bf16*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh;
+  bf16* DVg = static_cast<bf16*>(const_cast<void*>(p.dv.ptr)) + b * p.dv.sb + hk * p.dv.sh;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = kw + 32 * kb + l32;
+    if (key < p.Skv) {
+#pragma unroll
+      for (int c = 0; c < NDB; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * c + 8 * g + 4 * hh;
+          if (d < D) {
+            const float sc = p.scale;
+            *reinterpret_cast<bf16x4*>(DKg + (int64_t)key * p.dk.ss + d) =
+                to_bf16x4(dka[kb][c][4 * g] * sc, dka[kb][c][4 * g + 1] * sc, dka[kb][c][4 * g + 2] * sc,
+                          dka[kb][c][4 * g + 3] * sc);
+            *reinterpret_cast<bf16x4*>(DVg + (int64_t)key * p.dv.ss + d) =
+                to_bf16x4(dva[kb][c][4 * g], dva[kb][c][4 * g + 1], dva[kb][c][4 * g + 2], dva[kb][c][4 * g + 3]);
+          }
+        }
+    }
+  }
+}
+
+template <typename K>
+hipError_t set_lds(K k, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int D>
+hipError_t launch_all(const Params& p, hipStream_t stream) {
+  hipError_t e;
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
+  if (rows > 0) {
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    constexpr int KB = 1, NW = 4, TKW = NW * KB * 32;
+    const int64_t nblk = (int64_t)p.B * p.Hkv * ((p.Skv + TKW - 1) / TKW);
+    if (nblk > 0) {
+      auto k = dkdv_kernel<D, KB, NW>;
+      if ((e = set_lds(k, KvLds<D>::BYTES)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NW * 64), KvLds<D>::BYTES, stream, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  {
+    constexpr int QB = D >= 128 ? 1 : 2, NW = D >= 128 ? 8 : 4, TQ = NW * QB * 32;
+    const int64_t nblk = (int64_t)p.B * p.Hq * ((p.Sq + TQ - 1) / TQ);
+    if (nblk > 0) {
+      auto k = dq_kernel<D, QB, NW>;
+      if ((e = set_lds(k, DqLds<D>::BYTES)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NW * 64), DqLds<D>::BYTES, stream, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const Params& p, hipStream_t s) {
+  switch (p.D) {
+    case 16: return launch_all<16>(p, s);
+    case 32: return launch_all<32>(p, s);
+    case 64: return launch_all<64>(p, s);
+    case 128: return launch_all<128>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

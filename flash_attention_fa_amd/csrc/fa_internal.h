@@ -1,0 +1,41 @@
+// fa_internal.h - parameters shared by the host dispatcher and the kernels.
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+// A [B, H, S, D] tensor with unit D stride, strides in elements.
+struct Tensor {
+  const void* ptr;
+  int64_t sb, sh, ss;
+};
+
+struct Mask {
+  int kind;            // 0 FULL, 1 CAUSAL, 2 TTT
+  int shift;           // causal shift (>= 0)
+  const int* kv_valid; // device [B] or nullptr
+};
+
+// Everything a kernel needs.  Built once per call by the dispatcher.
+struct Params {
+  int B, Hq, Hkv, G, Sq, Skv, D;
+  float scale;         // softmax scale
+  float scale_log2;    // scale * log2(e): scores go through exp2
+  Mask mask;
+  Tensor q, k, v, o;   // o: forward output / backward input
+  Tensor dout;         // backward: dO
+  Tensor dq, dk, dv;   // backward outputs
+  float* lse;          // forward output
+  const float* lse_in; // backward input
+  float* delta;        // backward workspace [B, Hq, Sq]
+};
+
+// Launchers (one translation unit per kernel family).  Each returns the
+// hipError_t of its launches; shapes were validated by the dispatcher.
+hipError_t launch_fwd_bf16(const Params& p, hipStream_t s);
+hipError_t launch_bwd_bf16(const Params& p, hipStream_t s);
+hipError_t launch_fwd_f32(const Params& p, hipStream_t s);
+hipError_t launch_bwd_f32(const Params& p, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,140 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) fused training-attention library.
+ *
+ * The library computes exact scaled-dot-product attention and its gradient
+ * without ever holding the S x S score matrix in device memory:
+ *
+ *   forward   O = softmax(scale * Q K^T + mask) V, saving only O and the
+ *             per-row natural logsumexp LSE of the scaled, masked scores.
+ *             ("Flex Attention and Triton, Supporting Long Context Training
+ *             in SpecForge", section EAGLE3 Training, gives the formula;
+ *             the ggml flash-attn-training playbook, section 1 "What
+ *             exists", gives the saved state O + LSE.)
+ *   backward  recomputes P from LSE, forms Delta = rowsum(dO * O) and writes
+ *             dQ, dK, dV  (CS336 "Flash Attention (Triton)": the fused
+ *             kernel computes what the explicit QK^T -> softmax -> PV chain
+ *             computes; the playbook's section 1 asks for a bitwise
+ *             deterministic backward with no floating-point atomics).
+ *
+ * Mask kinds (SpecForge page, section "Flex Attention"):
+ *   FA_MASK_FULL    key j allowed iff j < kv_valid[b]
+ *   FA_MASK_CAUSAL  key j allowed iff j <= i - causal_shift and j < kv_valid[b]
+ *                   (top-left aligned when Sq != Skv)
+ *   FA_MASK_TTT     EAGLE3 training-time-test: with L = Sq and Skv = n * L,
+ *                   key j allowed iff
+ *                     (j <= i - causal_shift and j < kv_valid[b])            or
+ *                     (j >= L and (j - i) mod L == 0 and (j mod L) < kv_valid[b])
+ *                   i.e. causal over the step-0 keys plus, for every later
+ *                   step s, the key of step s at the query's own position.
+ *   A query row with no allowed key gets O = 0 and LSE = 0, and contributes
+ *   no gradient; a key no query may attend gets dK = dV = 0 exactly (ggml
+ *   playbook, "6. Trap list", items 8 and 9).
+ *   The mask is the same for every head.  Grouped-query attention maps query
+ *   head h to key/value head h / (Hq / Hkv).
+ *
+ * Layout.  Every tensor is a logical [B, H, S, D] array with unit stride in
+ * D and arbitrary element strides for B, H and S (so BHSD and BSHD views both
+ * work without a copy).  LSE is a contiguous float32 [B, Hq, Sq] array.
+ * All tensor pointers are device pointers.  Element type: FA_BF16 (bfloat16
+ * storage, float32 accumulation; O, dQ, dK, dV rounded to nearest even) or
+ * FA_F32 (float32 throughout).
+ *
+ * Ownership.  The caller owns every buffer, including the backward
+ * workspace.  The library allocates no device memory, keeps no state between
+ * calls, launches on the caller's stream and never synchronises the host.
+ *
+ * Errors.  All arguments are validated before anything is launched; on a
+ * non-OK status nothing was launched and fa_last_error() describes why.
+ * There is no fallback path of any kind.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,  /* NULL pointer, non-positive size, Hq % Hkv != 0,
+                              TTT with Skv % Sq != 0, negative shift,
+                              workspace too small, unit D stride violated */
+  FA_ERR_UNSUPPORTED = 2,  /* D not in {16, 32, 64, 128}, unknown dtype/kind */
+  FA_ERR_ALIGNMENT = 3,    /* base pointer or B/H/S stride not 16-byte aligned */
+  FA_ERR_ALIAS = 4,        /* an output's byte range overlaps an input's */
+  FA_ERR_HIP = 5           /* no usable device, or a launch failed */
+} fa_status;
+
+typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
+
+typedef enum { FA_MASK_FULL = 0, FA_MASK_CAUSAL = 1, FA_MASK_TTT = 2 } fa_mask_kind;
+
+/* One [B, H, S, D] tensor: base pointer and element strides (D stride = 1). */
+typedef struct {
+  void* data;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_s;
+} fa_tensor;
+
+typedef struct {
+  int32_t kind;              /* fa_mask_kind */
+  int32_t causal_shift;      /* >= 0; used by CAUSAL and by TTT's step-0 part */
+  const int32_t* kv_valid;   /* device int32 [B] valid key count per batch
+                                (clamped to [0, Skv] for FULL/CAUSAL and to
+                                [0, Sq] for TTT), or NULL = all keys valid */
+} fa_mask_desc;
+
+typedef struct {
+  int32_t dtype;             /* fa_dtype */
+  int32_t B, Hq, Hkv, Sq, Skv, D;
+  float scale;               /* softmax scale; <= 0 selects 1/sqrt(D) */
+  fa_tensor q;               /* in  [B, Hq,  Sq,  D] */
+  fa_tensor k;               /* in  [B, Hkv, Skv, D] */
+  fa_tensor v;               /* in  [B, Hkv, Skv, D] */
+  fa_tensor o;               /* out [B, Hq,  Sq,  D] */
+  float* lse;                /* out [B, Hq, Sq] float32, natural log */
+  fa_mask_desc mask;
+} fa_fwd_args;
+
+typedef struct {
+  int32_t dtype;
+  int32_t B, Hq, Hkv, Sq, Skv, D;
+  float scale;               /* must equal the forward's */
+  fa_tensor q, k, v;         /* in, as in the forward */
+  fa_tensor o;               /* in  forward output O */
+  fa_tensor dout;            /* in  upstream gradient dO [B, Hq, Sq, D] */
+  const float* lse;          /* in  forward LSE [B, Hq, Sq] */
+  fa_tensor dq;              /* out [B, Hq,  Sq,  D] */
+  fa_tensor dk;              /* out [B, Hkv, Skv, D] (summed over the group) */
+  fa_tensor dv;              /* out [B, Hkv, Skv, D] (summed over the group) */
+  fa_mask_desc mask;         /* must equal the forward's */
+} fa_bwd_args;
+
+/* Forward: writes O and LSE.  Asynchronous on `stream` (0 = null stream). */
+fa_status fa_fwd(const fa_fwd_args* args, hipStream_t stream);
+
+/* Bytes of device scratch fa_bwd needs for these arguments (Delta, a float32
+ * [B, Hq, Sq] array, rounded up to 256 bytes): linear in Sq, never S x S.
+ * Returns 0 when args is NULL. */
+size_t fa_bwd_workspace_bytes(const fa_bwd_args* args);
+
+/* Backward: writes dQ, dK, dV; bitwise identical on every rerun (fixed
+ * reduction orders, no floating-point atomics).  `ws` is caller-owned device
+ * memory of at least fa_bwd_workspace_bytes(args) bytes, 256-byte aligned. */
+fa_status fa_bwd(const fa_bwd_args* args, void* ws, size_t ws_bytes,
+                 hipStream_t stream);
+
+/* Text describing the last non-OK status returned on this thread
+ * ("" if none).  The pointer stays valid until the thread's next call. */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

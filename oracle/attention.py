@@ -105,13 +105,21 @@ def _row_softmax(S_masked):
     return P, lse
 
 
+def _row_blocks(Sq, rows):
+    """Query-row blocks to materialise: all rows, or the sampled range."""
+    lo, hi = (0, Sq) if rows is None else (int(rows[0]), int(rows[1]))
+    for r0 in range(lo, hi, _ROW_BLOCK):
+        yield np.arange(r0, min(hi, r0 + _ROW_BLOCK))
+
+
 def attention_forward(q, k, v, kind=FULL, shift=0, kv_valid=None, scale=None,
-                      heads=None):
+                      heads=None, rows=None):
     """O [B,Hq,Sq,D] and LSE [B,Hq,Sq] in float64.
 
-    ``heads`` optionally restricts the work to a list of query heads (the
-    other heads' outputs are left as NaN); used to time or check one GQA
-    group of a large configuration.
+    ``heads`` (a list of query heads) and ``rows`` (a half-open range
+    (lo, hi) of query rows) optionally restrict the work; outputs outside the
+    selection are left as NaN.  Used to check or time a sample of a large
+    configuration; every computed row is still complete over all keys.
     """
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
@@ -122,26 +130,25 @@ def attention_forward(q, k, v, kind=FULL, shift=0, kv_valid=None, scale=None,
     O = np.full(q.shape, np.nan)
     LSE = np.full((B, Hq, Sq), np.nan)
     for b in range(B):
-        for r0 in range(0, Sq, _ROW_BLOCK):
-            rows = np.arange(r0, min(Sq, r0 + _ROW_BLOCK))
-            A = allowed(kind, Sq, Skv, shift, kvv[b], rows)
+        for rb in _row_blocks(Sq, rows):
+            A = allowed(kind, Sq, Skv, shift, kvv[b], rb)
             for h in hs:
                 g = h // G
-                S = s * (q[b, h, rows] @ k[b, g].T)
+                S = s * (q[b, h, rb] @ k[b, g].T)
                 P, lse = _row_softmax(np.where(A, S, -np.inf))
-                O[b, h, rows] = P @ v[b, g]
-                LSE[b, h, rows] = lse
+                O[b, h, rb] = P @ v[b, g]
+                LSE[b, h, rb] = lse
     return O, LSE
 
 
 def attention_backward(q, k, v, do, kind=FULL, shift=0, kv_valid=None,
-                       scale=None, heads=None):
+                       scale=None, heads=None, rows=None):
     """dQ, dK, dV (float64) of L = sum(O * dO), plus Delta [B,Hq,Sq].
 
     P is rebuilt from the scores, exactly as the definition states; dK and dV
     of a key/value head sum the contributions of every query head in its
-    group.  With ``heads`` only those query heads contribute (to dK/dV as
-    well), and the other heads' dQ rows are NaN.
+    group.  With ``heads`` / ``rows`` only the selected query rows contribute
+    (to dK/dV as well), and the other dQ rows are NaN.
     """
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
@@ -154,28 +161,27 @@ def attention_backward(q, k, v, do, kind=FULL, shift=0, kv_valid=None,
     dV = np.zeros(v.shape)
     Delta = np.full((B, Hq, Sq), np.nan)
     for b in range(B):
-        for r0 in range(0, Sq, _ROW_BLOCK):
-            rows = np.arange(r0, min(Sq, r0 + _ROW_BLOCK))
-            A = allowed(kind, Sq, Skv, shift, kvv[b], rows)
+        for rb in _row_blocks(Sq, rows):
+            A = allowed(kind, Sq, Skv, shift, kvv[b], rb)
             for h in hs:
                 g = h // G
-                S = s * (q[b, h, rows] @ k[b, g].T)
+                S = s * (q[b, h, rb] @ k[b, g].T)
                 P, _ = _row_softmax(np.where(A, S, -np.inf))
-                dO = do[b, h, rows]
+                dO = do[b, h, rb]
                 dV[b, g] += P.T @ dO
                 dP = dO @ v[b, g].T
                 delta = (P * dP).sum(axis=1)
                 dS = P * (dP - delta[:, None])
-                dQ[b, h, rows] = s * (dS @ k[b, g])
-                dK[b, g] += s * (dS.T @ q[b, h, rows])
-                Delta[b, h, rows] = delta
+                dQ[b, h, rb] = s * (dS @ k[b, g])
+                dK[b, g] += s * (dS.T @ q[b, h, rb])
+                Delta[b, h, rb] = delta
     return dQ, dK, dV, Delta
 
 
 def attention_ref(q, k, v, do, kind=FULL, shift=0, kv_valid=None, scale=None,
-                  heads=None):
+                  heads=None, rows=None):
     """Forward and backward together: dict with O, LSE, dQ, dK, dV, Delta."""
-    O, LSE = attention_forward(q, k, v, kind, shift, kv_valid, scale, heads)
+    O, LSE = attention_forward(q, k, v, kind, shift, kv_valid, scale, heads, rows)
     dQ, dK, dV, Delta = attention_backward(q, k, v, do, kind, shift, kv_valid,
-                                           scale, heads)
+                                           scale, heads, rows)
     return dict(O=O, LSE=LSE, dQ=dQ, dK=dK, dV=dV, Delta=Delta)

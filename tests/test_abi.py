@@ -1,0 +1,189 @@
+"""The C ABI on the CPU: symbols, struct layout and argument validation.
+
+No kernel runs here.  Validation happens before any HIP call, so fake
+(aligned, never dereferenced) device addresses exercise every error path; a
+valid request on a machine without a GPU must fail cleanly with FA_ERR_HIP.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from flash_attention_fa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BASE = 1 << 32          # fake device addresses: 16-byte aligned, far apart
+GAP = 1 << 28
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:fa_status|size_t|const char\*)\s+(fa_\w+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    L = _lib.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_layout_matches_header():
+    # offsets a C compiler gives the structs of fa.h on x86-64
+    assert ctypes.sizeof(_lib.fa_tensor) == 32
+    assert ctypes.sizeof(_lib.fa_mask_desc) == 16
+    assert _lib.fa_fwd_args.q.offset == 32
+    assert _lib.fa_fwd_args.lse.offset == 32 + 4 * 32
+    assert _lib.fa_fwd_args.mask.offset == 32 + 4 * 32 + 8
+    assert _lib.fa_bwd_args.lse.offset == 32 + 5 * 32
+    assert _lib.fa_bwd_args.mask.offset == 32 + 5 * 32 + 8 + 3 * 32
+
+
+def _t(slot, B, H, S, D, eb=2, strides=None):
+    st = strides or (H * S * D, S * D, D)
+    return _lib.fa_tensor(BASE + slot * GAP, *st)
+
+
+def fwd_args(B=1, Hq=4, Hkv=2, Sq=64, Skv=64, D=64, dtype=_lib.FA_BF16, kind=1, shift=0):
+    a = _lib.fa_fwd_args()
+    a.dtype, a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = dtype, B, Hq, Hkv, Sq, Skv, D
+    a.scale = 0.0
+    a.q, a.k, a.v, a.o = _t(0, B, Hq, Sq, D), _t(1, B, Hkv, Skv, D), _t(2, B, Hkv, Skv, D), _t(3, B, Hq, Sq, D)
+    a.lse = BASE + 4 * GAP
+    a.mask = _lib.fa_mask_desc(kind, shift, None)
+    return a
+
+
+def bwd_args(B=1, Hq=4, Hkv=2, Sq=64, Skv=64, D=64, dtype=_lib.FA_BF16, kind=1):
+    a = _lib.fa_bwd_args()
+    a.dtype, a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = dtype, B, Hq, Hkv, Sq, Skv, D
+    a.scale = 0.0
+    a.q, a.k, a.v = _t(0, B, Hq, Sq, D), _t(1, B, Hkv, Skv, D), _t(2, B, Hkv, Skv, D)
+    a.o, a.dout = _t(3, B, Hq, Sq, D), _t(4, B, Hq, Sq, D)
+    a.lse = BASE + 5 * GAP
+    a.dq, a.dk, a.dv = _t(6, B, Hq, Sq, D), _t(7, B, Hkv, Skv, D), _t(8, B, Hkv, Skv, D)
+    a.mask = _lib.fa_mask_desc(kind, 0, None)
+    return a
+
+
+WS = BASE + 9 * GAP
+
+
+def fwd(a):
+    st = _lib.lib().fa_fwd(a, None)
+    return st, _lib.last_error()
+
+
+def bwd(a, ws=WS, ws_bytes=1 << 20):
+    st = _lib.lib().fa_bwd(a, ws, ws_bytes, None)
+    return st, _lib.last_error()
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_present(), reason="checks the no-device path")
+def test_valid_request_without_device_fails_cleanly():
+    st, msg = fwd(fwd_args())
+    assert st == _lib.FA_ERR_HIP and "device" in msg
+    st, msg = bwd(bwd_args())
+    assert st == _lib.FA_ERR_HIP and "device" in msg
+
+
+FWD_CASES = [
+    ("bad D", dict(D=48), _lib.FA_ERR_UNSUPPORTED, "head dim"),
+    ("bad D 256", dict(D=256), _lib.FA_ERR_UNSUPPORTED, "head dim"),
+    ("bad dtype", dict(dtype=7), _lib.FA_ERR_UNSUPPORTED, "dtype"),
+    ("bad kind", dict(kind=5), _lib.FA_ERR_UNSUPPORTED, "mask kind"),
+    ("gqa not dividing", dict(Hq=6, Hkv=4), _lib.FA_ERR_INVALID_ARG, "multiple of Hkv"),
+    ("zero heads", dict(Hq=0), _lib.FA_ERR_INVALID_ARG, "non-positive"),
+    ("negative S", dict(Sq=-1), _lib.FA_ERR_INVALID_ARG, "negative size"),
+    ("negative shift", dict(shift=-2), _lib.FA_ERR_INVALID_ARG, "causal_shift"),
+    ("ttt skv not multiple", dict(kind=2, Sq=64, Skv=100), _lib.FA_ERR_INVALID_ARG, "multiple of Sq"),
+]
+
+
+@pytest.mark.parametrize("name,kw,status,text", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_forward_validation(name, kw, status, text):
+    st, msg = fwd(fwd_args(**kw))
+    assert st == status, msg
+    assert text in msg
+
+
+def test_forward_pointer_alignment_alias_and_null():
+    a = fwd_args()
+    a.q.data = BASE + 8                       # misaligned base
+    st, msg = fwd(a)
+    assert st == _lib.FA_ERR_ALIGNMENT and "q" in msg
+    a = fwd_args()
+    a.k.stride_s = 60                         # 120 bytes: not a multiple of 16
+    st, msg = fwd(a)
+    assert st == _lib.FA_ERR_ALIGNMENT and "k" in msg
+    a = fwd_args()
+    a.o.data = a.q.data + 64                  # output inside an input
+    st, msg = fwd(a)
+    assert st == _lib.FA_ERR_ALIAS
+    a = fwd_args()
+    a.lse = a.v.data                          # lse on top of v
+    st, msg = fwd(a)
+    assert st == _lib.FA_ERR_ALIAS and "lse" in msg
+    a = fwd_args()
+    a.v.data = None
+    st, msg = fwd(a)
+    assert st == _lib.FA_ERR_INVALID_ARG and "NULL" in msg
+    a = fwd_args()
+    a.lse = None
+    st, msg = fwd(a)
+    assert st == _lib.FA_ERR_INVALID_ARG and "lse" in msg
+    a = fwd_args()
+    a.o.stride_s = 32                         # output rows overlap each other (D = 64)
+    st, msg = fwd(a)
+    assert st == _lib.FA_ERR_INVALID_ARG and "overlap" in msg
+    st = _lib.lib().fa_fwd(None, None)
+    assert st == _lib.FA_ERR_INVALID_ARG
+
+
+def test_forward_empty_is_a_noop():
+    for kw in (dict(B=0), dict(Sq=0)):
+        a = fwd_args(**kw)
+        st, msg = fwd(a)
+        assert st == _lib.FA_OK, msg
+
+
+def test_backward_validation():
+    a = bwd_args()
+    need = _lib.lib().fa_bwd_workspace_bytes(a)
+    assert need == (1 * 4 * 64 * 4 + 255) // 256 * 256
+    assert _lib.lib().fa_bwd_workspace_bytes(None) == 0
+    st, msg = bwd(a, ws_bytes=need - 1)
+    assert st == _lib.FA_ERR_INVALID_ARG and "workspace too small" in msg
+    st, msg = bwd(a, ws=None)
+    assert st == _lib.FA_ERR_INVALID_ARG and "workspace" in msg
+    st, msg = bwd(a, ws=WS + 16)
+    assert st == _lib.FA_ERR_ALIGNMENT and "workspace" in msg
+    a = bwd_args()
+    a.dk.data = a.dq.data                     # two outputs on one buffer
+    st, msg = bwd(a)
+    assert st == _lib.FA_ERR_ALIAS
+    a = bwd_args()
+    a.dv.data = a.dout.data                   # output on an input
+    st, msg = bwd(a)
+    assert st == _lib.FA_ERR_ALIAS
+    st, msg = bwd(bwd_args(), ws=bwd_args().q.data)   # workspace on an input
+    assert st == _lib.FA_ERR_ALIAS and "workspace" in msg
+    st, msg = bwd(bwd_args(D=8))
+    assert st == _lib.FA_ERR_UNSUPPORTED
+
+
+def test_workspace_is_linear_in_sequence_length():
+    sizes = [_lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=s, Skv=s, D=128))
+             for s in (16384, 32768)]
+    assert sizes[1] == 2 * sizes[0] == 2 * 32 * 16384 * 4

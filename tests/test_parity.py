@@ -1,0 +1,140 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small shapes that the oracle finishes in seconds but that still span several
+tiles and a ragged tail, for every mask kind, GQA ratio, head dim, dtype,
+padding and stride layout; plus the edge cases (single row/key, empty key set,
+NaN in padded rows, fully-masked rows) and bitwise determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from parity_util import check_case, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+FULL, CAUSAL, TTT = W.FULL, W.CAUSAL, W.TTT
+
+
+def rnd(shape, seed, dtype):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def inputs(B, Hq, Hkv, Sq, Skv, D, dtype, seed=0):
+    return (rnd((B, Hq, Sq, D), seed, dtype), rnd((B, Hkv, Skv, D), seed + 1, dtype),
+            rnd((B, Hkv, Skv, D), seed + 2, dtype), rnd((B, Hq, Sq, D), seed + 3, dtype))
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("kind", [CAUSAL, FULL])
+def test_bf16_self_attention_ragged(D, kind):
+    q, k, v, do = inputs(2, 4, 2, 300, 300, D, torch.bfloat16, seed=D)
+    check_case(q, k, v, do, kind, "bf16", label=f"bf16 self D={D}")
+
+
+@pytest.mark.parametrize("G", [1, 8])
+def test_bf16_gqa_causal(G):
+    q, k, v, do = inputs(1, 8, 8 // G, 520, 520, 128, torch.bfloat16, seed=7)
+    check_case(q, k, v, do, CAUSAL, "bf16", label=f"bf16 gqa G={G}")
+
+
+def test_bf16_cross_attention_padded_keys():
+    # Sq != Skv, per-batch valid key counts that are not tile multiples
+    q, k, v, do = inputs(2, 4, 4, 200, 333, 64, torch.bfloat16, seed=11)
+    check_case(q, k, v, do, FULL, "bf16", kv_valid=(300, 77), label="bf16 cross kv_valid")
+
+
+def test_bf16_padded_rows_hold_nan():
+    # NaN in K/V rows past kv_valid must never reach the outputs.
+    q, k, v, do = inputs(2, 2, 2, 130, 200, 64, torch.bfloat16, seed=13)
+    kv_valid = (150, 61)
+    clean = run_gpu(q, k, v, do, FULL, 0, kv_valid)
+    k2, v2 = k.clone(), v.clone()
+    for b, n in enumerate(kv_valid):
+        k2[b, :, n:] = float("nan")
+        v2[b, :, n:] = float("nan")
+    dirty = run_gpu(q, k2, v2, do, FULL, 0, kv_valid)
+    for name in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(clean[name], dirty[name]), name
+    check_case(q, k2, v2, do, FULL, "bf16", kv_valid=kv_valid, label="bf16 nan padding")
+
+
+@pytest.mark.parametrize("shift", [1, 3, 70])
+def test_bf16_causal_shift_with_empty_rows(shift):
+    q, k, v, do = inputs(1, 2, 1, 257, 257, 64, torch.bfloat16, seed=17)
+    check_case(q, k, v, do, CAUSAL, "bf16", shift=shift, label=f"bf16 causal shift={shift}")
+
+
+def test_bf16_causal_sq_ne_skv():
+    q, k, v, do = inputs(1, 4, 2, 150, 400, 64, torch.bfloat16, seed=19)
+    check_case(q, k, v, do, CAUSAL, "bf16", label="bf16 causal Sq<Skv")
+    q, k, v, do = inputs(1, 4, 2, 400, 150, 64, torch.bfloat16, seed=20)
+    check_case(q, k, v, do, CAUSAL, "bf16", label="bf16 causal Sq>Skv")
+
+
+@pytest.mark.parametrize("L,t,shift,kvv", [
+    (256, 2, 0, None), (130, 1, 0, None), (130, 2, 2, None), (100, 2, 0, (70,)),
+    (300, 0, 0, None), (96, 3, 1, (90,))])
+def test_bf16_ttt(L, t, shift, kvv):
+    q, k, v, do = inputs(1, 8, 2, L, (t + 1) * L, 128, torch.bfloat16, seed=L + t)
+    check_case(q, k, v, do, TTT, "bf16", shift=shift, kv_valid=kvv,
+               label=f"bf16 ttt L={L} t={t} shift={shift}")
+
+
+def test_bf16_bshd_strided_views():
+    # q/k/v/dO as transposed views of [B, S, H, D] storage (no copies)
+    B, S, Hq, Hkv, D = 2, 190, 4, 2, 64
+    g = torch.Generator("cpu").manual_seed(23)
+    mk = lambda H: torch.randn(B, S, H, D, generator=g).to(torch.bfloat16).transpose(1, 2)
+    q, k, v, do = mk(Hq), mk(Hkv), mk(Hkv), mk(Hq)
+    assert not q.is_contiguous()
+    check_case(q, k, v, do, CAUSAL, "bf16", label="bf16 bshd views")
+
+
+def test_bf16_explicit_scale():
+    q, k, v, do = inputs(1, 2, 2, 128, 128, 64, torch.bfloat16, seed=29)
+    check_case(q, k, v, do, CAUSAL, "bf16", scale=0.05, label="bf16 scale=0.05")
+
+
+def test_bf16_single_row_and_key():
+    q, k, v, do = inputs(1, 1, 1, 1, 1, 32, torch.bfloat16, seed=31)
+    check_case(q, k, v, do, CAUSAL, "bf16", label="bf16 1x1")
+
+
+def test_bf16_no_valid_keys():
+    q, k, v, do = inputs(2, 2, 2, 64, 64, 64, torch.bfloat16, seed=37)
+    got = run_gpu(q, k, v, do, FULL, 0, (0, 0))
+    for name in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.all(got[name] == 0.0), name
+
+
+@pytest.mark.parametrize("kind", [CAUSAL, FULL])
+def test_f32_tiny(kind):
+    w = W.tiny_fp32(kind)
+    q, k, v, do = W.make_inputs(w, seed=0)
+    check_case(q, k, v, do, kind, "f32", label=f"{w.name}")
+
+
+@pytest.mark.parametrize("D", [16, 128])
+def test_f32_ragged_gqa_ttt(D):
+    q, k, v, do = inputs(1, 4, 2, 70, 210, D, torch.float32, seed=41)
+    check_case(q, k, v, do, TTT, "f32", kv_valid=(65,), label=f"f32 ttt D={D}")
+    q, k, v, do = inputs(2, 4, 1, 99, 99, D, torch.float32, seed=43)
+    check_case(q, k, v, do, CAUSAL, "f32", shift=2, label=f"f32 causal D={D}")
+
+
+@pytest.mark.parametrize("kind", [CAUSAL, TTT])
+def test_bitwise_determinism(kind):
+    L = 384
+    Skv = 3 * L if kind == TTT else L
+    q, k, v, do = inputs(1, 8, 2, L, Skv, 128, torch.bfloat16, seed=47)
+    say(f"[determinism] kind={kind}")
+    a = run_gpu(q, k, v, do, kind)
+    # unrelated work in between, then the same call again
+    x = torch.randn(4096, 4096, device="cuda")
+    (x @ x).sum().item()
+    b = run_gpu(q, k, v, do, kind)
+    for name in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(a[name], b[name]), name
