@@ -261,37 +261,53 @@ dq_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV: a workgroup owns NW*KB*32 keys of one (batch, kv head) and streams
+// dK/dV: a workgroup owns NKB*32 keys of one (batch, kv head) and streams
 // query tiles (Q, dO, LSE, Delta) of every query head of the group through
 // LDS, in a fixed order.  Scores in natural orientation, S = Q K^T, so each
 // lane owns one key column; P and dS feed dV^T = dO^T P and dK^T = Q^T dS
 // from registers, with dO^T and Q^T read transposed from the row-major tiles.
+//
+// Two waves share each 32-key block: wave w takes key block w % NKB and the
+// (w / NKB)-th 32-row half of every 64-row query tile, so a SIMD runs two
+// waves and one hides the other's latency.  K^T stays in registers, V^T is
+// read from an LDS copy of the workgroup's V rows.  At the end the second
+// wave of each pair hands its partial dK/dV to the first through LDS, which
+// adds it to its own (always in that order) and writes the result.
 constexpr int KV_TQ = 64;
 
-template <int D>
+template <int D, int NKB, bool KLDS>
 struct KvLds {
   static constexpr int STR = D + 8;
-  static constexpr int TILE = KV_TQ * STR;               // one Q or dO tile
+  static constexpr int TILE = KV_TQ * STR;                    // one Q or dO tile
   static constexpr int STAGE = 2 * TILE * 2 + 2 * KV_TQ * 4;  // Q, dO, LSE, Delta
-  static constexpr int BYTES = 2 * STAGE;
+  static constexpr int VROWS = NKB * 32;
+  static constexpr int VBYTES = VROWS * STR * 2 * (KLDS ? 2 : 1);  // V rows (then K rows)
+  static constexpr int NDB = D >= 32 ? D / 32 : 1;
+  static constexpr int XBYTES = NKB * NDB * 16 * 64 * 4;      // one partial exchange
+  static constexpr int MAIN = 2 * STAGE + VBYTES;
+  static constexpr int BYTES = MAIN > XBYTES ? MAIN : XBYTES;
 };
 
-template <int D, int KB, int NW>
-__global__ void __launch_bounds__(NW * 64)
+template <int D, int NKB, bool KLDS>
+__global__ void __launch_bounds__(NKB * 2 * 64)
 dkdv_kernel(Params p) {
+  constexpr int NW = 2 * NKB;
   constexpr int NT = NW * 64;
-  constexpr int TKW = NW * KB * 32;   // keys per workgroup
+  constexpr int TKW = NKB * 32;       // keys per workgroup
   constexpr int TQ = KV_TQ;
   constexpr int DC = D / 8;
   constexpr int CHUNKS = TQ * DC;
   constexpr int PER_T = (CHUNKS + NT - 1) / NT;
   constexpr int NDB = D >= 32 ? D / 32 : 1;
   constexpr int NJ = D / 16;
-  using L = KvLds<D>;
+  using L = KvLds<D, NKB, KLDS>;
   extern __shared__ __align__(16) unsigned char smem[];
+  bf16* Vs = reinterpret_cast<bf16*>(smem + 2 * L::STAGE);
+  bf16* Ksh = Vs + L::VROWS * L::STR;  // K rows, when K^T is read from LDS
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
+  const int kblk = wave % NKB, qhalf = wave / NKB;
 
   const int nkt = (p.Skv + TKW - 1) / TKW;
   int col, rank;
@@ -300,30 +316,37 @@ dkdv_kernel(Params p) {
   const int ktile = rank;  // key tile 0 sees the most queries under causal masks
   const MaskB m = resolve_mask(p, b);
   const int ka = ktile * TKW, kbnd = min(p.Skv, ka + TKW);
-  const int kw = ka + wave * KB * 32, kwe = min(p.Skv, kw + KB * 32);
+  const int kw = ka + kblk * 32, kwe = min(p.Skv, kw + 32);
 
   const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
   const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
 
-  // K^T, V^T as B operands: lane (key = l32, hh) holds row key at d 16j+8hh.
-  bf16x8 kreg[KB][NJ], vreg[KB][NJ];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int key = kw + kb * 32 + l32;
+  // K^T as the B operand: lane (key = l32, hh) holds K[key][16j + 8hh .. +8].
+  bf16x8 kreg[KLDS ? 1 : NJ];
+  if constexpr (!KLDS) {
+    const int key = kw + l32;
     const bool ok = key_valid(m, key);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      kreg[kb][j] = ok ? *reinterpret_cast<const bf16x8*>(Kg + (int64_t)key * p.k.ss + 16 * j + 8 * hh)
-                       : bf16x8{};
-      vreg[kb][j] = ok ? *reinterpret_cast<const bf16x8*>(Vg + (int64_t)key * p.v.ss + 16 * j + 8 * hh)
-                       : bf16x8{};
+    for (int j = 0; j < NJ; ++j)
+      kreg[j] = ok ? *reinterpret_cast<const bf16x8*>(Kg + (int64_t)key * p.k.ss + 16 * j + 8 * hh)
+                   : bf16x8{};
+  }
+  // The workgroup's V (and K) rows, zero for keys that are not real.
+  for (int c = tid; c < TKW * DC; c += NT) {
+    const int r = c / DC, c8 = c % DC;
+    const int key = ka + r;
+    const bool ok = key_valid(m, key);
+    const i32x4 val = ok ? *reinterpret_cast<const i32x4*>(Vg + (int64_t)key * p.v.ss + 8 * c8) : i32x4{};
+    lds_write16(Vs + r * L::STR + 8 * c8, val);
+    if constexpr (KLDS) {
+      const i32x4 kv = ok ? *reinterpret_cast<const i32x4*>(Kg + (int64_t)key * p.k.ss + 8 * c8) : i32x4{};
+      lds_write16(Ksh + r * L::STR + 8 * c8, kv);
     }
   }
-  f32x16 dka[KB][NDB], dva[KB][NDB];
+
+  f32x16 dka[NDB], dva[NDB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int c = 0; c < NDB; ++c) { dka[kb][c] = f32x16{}; dva[kb][c] = f32x16{}; }
+  for (int c = 0; c < NDB; ++c) { dka[c] = f32x16{}; dva[c] = f32x16{}; }
 
   int qlo, qhi;
   query_hull(m, ka, kbnd, qlo, qhi);
@@ -387,80 +410,70 @@ dkdv_kernel(Params p) {
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const bool d_lane_ok = D >= 32 || ((lane >> 4) & 1) == 0;
+  const int key = kw + l32;
+  const bf16* Vrow = Vs + (kblk * 32 + l32) * L::STR + 8 * hh;
+  const bf16* Krow = Ksh + (kblk * 32 + l32) * L::STR + 8 * hh;
 
   for (int step = 0; step < nsteps; ++step) {
     if (step + 1 < nsteps) fetch(step + 1);
     const int q0 = (t_first + step % ntile) * TQ;
     const unsigned char* stg = smem + buf * L::STAGE;
-    const bf16* Qs = reinterpret_cast<const bf16*>(stg);
-    const bf16* Gs = Qs + L::TILE;
-    const float* Ls = reinterpret_cast<const float*>(Gs + L::TILE);
+    const bf16* Qs = reinterpret_cast<const bf16*>(stg) + 32 * qhalf * L::STR;
+    const bf16* Gs = reinterpret_cast<const bf16*>(stg) + L::TILE + 32 * qhalf * L::STR;
+    const float* Ls = reinterpret_cast<const float*>(stg + 2 * L::TILE * 2) + 32 * qhalf;
     const float* Ds = Ls + TQ;
-
-#pragma unroll
-    for (int qb = 0; qb < TQ / 32; ++qb) {
-      const int qa = q0 + 32 * qb;
-      const int state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + 32));
-      if (state == TILE_SKIP) continue;
-      f32x16 s[KB], dp[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
+    const int qa = q0 + 32 * qhalf;
+    const int state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + 32));
+    if (state != TILE_SKIP) {
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const bf16x8 aq = lds_read8(Qs + (32 * qb + l32) * L::STR + 16 * j + 8 * hh);
-        const bf16x8 ag = lds_read8(Gs + (32 * qb + l32) * L::STR + 16 * j + 8 * hh);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          s[kb] = mfma32(aq, kreg[kb][j], s[kb]);
-          dp[kb] = mfma32(ag, vreg[kb][j], dp[kb]);
-        }
+        const bf16x8 aq = lds_read8(Qs + l32 * L::STR + 16 * j + 8 * hh);
+        const bf16x8 ag = lds_read8(Gs + l32 * L::STR + 16 * j + 8 * hh);
+        const bf16x8 bv = lds_read8(Vrow + 16 * j);
+        bf16x8 bk;
+        if constexpr (KLDS) bk = lds_read8(Krow + 16 * j); else bk = kreg[j];
+        s = mfma32(aq, bk, s);
+        dp = mfma32(ag, bv, dp);
       }
       // Per-register query rows: q = qa + 8*(i/4) + 4*hh + i%4.
-      float lrow[16], drow[16];
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *FA_LDS(const f32x4, Ls + 32 * qb + 8 * g + 4 * hh);
-        const f32x4 d4 = *FA_LDS(const f32x4, Ds + 32 * qb + 8 * g + 4 * hh);
+      for (int st = 0; st < 2; ++st) {
+        float pe[8], de[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) { lrow[4 * g + u] = l4[u]; drow[4 * g + u] = d4[u]; }
-      }
-      bf16x8 pb[KB][2], dsb[KB][2];
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g = 2 * st + g2;
+          const f32x4 l4 = *FA_LDS(const f32x4, Ls + 8 * g + 4 * hh);
+          const f32x4 d4 = *FA_LDS(const f32x4, Ds + 8 * g + 4 * hh);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int key = kw + 32 * kb + l32;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          float pe[8], de[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int i = 8 * st + u;
-            float sv = s[kb][i];
+          for (int u = 0; u < 4; ++u) {
+            const int i = 4 * g + u;
+            float sv = s[i];
             if (state == TILE_PART) {
-              const int qi = qa + 8 * (i >> 2) + 4 * hh + (i & 3);
+              const int qi = qa + 8 * g + 4 * hh + u;
               if (!allowed(m, qi, key)) sv = -INFINITY;
             }
-            pe[u] = exp2_fast(sv * p.scale_log2 - lrow[i]);
-            de[u] = pe[u] * (dp[kb][i] - drow[i]);
+            const float pr = exp2_fast(sv * p.scale_log2 - l4[u]);
+            pe[4 * g2 + u] = pr;
+            de[4 * g2 + u] = pr * (dp[i] - d4[u]);
           }
-          pb[kb][st] = cat8(to_bf16x4(pe[0], pe[1], pe[2], pe[3]), to_bf16x4(pe[4], pe[5], pe[6], pe[7]));
-          dsb[kb][st] = cat8(to_bf16x4(de[0], de[1], de[2], de[3]), to_bf16x4(de[4], de[5], de[6], de[7]));
         }
+        pb[st] = cat8(to_bf16x4(pe[0], pe[1], pe[2], pe[3]), to_bf16x4(pe[4], pe[5], pe[6], pe[7]));
+        dsb[st] = cat8(to_bf16x4(de[0], de[1], de[2], de[3]), to_bf16x4(de[4], de[5], de[6], de[7]));
       }
       // dV^T += dO^T P,  dK^T += Q^T dS  (q-contraction, 16 rows per MFMA).
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int rbase = 32 * qb + 16 * st + 4 * hh + tr_row;
+        const int rbase = 16 * st + 4 * hh + tr_row;
 #pragma unroll
         for (int c = 0; c < NDB; ++c) {
           const int dcol = (D >= 32 ? 32 * c + tr_col : (tr_col & 15));
           bf16x8 ag = cat8(lds_read_tr4(Gs + rbase * L::STR + dcol), lds_read_tr4(Gs + (rbase + 8) * L::STR + dcol));
           bf16x8 aq = cat8(lds_read_tr4(Qs + rbase * L::STR + dcol), lds_read_tr4(Qs + (rbase + 8) * L::STR + dcol));
           if (!d_lane_ok) { ag = bf16x8{}; aq = bf16x8{}; }
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            dva[kb][c] = mfma32(ag, pb[kb][st], dva[kb][c]);
-            dka[kb][c] = mfma32(aq, dsb[kb][st], dka[kb][c]);
-          }
+          dva[c] = mfma32(ag, pb[st], dva[c]);
+          dka[c] = mfma32(aq, dsb[st], dka[c]);
         }
       }
     }
@@ -469,28 +482,42 @@ dkdv_kernel(Params p) {
     buf ^= 1;
   }
 
-  // dK = s * dK^T^T, dV = dV^T^T; lane (key, hh) holds d = 32c + 8g + 4hh + u.
+  // Pair reduction through LDS (the loop's last barrier freed it), then
+  // dK = s * (dK^T)^T, dV = (dV^T)^T; lane (key, hh) holds d = 32c + 8g + 4hh + u.
+  float* X = reinterpret_cast<float*>(smem);
   bf16* DKg = static_cast<bf16*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh;
   bf16* DVg = static_cast<bf16*>(const_cast<void*>(p.dv.ptr)) + b * p.dv.sb + hk * p.dv.sh;
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int key = kw + 32 * kb + l32;
-    if (key < p.Skv) {
+  for (int which = 0; which < 2; ++which) {
+    f32x16* acc = which == 0 ? dka : dva;
+    if (qhalf == 1) {
 #pragma unroll
       for (int c = 0; c < NDB; ++c)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = 32 * c + 8 * g + 4 * hh;
-          if (d < D) {
-            const float sc = p.scale;
-            *reinterpret_cast<bf16x4*>(DKg + (int64_t)key * p.dk.ss + d) =
-                to_bf16x4(dka[kb][c][4 * g] * sc, dka[kb][c][4 * g + 1] * sc, dka[kb][c][4 * g + 2] * sc,
-                          dka[kb][c][4 * g + 3] * sc);
-            *reinterpret_cast<bf16x4*>(DVg + (int64_t)key * p.dv.ss + d) =
-                to_bf16x4(dva[kb][c][4 * g], dva[kb][c][4 * g + 1], dva[kb][c][4 * g + 2], dva[kb][c][4 * g + 3]);
-          }
-        }
+        for (int i = 0; i < 16; ++i) X[((kblk * NDB + c) * 16 + i) * 64 + lane] = acc[c][i];
     }
+    __syncthreads();
+    if (qhalf == 0) {
+#pragma unroll
+      for (int c = 0; c < NDB; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[c][i] += X[((kblk * NDB + c) * 16 + i) * 64 + lane];
+      if (key < p.Skv) {
+        const float sc = which == 0 ? p.scale : 1.0f;
+        bf16* dst_row = (which == 0 ? DKg + (int64_t)key * p.dk.ss : DVg + (int64_t)key * p.dv.ss);
+#pragma unroll
+        for (int c = 0; c < NDB; ++c)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d = 32 * c + 8 * g + 4 * hh;
+            if (d < D)
+              *reinterpret_cast<bf16x4*>(dst_row + d) =
+                  to_bf16x4(acc[c][4 * g] * sc, acc[c][4 * g + 1] * sc, acc[c][4 * g + 2] * sc,
+                            acc[c][4 * g + 3] * sc);
+          }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -509,12 +536,14 @@ hipError_t launch_all(const Params& p, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {
-    constexpr int KB = 1, NW = 4, TKW = NW * KB * 32;
+    constexpr int NKB = 4, TKW = NKB * 32;
+    constexpr bool KLDS = D >= 128;
     const int64_t nblk = (int64_t)p.B * p.Hkv * ((p.Skv + TKW - 1) / TKW);
     if (nblk > 0) {
-      auto k = dkdv_kernel<D, KB, NW>;
-      if ((e = set_lds(k, KvLds<D>::BYTES)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NW * 64), KvLds<D>::BYTES, stream, p);
+      auto k = dkdv_kernel<D, NKB, KLDS>;
+      constexpr int lds = KvLds<D, NKB, KLDS>::BYTES;
+      if ((e = set_lds(k, lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NKB * 2 * 64), lds, stream, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
