@@ -100,6 +100,10 @@ fa_status check_tensor(const char* name, const fa_tensor& t, int n0, int n1, int
       return fail(FA_ERR_ALIGNMENT, "%s: stride %d (%lld elements) is not a multiple of 16 bytes",
                   name, i, (long long)st[i]);
   }
+  // The kernels address rows of one 64-row tile with 32-bit element offsets.
+  if (std::llabs(t.stride_s) >= (int64_t(1) << 24))
+    return fail(FA_ERR_UNSUPPORTED, "%s: sequence stride %lld elements is too large (limit 2^24)",
+                name, (long long)t.stride_s);
   if (output) {
     // No self-overlap: sort the outer dims by |stride|; each stride must
     // cover the extent of everything below it.

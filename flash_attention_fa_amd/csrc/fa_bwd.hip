@@ -48,35 +48,38 @@ __global__ void __launch_bounds__(256) delta_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // dQ: a workgroup owns NW*QB*32 query rows of one (batch, head) and streams
 // key tiles through LDS (as in the forward).  Transposed scores again: lane =
-// query column, so LSE and Delta are one scalar per lane.
+// query column, so LSE and Delta are one scalar per lane.  Each key tile is
+// staged three ways: K rows (for S^T = K Q^T), V rows (for dP^T = V dO^T) and
+// K transposed (for dQ^T = K^T dS^T).
 constexpr int DQ_TK = 64;
 
 template <int D>
 struct DqLds {
   static constexpr int KSTR = D + 8;
   static constexpr int VSTR = D + 8;
-  static constexpr int KTILE = DQ_TK * KSTR;
-  static constexpr int VTILE = DQ_TK * VSTR;
-  static constexpr int BYTES = 2 * (KTILE + VTILE) * 2;
+  static constexpr int KTILE = DQ_TK * KSTR;   // K rows
+  static constexpr int KTT = D * TSTR;         // K transposed
+  static constexpr int VTILE = DQ_TK * VSTR;   // V rows
+  static constexpr int BUF = KTILE + KTT + VTILE;
+  static constexpr int BYTES = 2 * BUF * 2;
 };
 
 template <int D, int QB, int NW>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64, 2)
 dq_kernel(Params p) {
   constexpr int NT = NW * 64;
   constexpr int TQ = NW * QB * 32;
   constexpr int TK = DQ_TK;
-  constexpr int DC = D / 8;
-  constexpr int CHUNKS = TK * DC;
-  constexpr int PER_T = (CHUNKS + NT - 1) / NT;
+  constexpr int HALF = NT / 2;               // threads staging K; the rest stage V
+  constexpr int UNITS = StageUnit<D>::COUNT;
+  constexpr int PER_T = (UNITS + HALF - 1) / HALF;
   constexpr int NDB = D >= 32 ? D / 32 : 1;
   constexpr int NJ = D / 16;
   using L = DqLds<D>;
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16* Ks = reinterpret_cast<bf16*>(smem);
-  bf16* Vs = Ks + 2 * L::KTILE;
+  bf16* const S0 = reinterpret_cast<bf16*>(smem);  // buffer b at S0 + b * L::BUF
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int nq = (p.Sq + TQ - 1) / TQ;
@@ -117,30 +120,39 @@ dq_kernel(Params p) {
 #pragma unroll
     for (int c = 0; c < NDB; ++c) acc[qb_][c] = f32x16{};
 
-  i32x4 kst[PER_T], vst[PER_T];
+  // Stage one key tile: the first half of the threads takes K (stored
+  // row-major and transposed), the second half V (row-major).
+  const bool stage_v = tid >= HALF;
+  const bf16* Sg = stage_v ? Vg : Kg;
+  const int64_t sss = stage_v ? p.v.ss : p.k.ss;
+  i32x4 stg[PER_T][4];
   auto fetch = [&](int t) {
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
-      const int c = tid + i * NT;
-      const int r = c / DC, c8 = c % DC;
-      const int key = t * TK + r;
-      if (c < CHUNKS && key_valid(m, key)) {
-        kst[i] = *reinterpret_cast<const i32x4*>(Kg + (int64_t)key * p.k.ss + 8 * c8);
-        vst[i] = *reinterpret_cast<const i32x4*>(Vg + (int64_t)key * p.v.ss + 8 * c8);
-      } else {
-        kst[i] = i32x4{};
-        vst[i] = i32x4{};
+      const int u = tid % HALF + i * HALF;
+      const StageUnit<D> su(u);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = t * TK + 4 * su.rg + r;
+        stg[i][r] = (u < UNITS && key_valid(m, key))
+                        ? *reinterpret_cast<const i32x4*>(Sg + (int64_t)key * sss + 8 * su.c8)
+                        : i32x4{};
       }
     }
   };
   auto store = [&](int buf) {
+    bf16* base = S0 + buf * L::BUF;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
-      const int c = tid + i * NT;
-      if (c < CHUNKS) {
-        const int r = c / DC, c8 = c % DC;
-        lds_write16(Ks + buf * L::KTILE + r * L::KSTR + 8 * c8, kst[i]);
-        lds_write16(Vs + buf * L::VTILE + r * L::VSTR + 8 * c8, vst[i]);
+      const int u = tid % HALF + i * HALF;
+      if (u < UNITS) {
+        const StageUnit<D> su(u);
+        if (stage_v) {
+          store_rows4(base + L::KTILE + L::KTT, L::VSTR, su.rg, su.c8, stg[i]);
+        } else {
+          store_rows4(base, L::KSTR, su.rg, su.c8, stg[i]);
+          store_trans4(base + L::KTILE, su.rg, su.c8, stg[i]);
+        }
       }
     }
   };
@@ -154,9 +166,8 @@ dq_kernel(Params p) {
   }
   __syncthreads();
 
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const bool d_lane_ok = D >= 32 || ((lane >> 4) & 1) == 0;
+  const bool d_lane_ok = D >= 32 || l32 < 16;
+  const int kt_row = d_lane_ok ? l32 : 0;
 
   while (walk.valid()) {
     const int t = walk.t;
@@ -167,8 +178,9 @@ dq_kernel(Params p) {
     const int k0 = t * TK;
     const int state = tile_state(m, k0, TK, wa, wb);
     if (state != TILE_SKIP) {
-      const bf16* Kt = Ks + buf * L::KTILE;
-      const bf16* Vt = Vs + buf * L::VTILE;
+      const bf16* Kt = S0 + buf * L::BUF;
+      const bf16* Ktt = Kt + L::KTILE;
+      const bf16* Vt = Ktt + L::KTT;
       f32x16 s[QB][2], dp[QB][2];
 #pragma unroll
       for (int qb_ = 0; qb_ < QB; ++qb_)
@@ -195,7 +207,7 @@ dq_kernel(Params p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-              if (!allowed(m, qi, key)) s[qb_][kb][i] = -INFINITY;
+              s[qb_][kb][i] = allowed(m, qi, key) ? s[qb_][kb][i] : -INFINITY;
             }
         }
       }
@@ -221,12 +233,9 @@ dq_kernel(Params p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const int kbase = 32 * kb + 16 * st + 4 * hh + tr_row;
 #pragma unroll
           for (int c = 0; c < NDB; ++c) {
-            const int dcol = (D >= 32 ? 32 * c + tr_col : (tr_col & 15));
-            bf16x8 a = cat8(lds_read_tr4(Kt + kbase * L::KSTR + dcol),
-                            lds_read_tr4(Kt + (kbase + 8) * L::KSTR + dcol));
+            bf16x8 a = lds_read8(Ktt + (32 * c + kt_row) * TSTR + 32 * kb + 16 * st + 8 * hh);
             if (!d_lane_ok) a = bf16x8{};
 #pragma unroll
             for (int qb_ = 0; qb_ < QB; ++qb_) acc[qb_][c] = mfma32(a, dsb[qb_][kb][st], acc[qb_][c]);
@@ -269,8 +278,10 @@ dq_kernel(Params p) {
 //
 // Two waves share each 32-key block: wave w takes key block w % NKB and the
 // (w / NKB)-th 32-row half of every 64-row query tile, so a SIMD runs two
-// waves and one hides the other's latency.  K^T stays in registers, V^T is
-// read from an LDS copy of the workgroup's V rows.  At the end the second
+// waves and one hides the other's latency.  K^T stays in registers (or, at
+// D = 128, in LDS beside V) and V^T is read from an LDS copy of the
+// workgroup's V rows.  Each query tile is staged row-major and transposed, so
+// every MFMA operand is one 16-byte LDS read.  At the end the second
 // wave of each pair hands its partial dK/dV to the first through LDS, which
 // adds it to its own (always in that order) and writes the result.
 constexpr int KV_TQ = 64;
@@ -278,13 +289,17 @@ constexpr int KV_TQ = 64;
 template <int D, int NKB, bool KLDS>
 struct KvLds {
   static constexpr int STR = D + 8;
-  static constexpr int TILE = KV_TQ * STR;                    // one Q or dO tile
-  static constexpr int STAGE = 2 * TILE * 2 + 2 * KV_TQ * 4;  // Q, dO, LSE, Delta
+  static constexpr int TILE = KV_TQ * STR;                    // Q or dO rows
+  static constexpr int TT = D * TSTR;                         // Q or dO transposed
+  // one stage: Q rows, Q^T, dO rows, dO^T (bf16), then LSE and Delta (fp32)
+  static constexpr int STAGE = 2 * (TILE + TT) * 2 + 2 * KV_TQ * 4;
   static constexpr int VROWS = NKB * 32;
   static constexpr int VBYTES = VROWS * STR * 2 * (KLDS ? 2 : 1);  // V rows (then K rows)
   static constexpr int NDB = D >= 32 ? D / 32 : 1;
   static constexpr int XBYTES = NKB * NDB * 16 * 64 * 4;      // one partial exchange
-  static constexpr int MAIN = 2 * STAGE + VBYTES;
+  // double-buffer the stage when it fits next to the K/V rows
+  static constexpr int NBUF = 2 * STAGE + VBYTES <= 160 * 1024 ? 2 : 1;
+  static constexpr int MAIN = NBUF * STAGE + VBYTES;
   static constexpr int BYTES = MAIN > XBYTES ? MAIN : XBYTES;
 };
 
@@ -296,16 +311,17 @@ dkdv_kernel(Params p) {
   constexpr int TKW = NKB * 32;       // keys per workgroup
   constexpr int TQ = KV_TQ;
   constexpr int DC = D / 8;
-  constexpr int CHUNKS = TQ * DC;
-  constexpr int PER_T = (CHUNKS + NT - 1) / NT;
+  constexpr int HALF = NT / 2;               // threads staging Q; the rest stage dO
+  constexpr int UNITS = StageUnit<D>::COUNT;
+  constexpr int PER_T = (UNITS + HALF - 1) / HALF;
   constexpr int NDB = D >= 32 ? D / 32 : 1;
   constexpr int NJ = D / 16;
   using L = KvLds<D, NKB, KLDS>;
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16* Vs = reinterpret_cast<bf16*>(smem + 2 * L::STAGE);
+  bf16* Vs = reinterpret_cast<bf16*>(smem + L::NBUF * L::STAGE);
   bf16* Ksh = Vs + L::VROWS * L::STR;  // K rows, when K^T is read from LDS
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hh = lane >> 5;
   const int kblk = wave % NKB, qhalf = wave / NKB;
 
@@ -355,24 +371,27 @@ dkdv_kernel(Params p) {
   const int ntile = t_last - t_first;
   const int nsteps = ntile * p.G;   // (head, query tile) pairs, head-major
 
-  i32x4 qst[PER_T], gst[PER_T];
+  // Stage layout: [Q rows | Q^T | dO rows | dO^T | LSE | Delta].
+  auto stage_ptr = [&](int buf) { return reinterpret_cast<bf16*>(smem + buf * L::STAGE); };
+  const bool stage_g = tid >= HALF;     // this thread stages dO (else Q)
+  i32x4 stg[PER_T][4];
   float lst = 0.f, dst = 0.f;
   auto fetch = [&](int step) {
     const int h = hk * p.G + step / ntile;
     const int q0 = (t_first + step % ntile) * TQ;
-    const bf16* Qg = static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
-    const bf16* Gg = static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh;
+    const bf16* Sg = stage_g ? static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh
+                             : static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
+    const int64_t sss = stage_g ? p.dout.ss : p.q.ss;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
-      const int c = tid + i * NT;
-      const int r = c / DC, c8 = c % DC;
-      const int row = q0 + r;
-      if (c < CHUNKS && row < p.Sq) {
-        qst[i] = *reinterpret_cast<const i32x4*>(Qg + (int64_t)row * p.q.ss + 8 * c8);
-        gst[i] = *reinterpret_cast<const i32x4*>(Gg + (int64_t)row * p.dout.ss + 8 * c8);
-      } else {
-        qst[i] = i32x4{};
-        gst[i] = i32x4{};
+      const int u = tid % HALF + i * HALF;
+      const StageUnit<D> su(u);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = q0 + 4 * su.rg + r;
+        stg[i][r] = (u < UNITS && row < p.Sq)
+                        ? *reinterpret_cast<const i32x4*>(Sg + (int64_t)row * sss + 8 * su.c8)
+                        : i32x4{};
       }
     }
     if (tid < TQ) {
@@ -383,21 +402,18 @@ dkdv_kernel(Params p) {
     }
   };
   auto store = [&](int buf) {
-    unsigned char* st = smem + buf * L::STAGE;
-    bf16* Qs = reinterpret_cast<bf16*>(st);
-    bf16* Gs = Qs + L::TILE;
-    float* Ls = reinterpret_cast<float*>(Gs + L::TILE);
-    float* Ds = Ls + TQ;
+    bf16* base = stage_ptr(buf) + (stage_g ? L::TILE + L::TT : 0);
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
-      const int c = tid + i * NT;
-      if (c < CHUNKS) {
-        const int r = c / DC, c8 = c % DC;
-        lds_write16(Qs + r * L::STR + 8 * c8, qst[i]);
-        lds_write16(Gs + r * L::STR + 8 * c8, gst[i]);
+      const int u = tid % HALF + i * HALF;
+      if (u < UNITS) {
+        const StageUnit<D> su(u);
+        store_rows4(base, L::STR, su.rg, su.c8, stg[i]);
+        store_trans4(base + L::TILE, su.rg, su.c8, stg[i]);
       }
     }
-    if (tid < TQ) { Ls[tid] = lst; Ds[tid] = dst; }
+    float* Ls = reinterpret_cast<float*>(stage_ptr(buf) + 2 * (L::TILE + L::TT));
+    if (tid < TQ) { Ls[tid] = lst; Ls[TQ + tid] = dst; }
   };
 
   int buf = 0;
@@ -407,9 +423,8 @@ dkdv_kernel(Params p) {
   }
   __syncthreads();
 
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const bool d_lane_ok = D >= 32 || ((lane >> 4) & 1) == 0;
+  const bool d_lane_ok = D >= 32 || l32 < 16;
+  const int t_row = d_lane_ok ? l32 : 0;
   const int key = kw + l32;
   const bf16* Vrow = Vs + (kblk * 32 + l32) * L::STR + 8 * hh;
   const bf16* Krow = Ksh + (kblk * 32 + l32) * L::STR + 8 * hh;
@@ -417,10 +432,12 @@ dkdv_kernel(Params p) {
   for (int step = 0; step < nsteps; ++step) {
     if (step + 1 < nsteps) fetch(step + 1);
     const int q0 = (t_first + step % ntile) * TQ;
-    const unsigned char* stg = smem + buf * L::STAGE;
-    const bf16* Qs = reinterpret_cast<const bf16*>(stg) + 32 * qhalf * L::STR;
-    const bf16* Gs = reinterpret_cast<const bf16*>(stg) + L::TILE + 32 * qhalf * L::STR;
-    const float* Ls = reinterpret_cast<const float*>(stg + 2 * L::TILE * 2) + 32 * qhalf;
+    const bf16* stg0 = stage_ptr(buf);
+    const bf16* Qs = stg0 + 32 * qhalf * L::STR;
+    const bf16* Qt = stg0 + L::TILE;
+    const bf16* Gs = stg0 + L::TILE + L::TT + 32 * qhalf * L::STR;
+    const bf16* Gt = stg0 + 2 * L::TILE + L::TT;
+    const float* Ls = reinterpret_cast<const float*>(stg0 + 2 * (L::TILE + L::TT)) + 32 * qhalf;
     const float* Ds = Ls + TQ;
     const int qa = q0 + 32 * qhalf;
     const int state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + 32));
@@ -452,7 +469,7 @@ dkdv_kernel(Params p) {
             float sv = s[i];
             if (state == TILE_PART) {
               const int qi = qa + 8 * g + 4 * hh + u;
-              if (!allowed(m, qi, key)) sv = -INFINITY;
+              sv = allowed(m, qi, key) ? sv : -INFINITY;
             }
             const float pr = exp2_fast(sv * p.scale_log2 - l4[u]);
             pe[4 * g2 + u] = pr;
@@ -462,24 +479,32 @@ dkdv_kernel(Params p) {
         pb[st] = cat8(to_bf16x4(pe[0], pe[1], pe[2], pe[3]), to_bf16x4(pe[4], pe[5], pe[6], pe[7]));
         dsb[st] = cat8(to_bf16x4(de[0], de[1], de[2], de[3]), to_bf16x4(de[4], de[5], de[6], de[7]));
       }
-      // dV^T += dO^T P,  dK^T += Q^T dS  (q-contraction, 16 rows per MFMA).
+      // dV^T += dO^T P,  dK^T += Q^T dS  (q-contraction, 16 rows per MFMA),
+      // operands from the transposed copies.
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int rbase = 16 * st + 4 * hh + tr_row;
+        const int pos = 32 * qhalf + 16 * st + 8 * hh;
 #pragma unroll
         for (int c = 0; c < NDB; ++c) {
-          const int dcol = (D >= 32 ? 32 * c + tr_col : (tr_col & 15));
-          bf16x8 ag = cat8(lds_read_tr4(Gs + rbase * L::STR + dcol), lds_read_tr4(Gs + (rbase + 8) * L::STR + dcol));
-          bf16x8 aq = cat8(lds_read_tr4(Qs + rbase * L::STR + dcol), lds_read_tr4(Qs + (rbase + 8) * L::STR + dcol));
+          bf16x8 ag = lds_read8(Gt + (32 * c + t_row) * TSTR + pos);
+          bf16x8 aq = lds_read8(Qt + (32 * c + t_row) * TSTR + pos);
           if (!d_lane_ok) { ag = bf16x8{}; aq = bf16x8{}; }
           dva[c] = mfma32(ag, pb[st], dva[c]);
           dka[c] = mfma32(aq, dsb[st], dka[c]);
         }
       }
     }
-    if (step + 1 < nsteps) store(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+    if constexpr (L::NBUF == 2) {
+      if (step + 1 < nsteps) store(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    } else {
+      __syncthreads();
+      if (step + 1 < nsteps) {
+        store(0);
+        __syncthreads();
+      }
+    }
   }
 
   // Pair reduction through LDS (the loop's last barrier freed it), then
@@ -526,6 +551,17 @@ hipError_t set_lds(K k, int bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+template <int D, int QB, int NW>
+hipError_t launch_dq(const Params& p, hipStream_t stream) {
+  constexpr int TQ = NW * QB * 32;
+  const int64_t nblk = (int64_t)p.B * p.Hq * ((p.Sq + TQ - 1) / TQ);
+  auto k = dq_kernel<D, QB, NW>;
+  hipError_t e = set_lds(k, DqLds<D>::BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NW * 64), DqLds<D>::BYTES, stream, p);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_all(const Params& p, hipStream_t stream) {
   hipError_t e;
@@ -547,15 +583,11 @@ hipError_t launch_all(const Params& p, hipStream_t stream) {
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  {
-    constexpr int QB = D >= 128 ? 1 : 2, NW = D >= 128 ? 8 : 4, TQ = NW * QB * 32;
-    const int64_t nblk = (int64_t)p.B * p.Hq * ((p.Sq + TQ - 1) / TQ);
-    if (nblk > 0) {
-      auto k = dq_kernel<D, QB, NW>;
-      if ((e = set_lds(k, DqLds<D>::BYTES)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NW * 64), DqLds<D>::BYTES, stream, p);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+  if (p.B > 0 && p.Sq > 0) {
+    // 8-wave workgroups when there are enough to fill the chip twice over
+    const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
+    if ((e = wg8 >= 512 ? launch_dq<D, 1, 8>(p, stream) : launch_dq<D, 1, 4>(p, stream)) != hipSuccess)
+      return e;
   }
   return hipSuccess;
 }

@@ -70,12 +70,134 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 __device__ __forceinline__ void lds_write16(bf16* p, i32x4 v) { *FA_LDS(i32x4, p) = v; }
+__device__ __forceinline__ void lds_write8(bf16* p, uint2 v) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 w;
+  w[0] = v.x;
+  w[1] = v.y;
+  *FA_LDS(u32x2, p) = w;
+}
 
 // Four fp32 accumulator values -> 4 bf16 (round to nearest even).
 __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
   bf16x4 r;
   r[0] = (bf16)a; r[1] = (bf16)b; r[2] = (bf16)c; r[3] = (bf16)d;
   return r;
+}
+
+// --------------------------------------------------------------------------
+// Tile staging.  A 64-row tile of a row-major [rows][D] bf16 matrix is moved
+// into LDS in units of 4 rows x 8 columns: each thread loads 4 x 16 bytes and
+// writes a row-major copy and/or a transposed copy ([D][64], row stride
+// TSTR) in which, inside every group of 16 rows, bits 2 and 3 of the row
+// index are swapped.  That order makes the 8 values one MFMA k-step needs
+// (two runs of 4 in the 32x32 accumulator layout) contiguous, so the
+// transposed operand is a single 16-byte LDS read.  The unit -> lane map keeps
+// 16 consecutive lanes on distinct bank slots for the row-major writes and at
+// most two lanes per slot for the 8-byte transposed writes.
+
+constexpr int STAGE_ROWS = 64;
+constexpr int TSTR = STAGE_ROWS + 8;   // transposed-copy row stride (elements)
+
+__device__ __forceinline__ int tpos(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+template <int D>
+struct StageUnit {
+  static constexpr int COUNT = (STAGE_ROWS / 4) * (D / 8);
+  int rg, c8;  // rows 4*rg .. 4*rg+3, columns 8*c8 .. 8*c8+7
+  __device__ __forceinline__ explicit StageUnit(int u) {
+    const int lam = u & 63, hi = u >> 6;
+    if constexpr (D / 8 >= 4) {
+      rg = 4 * (lam >> 4) + ((lam >> 2) & 3);
+      c8 = (lam & 3) + 4 * hi;
+    } else {
+      rg = lam / (D / 8);
+      c8 = lam % (D / 8);
+    }
+  }
+};
+
+// Transposes a 4 x 8 bf16 block (4 rows of 8) into 8 columns of 4.
+__device__ __forceinline__ void transpose4x8(const i32x4 (&in)[4], uint2 (&out)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const unsigned a0 = in[0][e], a1 = in[1][e], a2 = in[2][e], a3 = in[3][e];
+    out[2 * e].x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+    out[2 * e].y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+    out[2 * e + 1].x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+    out[2 * e + 1].y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+  }
+}
+
+__device__ __forceinline__ void store_rows4(bf16* X, int xstr, int rg, int c8, const i32x4 (&v)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lds_write16(X + (4 * rg + r) * xstr + 8 * c8, v[r]);
+}
+
+__device__ __forceinline__ void store_trans4(bf16* Xt, int rg, int c8, const i32x4 (&v)[4]) {
+  uint2 t[8];
+  transpose4x8(v, t);
+  const int pos = tpos(4 * rg);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) lds_write8(Xt + (8 * c8 + e) * TSTR + pos, t[e]);
+}
+
+// --------------------------------------------------------------------------
+// Asynchronous tile staging (HBM -> LDS without registers).  A 64-row tile of
+// a row-major [rows][D] bf16 matrix is stored unpadded; inside each row the
+// 16-byte chunk c lives at slot c ^ swz(row), which keeps both the row reads
+// (16 rows x one chunk) and the transposing reads (4 rows x 64 bytes) free of
+// bank conflicts.  One load instruction moves 64 chunks (1 KB, contiguous in
+// LDS): each lane fetches the global chunk that belongs in its slot.
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else if constexpr (D == 32) return (r >> 2) & 3;
+  else return (r >> 3) & 1;
+}
+
+// Byte offset of element e (multiple of 4) of row r inside a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int e) {
+  return r * (2 * D) + 16 * ((e >> 3) ^ swz<D>(r)) + 2 * (e & 7);
+}
+
+// One asynchronous 1 KB copy: lane l's 16 bytes at g land at lds_base + 16 l.
+// Issued through inline assembly so the compiler does not treat every later
+// LDS read as possibly aliasing the copy (it would drain all outstanding
+// copies before each read); completion is awaited explicitly with
+// wait_vmcnt() and ordered across waves by barrier_lds().  M0 carries the LDS
+// address; one wait state separates its write from the copy.
+__device__ __forceinline__ void lds_dma16(const void* g, unsigned char* lds_base) {
+  const unsigned lds_addr = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (<= n).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0), others free
+}
+// Workgroup barrier that does not wait for outstanding HBM loads (the caller
+// has waited for the ones it needs); a compiler fence keeps LDS accesses on
+// their side of it.
+__device__ __forceinline__ void barrier_lds() {
+  wait_lgkm0();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // --------------------------------------------------------------------------
@@ -98,15 +220,23 @@ __device__ __forceinline__ MaskB resolve_mask(const Params& p, int b) {
   return m;
 }
 
-// May query i attend key j?  (The three mask kinds of fa.h.)
+// May query i attend key j?  (The three mask kinds of fa.h.)  Written
+// without per-lane branches (the mask kind is uniform), so callers can use it
+// as a select on score registers.
 __device__ __forceinline__ bool allowed(const MaskB& m, int i, int j) {
-  if (m.kind == MASK_FULL) return j < m.kvv;
-  const bool causal = (j <= i - m.shift) && (j < m.kvv);
-  if (m.kind == MASK_CAUSAL || causal) return causal;
+  const bool valid = j < m.kvv;
+  if (m.kind == MASK_FULL) return valid;
+  const bool causal = (j <= i - m.shift) & valid;
+  if (m.kind == MASK_CAUSAL) return causal;
   // TTT suffix: key of a later step at the query's own position.
-  if (j < m.L) return false;
-  const int jm = j % m.L;
-  return jm == i && jm < m.kvv;
+  const int jm = j - (j / m.L) * m.L;
+  return causal | ((j >= m.L) & (jm == i) & (jm < m.kvv));
+}
+
+// The wave index as a provably uniform (scalar) value, so everything derived
+// from it (tile ranges, tile states, loop bounds) stays in scalar registers.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
 // Is key j a real key (its K/V row may be used at all)?

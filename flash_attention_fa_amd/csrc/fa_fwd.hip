@@ -9,48 +9,54 @@
 // max and normaliser (CS336 "Flash Attention (Triton)", How it works) so only
 // O and LSE ever reach HBM (ggml flash-attn-training playbook, section 1).
 //
-// Work split.  A workgroup owns NW*QB*32 query rows of one (batch, head); each
-// wave owns QB blocks of 32 rows.  Keys stream through LDS in tiles of 64,
-// double-buffered: tile t+1 is fetched into registers while tile t is used.
+// Work split.  A workgroup owns NW*32 query rows of one (batch, head); each
+// wave owns one block of 32 rows.  Keys stream through LDS in tiles of 64.
 // Scores are computed transposed, S^T = K Q^T, so each lane owns one query
 // column and 16 keys of it: the row max and row sum are in-lane reductions
 // plus one cross-half swap, and the softmax scale, max and normaliser are one
 // scalar per lane.  O^T = V^T P^T then takes P straight from the score
-// registers (the key order inside each 16-key MFMA step is permuted the same
-// way in both operands) and V^T straight from the row-major V tile with the
-// transposing LDS read.
+// registers and V^T from a transposed copy of the V tile that the workgroup
+// writes once per tile (keys inside each 16-key MFMA step ordered the way the
+// score registers hold them), so both operands of both products are single
+// 16-byte LDS reads.
+//
+// Pipeline.  Four LDS buffers hold tiles i .. i+3.  K and V rows are copied
+// HBM -> LDS asynchronously (no registers, no vector instructions) three tiles
+// ahead; iteration i issues the QK^T products of tile i+1, then the
+// exponentials of tile i (independent of those products, so the matrix cores
+// and the vector ALUs work at once inside one wave), then the PV products of
+// tile i, with V^T read transposed from the row-major V tile; the mask, max
+// and (rare) rescale of tile i+1 close the iteration.  One barrier per tile,
+// which waits only for the copies of tile i+2.
 #include "fa_device.h"
 
 namespace fa {
 namespace {
 
-constexpr int TK = 64;  // keys per LDS tile
+constexpr int TK = 64;    // keys per LDS tile
+constexpr int NBUF = 4;   // tiles in flight in LDS
 
 template <int D>
 struct FwdLds {
-  static constexpr int KSTR = D + 8;                     // K row stride (elements)
-  static constexpr int VSTR = D >= 64 ? D + 32 : D;      // V row stride (elements)
-  static constexpr int KTILE = TK * KSTR;
-  static constexpr int VTILE = TK * VSTR;
-  static constexpr int BYTES = 2 * (KTILE + VTILE) * 2;  // two buffers, bf16
+  static constexpr int TILE_BYTES = TK * D * 2;          // one K or V tile, swizzled rows
+  static constexpr int BUF = 2 * TILE_BYTES;             // K then V
+  static constexpr int BYTES = NBUF * BUF;
 };
 
-template <int D, int QB, int NW>
-__global__ void __launch_bounds__(NW * 64)
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64, 2)
 fwd_kernel(Params p) {
-  constexpr int NT = NW * 64;
-  constexpr int TQ = NW * QB * 32;
-  constexpr int DC = D / 8;                  // 16-byte chunks per row
-  constexpr int CHUNKS = TK * DC;            // chunks per K (or V) tile
-  constexpr int PER_T = (CHUNKS + NT - 1) / NT;
+  constexpr int TQ = NW * 32;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;              // rows per 1 KB copy instruction
+  constexpr int NINS = TK / RPI;             // copy instructions per tile per tensor
+  constexpr int LPW = (2 * NINS + NW - 1) / NW;  // copy instructions per wave per tile
   constexpr int NDB = D >= 32 ? D / 32 : 1;  // 32-wide d blocks of O^T
   constexpr int NJ = D / 16;                 // 16-wide d steps of S^T
   using L = FwdLds<D>;
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16* Ks = reinterpret_cast<bf16*>(smem);
-  bf16* Vs = Ks + 2 * L::KTILE;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int nq = (p.Sq + TQ - 1) / TQ;
@@ -61,211 +67,224 @@ fwd_kernel(Params p) {
   const MaskB m = resolve_mask(p, b);
 
   const int qa = qtile * TQ, qb = min(p.Sq, qa + TQ);
-  const int wa = qa + wave * QB * 32, wb = min(p.Sq, wa + QB * 32);
+  const int wa = qa + wave * 32, wb = min(p.Sq, wa + 32);
+  const int qi = wa + l32;                  // this lane's query row
 
   const bf16* Qg = static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
   const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
   const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
 
   // Q^T as the B operand: lane (q = l32, half hh) holds Q[q][16j + 8hh .. +8].
-  bf16x8 qreg[QB][NJ];
+  bf16x8 qreg[NJ];
 #pragma unroll
-  for (int qb_ = 0; qb_ < QB; ++qb_) {
-    const int row = wa + qb_ * 32 + l32;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if (row < p.Sq)
-        qreg[qb_][j] = *reinterpret_cast<const bf16x8*>(Qg + (int64_t)row * p.q.ss + 16 * j + 8 * hh);
-      else
-        qreg[qb_][j] = bf16x8{};
-    }
-  }
+  for (int j = 0; j < NJ; ++j)
+    qreg[j] = qi < p.Sq ? *reinterpret_cast<const bf16x8*>(Qg + (int64_t)qi * p.q.ss + 16 * j + 8 * hh)
+                        : bf16x8{};
+  wait_vmcnt<0>();  // Q is in registers before any copy is queued behind it
 
-  f32x16 acc[QB][NDB];
-  float mrun[QB], lsum[QB];
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int qb_ = 0; qb_ < QB; ++qb_) {
-    mrun[qb_] = kMaxInit;
-    lsum[qb_] = 0.f;
-#pragma unroll
-    for (int c = 0; c < NDB; ++c) acc[qb_][c] = f32x16{};
-  }
+  for (int c = 0; c < NDB; ++c) acc[c] = f32x16{};
+  float mrun = kMaxInit, lsum = 0.f;
 
-  // Stage one key tile into registers (zero rows for keys that are not real).
-  i32x4 kst[PER_T], vst[PER_T];
-  auto fetch = [&](int t) {
+  // Asynchronous copy of key tile t into buffer k: this wave's share of the
+  // 2 * NINS instructions (K rows first, then V rows).  Rows that are not
+  // real keys (and every row when t < 0) are fetched from key 0 instead: a
+  // real row, so the values are finite, and the mask zeroes their weights.
+  // (Only reached when the tile has a real key, so key 0 is real.)
+  const int my_ins = wave * LPW < 2 * NINS ? LPW : 0;   // copies per tile, this wave
+  const int crow = lane / CPR, cslot = lane % CPR;
+  // Per-lane, per-copy constants: element offset of this lane's chunk inside
+  // a tile (row offset + swizzled chunk) and of the same chunk in key 0.
+  int roff[LPW], zoff[LPW];
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int c = tid + i * NT;
-      const int r = c / DC, c8 = c % DC;
-      const int key = t * TK + r;
-      if (c < CHUNKS && key_valid(m, key)) {
-        kst[i] = *reinterpret_cast<const i32x4*>(Kg + (int64_t)key * p.k.ss + 8 * c8);
-        vst[i] = *reinterpret_cast<const i32x4*>(Vg + (int64_t)key * p.v.ss + 8 * c8);
-      } else {
-        kst[i] = i32x4{};
-        vst[i] = i32x4{};
+  for (int x = 0; x < LPW; ++x) {
+    const int idx = wave * LPW + x;
+    const int ii = idx % NINS;
+    const int row = ii * RPI + crow;
+    const int gch = cslot ^ swz<D>(row);
+    const int64_t ss = idx / NINS == 0 ? p.k.ss : p.v.ss;
+    roff[x] = (int)(row * ss) + 8 * gch;
+    zoff[x] = 8 * gch;
+  }
+  const bool ttt = m.kind == MASK_TTT;
+  auto copy_tile = [&](int t, int k) {
+    const int tb = t * TK;
+    const int lim = t >= 0 ? m.kvv - tb : 0;   // rows below lim are real keys (FULL/CAUSAL)
+#pragma unroll
+    for (int x = 0; x < LPW; ++x) {
+      const int idx = wave * LPW + x;
+      if (idx < 2 * NINS) {
+        const int tensor = idx / NINS, ii = idx % NINS;
+        const int row = ii * RPI + crow;
+        const bool ok = ttt ? (t >= 0 && key_valid(m, tb + row)) : row < lim;
+        const bf16* base = tensor == 0 ? Kg : Vg;
+        const int64_t ss = tensor == 0 ? p.k.ss : p.v.ss;
+        const bf16* g = ok ? base + (int64_t)tb * ss + roff[x] : base + zoff[x];
+        lds_dma16(g, smem + k * L::BUF + tensor * L::TILE_BYTES + ii * 1024);
       }
     }
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int c = tid + i * NT;
-      if (c < CHUNKS) {
-        const int r = c / DC, c8 = c % DC;
-        lds_write16(Ks + buf * L::KTILE + r * L::KSTR + 8 * c8, kst[i]);
-        lds_write16(Vs + buf * L::VTILE + r * L::VSTR + 8 * c8, vst[i]);
-      }
-    }
+  // Waits until this wave's copies of all but the newest tile have landed.
+  auto wait_copies = [&]() {
+    if (my_ins == LPW) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
   };
 
-  TileWalk walk;
-  walk.start(m, qa, qb, TK);
-  int buf = 0;
-  if (walk.valid()) {
-    fetch(walk.t);
-    store(0);
-  }
-  __syncthreads();
-
-  // Per-lane addressing inside a tile.
-  const int tr_row = (lane & 15) >> 2;                 // row offset within a 4-key run
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const bool d_lane_ok = D >= 32 || ((lane >> 4) & 1) == 0;
-
-  while (walk.valid()) {
-    const int t = walk.t;
-    TileWalk nxt = walk;
-    nxt.next(m, qa, qb, TK);
-    if (nxt.valid()) fetch(nxt.t);
-
+  // S^T of one tile: 2 key blocks of 32.
+  auto qk = [&](int k, f32x16 (&s)[2]) {
+    const unsigned char* Kt = smem + k * L::BUF;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *FA_LDS(const bf16x8, Kt + swz_off<D>(32 * kb + l32, 16 * j + 8 * hh));
+        s[kb] = mfma32(a, qreg[j], s[kb]);
+      }
+  };
+  // Mask of tile t, then the running max; the accumulators are rescaled only
+  // when some row's max grows by more than kRescaleSlack powers of two.
+  auto prep = [&](int t, f32x16 (&s)[2]) {
     const int k0 = t * TK;
     const int state = tile_state(m, k0, TK, wa, wb);
-    if (state != TILE_SKIP) {
-      const bf16* Kt = Ks + buf * L::KTILE;
-      const bf16* Vt = Vs + buf * L::VTILE;
-      // S^T = K Q^T : 2 key blocks of 32, QB query blocks.
-      f32x16 s[QB][2];
-#pragma unroll
-      for (int qb_ = 0; qb_ < QB; ++qb_) { s[qb_][0] = f32x16{}; s[qb_][1] = f32x16{}; }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = lds_read8(Kt + (32 * kb + l32) * L::KSTR + 16 * j + 8 * hh);
-#pragma unroll
-          for (int qb_ = 0; qb_ < QB; ++qb_) s[qb_][kb] = mfma32(a, qreg[qb_][j], s[qb_][kb]);
-        }
-      }
-      if (state == TILE_PART) {
-#pragma unroll
-        for (int qb_ = 0; qb_ < QB; ++qb_) {
-          const int qi = wa + qb_ * 32 + l32;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-              if (!allowed(m, qi, key)) s[qb_][kb][i] = -INFINITY;
-            }
-        }
-      }
-      // Online softmax, lazily rescaled.
-      bf16x8 pb[QB][2][2];
-#pragma unroll
-      for (int qb_ = 0; qb_ < QB; ++qb_) {
-        float mx = s[qb_][0][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[qb_][0][i]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb_][1][i]);
-        mx = half_swap_max(mx) * p.scale_log2;
-        if (__any(mx > mrun[qb_] + kRescaleSlack)) {
-          const float mn = fmaxf(mrun[qb_], mx);
-          const float alpha = exp2_fast(mrun[qb_] - mn);
-          mrun[qb_] = mn;
-          lsum[qb_] *= alpha;
-#pragma unroll
-          for (int c = 0; c < NDB; ++c)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[qb_][c][i] *= alpha;
-        }
-        const float mcur = mrun[qb_];
-        float ls = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            float e[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              e[u] = exp2_fast(s[qb_][kb][8 * st + u] * p.scale_log2 - mcur);
-              ls += e[u];
-            }
-            const bf16x4 lo = to_bf16x4(e[0], e[1], e[2], e[3]);
-            const bf16x4 hi = to_bf16x4(e[4], e[5], e[6], e[7]);
-            pb[qb_][kb][st] = cat8(lo, hi);
-          }
-        lsum[qb_] += ls;
-      }
-      // O^T += V^T P^T.
+    if (state != TILE_FULL) {
+      const bool skip = state == TILE_SKIP;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int kbase = 32 * kb + 16 * st + 4 * hh + tr_row;
-#pragma unroll
-          for (int c = 0; c < NDB; ++c) {
-            const int dcol = (D >= 32 ? 32 * c + tr_col : (tr_col & 15));
-            bf16x8 a = cat8(lds_read_tr4(Vt + kbase * L::VSTR + dcol),
-                            lds_read_tr4(Vt + (kbase + 8) * L::VSTR + dcol));
-            if (!d_lane_ok) a = bf16x8{};
-#pragma unroll
-            for (int qb_ = 0; qb_ < QB; ++qb_) acc[qb_][c] = mfma32(a, pb[qb_][kb][st], acc[qb_][c]);
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
+          s[kb][i] = (!skip && allowed(m, qi, key)) ? s[kb][i] : -INFINITY;
         }
     }
+    float mx = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    mx = half_swap_max(mx) * p.scale_log2;
+    if (__any(mx > mrun + kRescaleSlack)) {
+      const float mn = fmaxf(mrun, mx);
+      const float alpha = exp2_fast(mrun - mn);
+      mrun = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int c = 0; c < NDB; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[c][i] *= alpha;
+    }
+  };
 
-    if (nxt.valid()) store(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    walk = nxt;
+  // Transposing reads of V: lane r of each 16-lane group points at row
+  // kbase + r/4, column dcol + 4*(r%4); lanes whose d column does not exist
+  // (D = 16) read a real column and use zeros.
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const bool d_lane_ok = D >= 32 || ((lane >> 4) & 1) == 0;
+
+  // Tiles i (cur) .. i+3 (nx3) of the walk.
+  TileWalk cur;
+  cur.start(m, qa, qb, TK);
+  TileWalk nx1 = cur;
+  if (nx1.valid()) nx1.next(m, qa, qb, TK);
+  TileWalk nx2 = nx1;
+  if (nx2.valid()) nx2.next(m, qa, qb, TK);
+  TileWalk nx3 = nx2;
+  if (nx3.valid()) nx3.next(m, qa, qb, TK);
+
+  f32x16 scur[2], snxt[2];
+  int kbuf = 0;  // LDS buffer of the current tile
+  if (cur.valid()) {
+    copy_tile(cur.t, 0);
+    copy_tile(nx1.valid() ? nx1.t : -1, 1);
+    copy_tile(nx2.valid() ? nx2.t : -1, 2);
+    wait_copies();
+  }
+  barrier_lds();
+  if (cur.valid()) {
+    qk(0, scur);
+    prep(cur.t, scur);
+  }
+
+  while (cur.valid()) {
+    const int k1 = (kbuf + 1) & (NBUF - 1);
+    copy_tile(nx3.valid() ? nx3.t : -1, (kbuf + 3) & (NBUF - 1));
+    // QK^T of tile i+1 (its buffer may hold a stale tile at the end: unused).
+    qk(k1, snxt);
+    // P of tile i, rounded to bf16 for the PV product.
+    bf16x8 pb[2][2];
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          e[u] = exp2_fast(scur[kb][8 * st + u] * p.scale_log2 - mrun);
+          ls += e[u];
+        }
+        pb[kb][st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
+      }
+    lsum += ls;
+    // O^T += V^T P^T.
+    const unsigned char* Vt = smem + kbuf * L::BUF + L::TILE_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int kbase = 32 * kb + 16 * st + 4 * hh + tr_row;
+#pragma unroll
+        for (int c = 0; c < NDB; ++c) {
+          const int dcol = D >= 32 ? 32 * c + tr_col : (tr_col & 15);
+          bf16x8 a = cat8(lds_read_tr4(reinterpret_cast<const bf16*>(Vt + swz_off<D>(kbase, dcol))),
+                          lds_read_tr4(reinterpret_cast<const bf16*>(Vt + swz_off<D>(kbase + 8, dcol))));
+          if (!d_lane_ok) a = bf16x8{};
+          acc[c] = mfma32(a, pb[kb][st], acc[c]);
+        }
+      }
+    if (nx1.valid()) prep(nx1.t, snxt);
+    wait_copies();
+    barrier_lds();
+    scur[0] = snxt[0];
+    scur[1] = snxt[1];
+    kbuf = k1;
+    cur = nx1;
+    nx1 = nx2;
+    nx2 = nx3;
+    if (nx3.valid()) nx3.next(m, qa, qb, TK);
   }
 
   // Epilogue: O = acc / l, LSE = ln(sum exp(scaled scores)); empty rows -> 0.
   bf16* Og = static_cast<bf16*>(const_cast<void*>(p.o.ptr)) + b * p.o.sb + h * p.o.sh;
   float* Lg = p.lse + ((int64_t)b * p.Hq + h) * p.Sq;
+  const float lt = half_swap_sum(lsum);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qi < p.Sq) {
+    if (hh == 0) Lg[qi] = lt > 0.f ? (mrun + log2_fast(lt)) * kLn2 : 0.f;
 #pragma unroll
-  for (int qb_ = 0; qb_ < QB; ++qb_) {
-    const int row = wa + qb_ * 32 + l32;
-    const float lt = half_swap_sum(lsum[qb_]);
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    if (row < p.Sq) {
-      if (hh == 0) Lg[row] = lt > 0.f ? (mrun[qb_] + log2_fast(lt)) * kLn2 : 0.f;
+    for (int c = 0; c < NDB; ++c)
 #pragma unroll
-      for (int c = 0; c < NDB; ++c)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = 32 * c + 8 * g + 4 * hh;
-          if (d < D) {
-            const bf16x4 o = to_bf16x4(acc[qb_][c][4 * g] * inv, acc[qb_][c][4 * g + 1] * inv,
-                                       acc[qb_][c][4 * g + 2] * inv, acc[qb_][c][4 * g + 3] * inv);
-            *reinterpret_cast<bf16x4*>(Og + (int64_t)row * p.o.ss + d) = o;
-          }
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * c + 8 * g + 4 * hh;
+        if (d < D) {
+          const bf16x4 o = to_bf16x4(acc[c][4 * g] * inv, acc[c][4 * g + 1] * inv,
+                                     acc[c][4 * g + 2] * inv, acc[c][4 * g + 3] * inv);
+          *reinterpret_cast<bf16x4*>(Og + (int64_t)qi * p.o.ss + d) = o;
         }
-    }
+      }
   }
 }
 
-template <int D, int QB, int NW>
+template <int D, int NW>
 hipError_t launch(const Params& p, hipStream_t stream) {
-  constexpr int TQ = NW * QB * 32;
+  constexpr int TQ = NW * 32;
   const int nq = (p.Sq + TQ - 1) / TQ;
   const int64_t nblk = (int64_t)p.B * p.Hq * nq;
   if (nblk == 0) return hipSuccess;
   const int lds = FwdLds<D>::BYTES;
-  auto k = fwd_kernel<D, QB, NW>;
+  auto k = fwd_kernel<D, NW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
@@ -273,14 +292,23 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// 8-wave workgroups (256 query rows) when there are enough of them to fill
+// the chip twice over, 4-wave ones (128 rows) for small problems.
+template <int D>
+hipError_t launch_d(const Params& p, hipStream_t s) {
+  const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
+  if (wg8 >= 512) return launch<D, 8>(p, s);
+  return launch<D, 4>(p, s);
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t s) {
   switch (p.D) {
-    case 16: return launch<16, 2, 4>(p, s);
-    case 32: return launch<32, 2, 4>(p, s);
-    case 64: return launch<64, 2, 4>(p, s);
-    case 128: return launch<128, 1, 8>(p, s);
+    case 16: return launch_d<16>(p, s);
+    case 32: return launch_d<32>(p, s);
+    case 64: return launch_d<64>(p, s);
+    case 128: return launch_d<128>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -63,7 +63,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1,  /* NULL pointer, non-positive size, Hq % Hkv != 0,
                               TTT with Skv % Sq != 0, negative shift,
                               workspace too small, unit D stride violated */
-  FA_ERR_UNSUPPORTED = 2,  /* D not in {16, 32, 64, 128}, unknown dtype/kind */
+  FA_ERR_UNSUPPORTED = 2,  /* D not in {16, 32, 64, 128}, unknown dtype/kind,
+                              sequence stride of 2^24 elements or more */
   FA_ERR_ALIGNMENT = 3,    /* base pointer or B/H/S stride not 16-byte aligned */
   FA_ERR_ALIAS = 4,        /* an output's byte range overlaps an input's */
   FA_ERR_HIP = 5           /* no usable device, or a launch failed */
