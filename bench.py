@@ -8,12 +8,28 @@ allowed (query, key) pairs only: 4*D flop per pair forward, 10*D backward
 (the five contractions QK^T, PV, dO V^T, P^T dO, dS K / dS^T Q), 14*D in all.
 
 Prints one JSON line: the metric, the per-step time, fwd / bwd / fwd+bwd
-TFLOP/s and their fraction of the 2516.6 TFLOP/s dense bf16 peak, the
-roofline of the dominant kernel (timed with HIP events on the launch
-stream), the peak device memory, and the fp64 oracle timed on a bounded
-sample of the same workload on the host CPU.
+TFLOP/s and their fraction of the 2516.6 TFLOP/s dense bf16 peak, the time of
+each kernel (the backward runs as its three stages, Delta, dK/dV and dQ, with
+HIP events between them on the launch stream), the roofline of the dominant
+kernel (dK/dV), the peak device memory, and the fp64 oracle timed on a
+bounded sample of the same workload on the host CPU.
+
+Algorithmic work per allowed pair, by kernel: forward 4*D (S = QK^T, PV);
+dK/dV 8*D (S, dP = dO V^T, dV += P^T dO, dK += dS^T Q); dQ 2*D (dQ += dS K;
+its recomputation of S and dP is overhead and is not counted); Delta reads
+O and dO (4*D bytes per query row in bf16) and does no contraction.
+
+The roofline's ``traffic`` (HBM bytes per launch of the dK/dV kernel) comes
+from a committed rocprofv3 counter summary (FETCH_SIZE, WRITE_SIZE) whose
+recorded source hash must match the current kernel sources, else it is null.
+
+    python bench.py --copy-calibration
+
+runs one 256 MiB device-to-device copy: its FETCH_SIZE/WRITE_SIZE readings
+give the factor that turns those counters into bytes.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -55,6 +71,57 @@ def flops(w):
     return 4 * w.D * pairs, 10 * w.D * pairs
 
 
+def kernel_flops(w):
+    """Algorithmic flops of one launch of each kernel."""
+    pairs = sum(pair_count(w)) * w.Hq
+    return {"fwd": 4 * w.D * pairs, "dkdv": 8 * w.D * pairs, "dq": 2 * w.D * pairs}
+
+
+# Sources compiled into the dK/dV kernel: a counter summary taken on other
+# sources no longer describes it.
+DKDV_SOURCES = ("flash_attention_fa_amd/csrc/fa_bwd.hip", "flash_attention_fa_amd/csrc/fa_device.h",
+                "flash_attention_fa_amd/csrc/fa_internal.h", "flash_attention_fa_amd/build.py")
+
+
+def sources_sha256(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload, sources):
+    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.md, or
+    None when there is no summary or it was taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", " ")):
+            key, _, val = line.partition(":")
+            kv[key.strip()] = val.strip()
+    if kv.get("sources_sha256") != sources_sha256(sources):
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """One 256 MiB copy for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 256 << 20
+    x = torch.ones(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+    return 0
+
+
 def find_workload(name):
     for w in W.all_workloads():
         if w.name == name:
@@ -62,35 +129,26 @@ def find_workload(name):
     raise SystemExit(f"unknown workload {name}; known: {[w.name for w in W.all_workloads()]}")
 
 
-def cpu_baseline(w, q, k, v, do, rows):
-    """The fp64 oracle on query head 0, rows [Sq - rows, Sq) (the heaviest
-    rows of a causal mask), timed on the host; returns the JSON object."""
+def cpu_baseline(w, q, k, v, do, nheads):
+    """The fp64 oracle, forward and backward, on batch 0 and query heads
+    [0, nheads) of the workload (every row), timed on the host; returns the
+    JSON object."""
     from threadpoolctl import threadpool_info
     from oracle import attention_ref
-    Sq = w.Sq
-    lo = max(0, Sq - rows)
+    nheads = max(1, min(nheads, w.Hq))
     kvv = None if w.kv_valid is None else list(w.kv_valid)
     args = [x[:1].double().numpy() for x in (q, k, v, do)]
     t0 = time.perf_counter()
-    attention_ref(*args, w.kind, w.shift, kvv, w.scale, heads=[0], rows=(lo, Sq))
+    attention_ref(*args, w.kind, w.shift, None if kvv is None else kvv[:1], w.scale,
+                  heads=list(range(nheads)))
     sec = time.perf_counter() - t0
-    # allowed pairs in the sample (batch 0, one head)
-    wi = w.with_(B=1, kv_valid=None if kvv is None else (kvv[0],))
-    i = np.arange(lo, Sq, dtype=np.int64)
-    cap = w.Sq if w.kind == W.TTT else w.Skv
-    n_valid = cap if kvv is None else min(kvv[0], cap)
-    if w.kind == W.FULL:
-        pairs = (Sq - lo) * n_valid
-    else:
-        pairs = int(np.clip(i - w.shift + 1, 0, n_valid).sum())
-        if w.kind == W.TTT:
-            pairs += (w.Skv // w.Sq - 1) * int((i < n_valid).sum())
-    del wi
+    pairs = pair_count(w)[0] * nheads
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": 14 * w.D * pairs / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle, fwd+bwd of batch 0, query head 0, rows [{lo}, {Sq}) "
-                      f"of {w.name} ({pairs} allowed pairs, {sec:.2f} s, host nproc {os.cpu_count()})"}
+            "sample": f"fp64 numpy oracle, fwd+bwd of batch 0, query heads [0, {nheads}), all "
+                      f"{w.Sq} rows, of {w.name} ({pairs} allowed pairs, {sec:.2f} s, "
+                      f"host nproc {os.cpu_count()})"}
 
 
 def main():
@@ -99,15 +157,19 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=W.HEADLINE.name)
-    ap.add_argument("--cpu-rows", type=int, default=1024,
-                    help="query rows of one head the oracle baseline computes")
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="query heads of batch 0 the oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 256 MiB device copy (counter calibration) and exit")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
-              "(the library is single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "(one process drives one GPU; the library does not shard across GPUs)", file=sys.stderr)
         return 2
 
+    if a.copy_calibration:
+        return copy_calibration()
     import flash_attention_fa_amd as fa
     w = find_workload(a.workload)
     dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", 0)))
@@ -125,8 +187,12 @@ def main():
     def fwd():
         fa.fa_fwd(qg, kg, vg, out=o, lse=lse, **kw)
 
-    def bwd():
-        fa.fa_bwd(qg, kg, vg, o, lse, dog, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+    def bwd(marks=None):
+        # fa_bwd's three stages, in fa_bwd's order, with an optional event after each
+        for i, stage in enumerate((fa.FA_BWD_DELTA, fa.FA_BWD_DKDV, fa.FA_BWD_DQ)):
+            fa.fa_bwd_stage(stage, qg, kg, vg, o, lse, dog, dq, dk, dv, ws, **kw)
+            if marks is not None:
+                marks[i].record(stream)
 
     torch.cuda.synchronize()
     mem0 = torch.cuda.memory_allocated(dev)
@@ -136,20 +202,22 @@ def main():
         bwd()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    # events: step start, fwd end, Delta end, dK/dV end, dQ end (= step end)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(a.steps):
         ev[s][0].record(stream)
         fwd()
         ev[s][1].record(stream)
-        bwd()
-        ev[s][2].record(stream)
+        bwd(ev[s][2:])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    total_ms = ev[0][0].elapsed_time(ev[-1][2])
+    span = lambda i, j: [e[i].elapsed_time(e[j]) for e in ev]
+    fwd_ms = span(0, 1)
+    bwd_ms = span(1, 4)
+    stage_ms = {"delta": span(1, 2), "dkdv": span(2, 3), "dq": span(3, 4)}
+    total_ms = ev[0][0].elapsed_time(ev[-1][4])
     ms_step = total_ms / a.steps
     f_fwd, f_bwd = flops(w)
     fwd_med, bwd_med = float(np.median(fwd_ms)), float(np.median(bwd_ms))
@@ -160,7 +228,17 @@ def main():
     # inputs + outputs + workspace resident during the step
     resident = sum(t.numel() * t.element_size() for t in (qg, kg, vg, dog, o, lse, dq, dk, dv, ws))
 
-    fwd_tf = tf(f_fwd, fwd_avg)
+    kf = kernel_flops(w)
+    k_avg = {"fwd": fwd_avg, **{n: float(np.mean(v)) for n, v in stage_ms.items()}}
+    kernels = {n: {"ms_mean": round(ms, 4)} for n, ms in k_avg.items()}
+    for n, f in kf.items():
+        kernels[n]["algorithmic_tflops"] = round(tf(f, k_avg[n]), 2)
+        kernels[n]["pct_of_peak"] = round(100 * tf(f, k_avg[n]) / PEAK_BF16_TFLOPS, 2)
+    # Delta is HBM-bound: reads O and dO, writes one float per row
+    delta_bytes = 2 * w.B * w.Hq * w.Sq * w.D * (2 if w.dtype == "bf16" else 4) + 4 * w.B * w.Hq * w.Sq
+    kernels["delta"]["gbs"] = round(delta_bytes / (k_avg["delta"] * 1e-3) / 1e9, 1)
+    dkdv_tf = tf(kf["dkdv"], k_avg["dkdv"])
+    traffic = measured_traffic("dkdv", w.name, DKDV_SOURCES)
     out = {
         "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak at 1 MI355X (causal S=16K)",
         "value": round(value, 2),
@@ -183,15 +261,19 @@ def main():
         "bwd": {"ms_median": round(bwd_med, 4), "tflops": round(tf(f_bwd, bwd_med), 2),
                 "pct_of_peak": round(100 * tf(f_bwd, bwd_med) / PEAK_BF16_TFLOPS, 2)},
         "gflop_per_step": round((f_fwd + f_bwd) / 1e9, 3),
-        "roofline": {"kernel": "fwd_kernel (fa_fwd: one launch)", "bound": "mfma",
-                     "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "kernels": kernels,
+        "roofline": {"kernel": "dkdv_kernel (fa_bwd_stage FA_BWD_DKDV: one launch)",
+                     "bound": "mfma", "achieved": round(dkdv_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, "
+                                     "copy-calibrated)"},
         "memory": {"peak_allocated_bytes": int(peak_mem), "resident_bytes": int(resident),
                    "baseline_bytes": int(mem0)},
         "wall_s_timed": round(wall, 3),
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, a.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, a.cpu_heads)
     print(json.dumps(out), flush=True)
     return 0
 

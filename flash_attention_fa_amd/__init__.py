@@ -6,6 +6,7 @@ memory and the current stream.  The functions mirror the C entry points:
 
     fa_fwd(q, k, v, ...)                     -> (o, lse)
     fa_bwd(q, k, v, o, lse, dout, ...)       -> (dq, dk, dv)
+    fa_bwd_stage(stage, q, k, v, ..., dq, dk, dv, workspace)   (one stage of fa_bwd)
     fa_bwd_workspace_bytes(q, k, ...)        -> int
     fa_last_error()                          -> str
 
@@ -25,11 +26,12 @@ import torch
 
 from . import _lib
 from ._lib import (FAError, FA_BF16, FA_F32, FA_MASK_FULL, FA_MASK_CAUSAL,  # noqa: F401
-                   FA_MASK_TTT)
+                   FA_MASK_TTT, FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ)
 
 FULL, CAUSAL, TTT = FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_TTT
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_last_error",
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes", "fa_last_error",
+           "FA_BWD_DELTA", "FA_BWD_DKDV", "FA_BWD_DQ",
            "attention", "FAError", "FULL", "CAUSAL", "TTT"]
 
 
@@ -135,6 +137,19 @@ def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=No
     _lib.check(_lib.lib().fa_bwd(a, ws_ptr, workspace.numel() * workspace.element_size(),
                                  _stream(q, stream)))
     return dq, dk, dv
+
+
+def fa_bwd_stage(stage, q, k, v, o, lse, dout, dq, dk, dv, workspace, *, mask_kind=FULL,
+                 causal_shift=0, kv_valid=None, scale=None, stream=None):
+    """One stage (FA_BWD_DELTA, FA_BWD_DKDV or FA_BWD_DQ) of ``fa_bwd``.
+
+    The caller provides the outputs and the workspace; DKDV and DQ read the
+    Delta that a DELTA stage left in ``workspace``.
+    """
+    a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale)
+    _lib.check(_lib.lib().fa_bwd_stage(a, int(stage), workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(q, stream)))
 
 
 def fa_last_error():

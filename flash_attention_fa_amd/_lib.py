@@ -24,7 +24,10 @@ FA_MASK_FULL = 0
 FA_MASK_CAUSAL = 1
 FA_MASK_TTT = 2
 
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes", "fa_last_error")
+
+
+FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2
 
 
 class fa_tensor(ctypes.Structure):
@@ -80,6 +83,9 @@ def lib():
         L.fa_bwd.argtypes = [ctypes.POINTER(fa_bwd_args), ctypes.c_void_p,
                              ctypes.c_size_t, ctypes.c_void_p]
         L.fa_bwd.restype = ctypes.c_int
+        L.fa_bwd_stage.argtypes = [ctypes.POINTER(fa_bwd_args), ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_void_p]
+        L.fa_bwd_stage.restype = ctypes.c_int
         L.fa_bwd_workspace_bytes.argtypes = [ctypes.POINTER(fa_bwd_args)]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fa_last_error.argtypes = []

@@ -200,7 +200,9 @@ size_t fa_bwd_workspace_bytes(const fa_bwd_args* a) {
   return delta_bytes(s);
 }
 
-fa_status fa_bwd(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+// Validates a backward call and launches the requested stages in order.
+static fa_status bwd_run(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStream_t stream,
+                         int first_stage, int last_stage) {
   if (!a) return fail(FA_ERR_INVALID_ARG, "fa_bwd: args is NULL");
   Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
   fa_status st = check_shape(s, a->mask);
@@ -256,9 +258,22 @@ fa_status fa_bwd(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStream_t st
   p.dout = tensor(a->dout); p.dq = tensor(a->dq); p.dk = tensor(a->dk); p.dv = tensor(a->dv);
   p.lse_in = a->lse;
   p.delta = static_cast<float*>(ws);
-  hipError_t e = s.dtype == FA_BF16 ? fa::launch_bwd_bf16(p, stream) : fa::launch_bwd_f32(p, stream);
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_bwd launch failed: %s", hipGetErrorString(e));
+  for (int stage = first_stage; stage <= last_stage; ++stage) {
+    hipError_t e = s.dtype == FA_BF16 ? fa::launch_bwd_bf16(p, stage, stream)
+                                      : fa::launch_bwd_f32(p, stage, stream);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_bwd launch failed: %s", hipGetErrorString(e));
+  }
   return FA_OK;
+}
+
+fa_status fa_bwd(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return bwd_run(a, ws, ws_bytes, stream, fa::STAGE_DELTA, fa::STAGE_DQ);
+}
+
+fa_status fa_bwd_stage(const fa_bwd_args* a, int stage, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (stage != FA_BWD_DELTA && stage != FA_BWD_DKDV && stage != FA_BWD_DQ)
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd_stage: unknown stage %d", stage);
+  return bwd_run(a, ws, ws_bytes, stream, stage, stage);
 }
 
 }  // extern "C"

@@ -58,7 +58,7 @@ struct DqLds {
   static constexpr int KSTR = D + 8;
   static constexpr int VSTR = D + 8;
   static constexpr int KTILE = DQ_TK * KSTR;   // K rows
-  static constexpr int KTT = D * TSTR;         // K transposed
+  static constexpr int KTT = D * STAGE_ROWS;   // K transposed
   static constexpr int VTILE = DQ_TK * VSTR;   // V rows
   static constexpr int BUF = KTILE + KTT + VTILE;
   static constexpr int BYTES = 2 * BUF * 2;
@@ -235,7 +235,7 @@ dq_kernel(Params p) {
         for (int st = 0; st < 2; ++st) {
 #pragma unroll
           for (int c = 0; c < NDB; ++c) {
-            bf16x8 a = lds_read8(Ktt + (32 * c + kt_row) * TSTR + 32 * kb + 16 * st + 8 * hh);
+            bf16x8 a = lds_read8(Ktt + tswz(32 * c + kt_row, 32 * kb + 16 * st + 8 * hh));
             if (!d_lane_ok) a = bf16x8{};
 #pragma unroll
             for (int qb_ = 0; qb_ < QB; ++qb_) acc[qb_][c] = mfma32(a, dsb[qb_][kb][st], acc[qb_][c]);
@@ -290,7 +290,7 @@ template <int D, int NKB, bool KLDS>
 struct KvLds {
   static constexpr int STR = D + 8;
   static constexpr int TILE = KV_TQ * STR;                    // Q or dO rows
-  static constexpr int TT = D * TSTR;                         // Q or dO transposed
+  static constexpr int TT = D * STAGE_ROWS;                   // Q or dO transposed
   // one stage: Q rows, Q^T, dO rows, dO^T (bf16), then LSE and Delta (fp32)
   static constexpr int STAGE = 2 * (TILE + TT) * 2 + 2 * KV_TQ * 4;
   static constexpr int VROWS = NKB * 32;
@@ -369,7 +369,11 @@ dkdv_kernel(Params p) {
   const int t_first = qlo < qhi ? qlo / TQ : 0;
   const int t_last = qlo < qhi ? (qhi + TQ - 1) / TQ : 0;
   const int ntile = t_last - t_first;
-  const int nsteps = ntile * p.G;   // (head, query tile) pairs, head-major
+  // (query tile, head) pairs: tiles from the last down, the group's heads
+  // inside.  Every workgroup starts at the last query tile and walks down at
+  // the same pace, so the workgroups sharing an XCD read the same Q / dO
+  // tiles at about the same time and its L2 serves them all.
+  const int nsteps = ntile * p.G;
 
   // Stage layout: [Q rows | Q^T | dO rows | dO^T | LSE | Delta].
   auto stage_ptr = [&](int buf) { return reinterpret_cast<bf16*>(smem + buf * L::STAGE); };
@@ -377,8 +381,8 @@ dkdv_kernel(Params p) {
   i32x4 stg[PER_T][4];
   float lst = 0.f, dst = 0.f;
   auto fetch = [&](int step) {
-    const int h = hk * p.G + step / ntile;
-    const int q0 = (t_first + step % ntile) * TQ;
+    const int h = hk * p.G + step % p.G;
+    const int q0 = (t_last - 1 - step / p.G) * TQ;
     const bf16* Sg = stage_g ? static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh
                              : static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
     const int64_t sss = stage_g ? p.dout.ss : p.q.ss;
@@ -431,7 +435,7 @@ dkdv_kernel(Params p) {
 
   for (int step = 0; step < nsteps; ++step) {
     if (step + 1 < nsteps) fetch(step + 1);
-    const int q0 = (t_first + step % ntile) * TQ;
+    const int q0 = (t_last - 1 - step / p.G) * TQ;
     const bf16* stg0 = stage_ptr(buf);
     const bf16* Qs = stg0 + 32 * qhalf * L::STR;
     const bf16* Qt = stg0 + L::TILE;
@@ -486,8 +490,8 @@ dkdv_kernel(Params p) {
         const int pos = 32 * qhalf + 16 * st + 8 * hh;
 #pragma unroll
         for (int c = 0; c < NDB; ++c) {
-          bf16x8 ag = lds_read8(Gt + (32 * c + t_row) * TSTR + pos);
-          bf16x8 aq = lds_read8(Qt + (32 * c + t_row) * TSTR + pos);
+          bf16x8 ag = lds_read8(Gt + tswz(32 * c + t_row, pos));
+          bf16x8 aq = lds_read8(Qt + tswz(32 * c + t_row, pos));
           if (!d_lane_ok) { ag = bf16x8{}; aq = bf16x8{}; }
           dva[c] = mfma32(ag, pb[st], dva[c]);
           dka[c] = mfma32(aq, dsb[st], dka[c]);
@@ -563,15 +567,15 @@ hipError_t launch_dq(const Params& p, hipStream_t stream) {
 }
 
 template <int D>
-hipError_t launch_all(const Params& p, hipStream_t stream) {
+hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
   hipError_t e;
   const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
-  if (rows > 0) {
+  if (stage == STAGE_DELTA && rows > 0) {
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  {
+  if (stage == STAGE_DKDV) {
     constexpr int NKB = 4, TKW = NKB * 32;
     constexpr bool KLDS = D >= 128;
     const int64_t nblk = (int64_t)p.B * p.Hkv * ((p.Skv + TKW - 1) / TKW);
@@ -583,7 +587,7 @@ hipError_t launch_all(const Params& p, hipStream_t stream) {
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  if (p.B > 0 && p.Sq > 0) {
+  if (stage == STAGE_DQ && p.B > 0 && p.Sq > 0) {
     // 8-wave workgroups when there are enough to fill the chip twice over
     const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
     if ((e = wg8 >= 512 ? launch_dq<D, 1, 8>(p, stream) : launch_dq<D, 1, 4>(p, stream)) != hipSuccess)
@@ -594,12 +598,12 @@ hipError_t launch_all(const Params& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const Params& p, hipStream_t s) {
+hipError_t launch_bwd_bf16(const Params& p, int stage, hipStream_t s) {
   switch (p.D) {
-    case 16: return launch_all<16>(p, s);
-    case 32: return launch_all<32>(p, s);
-    case 64: return launch_all<64>(p, s);
-    case 128: return launch_all<128>(p, s);
+    case 16: return launch_stage<16>(p, stage, s);
+    case 32: return launch_stage<32>(p, stage, s);
+    case 64: return launch_stage<64>(p, stage, s);
+    case 128: return launch_stage<128>(p, stage, s);
   }
   return hipErrorInvalidValue;
 }

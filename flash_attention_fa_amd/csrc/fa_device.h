@@ -88,16 +88,27 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) 
 // --------------------------------------------------------------------------
 // Tile staging.  A 64-row tile of a row-major [rows][D] bf16 matrix is moved
 // into LDS in units of 4 rows x 8 columns: each thread loads 4 x 16 bytes and
-// writes a row-major copy and/or a transposed copy ([D][64], row stride
-// TSTR) in which, inside every group of 16 rows, bits 2 and 3 of the row
-// index are swapped.  That order makes the 8 values one MFMA k-step needs
-// (two runs of 4 in the 32x32 accumulator layout) contiguous, so the
-// transposed operand is a single 16-byte LDS read.  The unit -> lane map keeps
-// 16 consecutive lanes on distinct bank slots for the row-major writes and at
-// most two lanes per slot for the 8-byte transposed writes.
+// writes a row-major copy and/or a transposed copy ([D][64]) in which, inside
+// every group of 16 rows, bits 2 and 3 of the row index are swapped.  That
+// order makes the 8 values one MFMA k-step needs (two runs of 4 in the 32x32
+// accumulator layout) contiguous, so the transposed operand is a single
+// 16-byte LDS read.
+//
+// The transposed copy is unpadded and XOR-swizzled (tswz): column pair
+// (2p, 2p+1) fills one 256-byte bank line, and the sixteen 16-byte slots of
+// that line are permuted by p mod 16.  Then the MFMA operand reads (16
+// consecutive columns, one 16-byte chunk each) and the 8-byte transposing
+// writes (32 lanes: 4 columns 8 apart x 8 row quads) both touch every bank
+// exactly once per 256 bytes.  The unit -> lane map keeps 16 consecutive
+// lanes on distinct bank slots for the row-major writes.
 
 constexpr int STAGE_ROWS = 64;
-constexpr int TSTR = STAGE_ROWS + 8;   // transposed-copy row stride (elements)
+
+// Element offset of (column d, stored row position pos) in a [D][64]
+// transposed tile.
+__device__ __forceinline__ int tswz(int d, int pos) {
+  return (d >> 1) * 128 + 8 * ((((d & 1) << 3) | (pos >> 3)) ^ ((d >> 1) & 15)) + (pos & 7);
+}
 
 __device__ __forceinline__ int tpos(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -141,7 +152,7 @@ __device__ __forceinline__ void store_trans4(bf16* Xt, int rg, int c8, const i32
   transpose4x8(v, t);
   const int pos = tpos(4 * rg);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) lds_write8(Xt + (8 * c8 + e) * TSTR + pos, t[e]);
+  for (int e = 0; e < 8; ++e) lds_write8(Xt + tswz(8 * c8 + e, pos), t[e]);
 }
 
 // --------------------------------------------------------------------------

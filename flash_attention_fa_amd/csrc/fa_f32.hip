@@ -96,6 +96,21 @@ __global__ void __launch_bounds__(F_ROWS) fwd_f32_kernel(Params p) {
   }
 }
 
+// Delta_i = sum_d dO_id O_id, one thread per row.
+template <int D>
+__global__ void __launch_bounds__(256) delta_f32_kernel(Params p) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= (int64_t)p.B * p.Hq * p.Sq) return;
+  const int i = (int)(r % p.Sq);
+  const int64_t bh = r / p.Sq;
+  const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+  const float* orow = static_cast<const float*>(p.o.ptr) + b * p.o.sb + h * p.o.sh + (int64_t)i * p.o.ss;
+  const float* grow = static_cast<const float*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh + (int64_t)i * p.dout.ss;
+  float acc = 0.f;
+  for (int d = 0; d < D; ++d) acc = fmaf(orow[d], grow[d], acc);
+  p.delta[r] = acc;
+}
+
 template <int D>
 __global__ void __launch_bounds__(F_ROWS) dq_f32_kernel(Params p) {
   extern __shared__ __align__(16) float fsm[];
@@ -112,7 +127,6 @@ __global__ void __launch_bounds__(F_ROWS) dq_f32_kernel(Params p) {
   const int i = qa + threadIdx.x;
   const float* Qg = static_cast<const float*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
   const float* Gg = static_cast<const float*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh;
-  const float* Og = static_cast<const float*>(p.o.ptr) + b * p.o.sb + h * p.o.sh;
   const float* Kg = static_cast<const float*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
   const float* Vg = static_cast<const float*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
   load_rows<D>(Qs, Qg, p.q.ss, qa, F_ROWS, p.Sq, &m, false);
@@ -121,12 +135,7 @@ __global__ void __launch_bounds__(F_ROWS) dq_f32_kernel(Params p) {
   float lse2 = 0.f, delta = 0.f;
   if (i < p.Sq) {
     lse2 = p.lse_in[rb + i] * 1.4426950408889634f;
-    float acc = 0.f;
-    const float* orow = Og + (int64_t)i * p.o.ss;
-    const float* grow = Gg + (int64_t)i * p.dout.ss;
-    for (int d = 0; d < D; ++d) acc = fmaf(orow[d], grow[d], acc);
-    delta = acc;
-    p.delta[rb + i] = delta;  // shared with the dK/dV kernel (launched after)
+    delta = p.delta[rb + i];
   }
   float dq[D];
 #pragma unroll
@@ -247,14 +256,19 @@ hipError_t fwd_d(const Params& p, hipStream_t s) {
 }
 
 template <int D>
-hipError_t bwd_d(const Params& p, hipStream_t s) {
+hipError_t bwd_d(const Params& p, int stage, hipStream_t s) {
   hipError_t e;
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
+  if (stage == STAGE_DELTA && rows > 0) {
+    hipLaunchKernelGGL(delta_f32_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int64_t nq = (int64_t)p.B * p.Hq * ((p.Sq + F_ROWS - 1) / F_ROWS);
-  if (nq > 0) {  // also writes Delta for the dK/dV kernel
+  if (stage == STAGE_DQ && nq > 0) {
     if ((e = launch_dyn(dq_f32_kernel<D>, nq, (2 * F_TK + 2 * F_ROWS) * D * 4, s, p)) != hipSuccess) return e;
   }
   const int64_t nk = (int64_t)p.B * p.Hkv * ((p.Skv + F_ROWS - 1) / F_ROWS);
-  if (nk > 0) {
+  if (stage == STAGE_DKDV && nk > 0) {
     if ((e = launch_dyn(dkdv_f32_kernel<D>, nk, (2 * F_TK + 2 * F_ROWS) * D * 4 + 2 * F_TK * 4, s, p)) != hipSuccess)
       return e;
   }
@@ -273,12 +287,12 @@ hipError_t launch_fwd_f32(const Params& p, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_f32(const Params& p, hipStream_t s) {
+hipError_t launch_bwd_f32(const Params& p, int stage, hipStream_t s) {
   switch (p.D) {
-    case 16: return bwd_d<16>(p, s);
-    case 32: return bwd_d<32>(p, s);
-    case 64: return bwd_d<64>(p, s);
-    case 128: return bwd_d<128>(p, s);
+    case 16: return bwd_d<16>(p, stage, s);
+    case 32: return bwd_d<32>(p, stage, s);
+    case 64: return bwd_d<64>(p, stage, s);
+    case 128: return bwd_d<128>(p, stage, s);
   }
   return hipErrorInvalidValue;
 }

@@ -33,9 +33,12 @@ struct Params {
 
 // Launchers (one translation unit per kernel family).  Each returns the
 // hipError_t of its launches; shapes were validated by the dispatcher.
+// Backward stages: Delta = rowsum(dO * O), then the dK/dV and dQ kernels
+// (independent of each other once Delta exists).
+enum { STAGE_DELTA = 0, STAGE_DKDV = 1, STAGE_DQ = 2 };
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t s);
-hipError_t launch_bwd_bf16(const Params& p, hipStream_t s);
+hipError_t launch_bwd_bf16(const Params& p, int stage, hipStream_t s);
 hipError_t launch_fwd_f32(const Params& p, hipStream_t s);
-hipError_t launch_bwd_f32(const Params& p, hipStream_t s);
+hipError_t launch_bwd_f32(const Params& p, int stage, hipStream_t s);
 
 }  // namespace fa

@@ -130,6 +130,25 @@ size_t fa_bwd_workspace_bytes(const fa_bwd_args* args);
 fa_status fa_bwd(const fa_bwd_args* args, void* ws, size_t ws_bytes,
                  hipStream_t stream);
 
+/* The three stages of fa_bwd, in the order fa_bwd runs them. */
+typedef enum {
+  FA_BWD_DELTA = 0,  /* Delta_i = sum_d dO_id O_id into the workspace (the row
+                        term of dS = P * (dP - Delta); CS336 "Flash Attention
+                        (Triton)", backward pass) */
+  FA_BWD_DKDV = 1,   /* dK, dV: one workgroup per key block, summing over the
+                        group's query heads in a fixed order */
+  FA_BWD_DQ = 2      /* dQ: one workgroup per query block */
+} fa_bwd_stage_id;
+
+/* Runs one stage of fa_bwd with the same arguments, validation and workspace.
+ * DKDV and DQ read the Delta that a DELTA stage left in `ws` (on the same
+ * stream, or ordered after it by the caller); given that, running DELTA,
+ * DKDV, DQ in turn writes bitwise the same dQ, dK, dV as fa_bwd.  For callers
+ * that overlap the two gradient kernels on separate streams or time them one
+ * by one.  An unknown stage returns FA_ERR_INVALID_ARG. */
+fa_status fa_bwd_stage(const fa_bwd_args* args, int stage, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
 /* Text describing the last non-OK status returned on this thread
  * ("" if none).  The pointer stays valid until the thread's next call. */
 const char* fa_last_error(void);

@@ -187,3 +187,24 @@ def test_workspace_is_linear_in_sequence_length():
     sizes = [_lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=s, Skv=s, D=128))
              for s in (16384, 32768)]
     assert sizes[1] == 2 * sizes[0] == 2 * 32 * 16384 * 4
+
+
+def test_bwd_stage_rejects_unknown_stage():
+    for stage in (-1, 3, 100):
+        st = _lib.lib().fa_bwd_stage(bwd_args(), stage, WS, 1 << 20, None)
+        assert st == _lib.FA_ERR_INVALID_ARG
+        assert "stage" in _lib.last_error()
+
+
+def test_bwd_stage_validates_like_bwd():
+    # the same argument errors come back from every stage, before any launch
+    bad = [bwd_args(Hq=3, Hkv=2), bwd_args(D=96), bwd_args(dtype=7)]
+    for a in bad:
+        ref, _ = bwd(a)
+        assert ref != _lib.FA_OK
+        for stage in (_lib.FA_BWD_DELTA, _lib.FA_BWD_DKDV, _lib.FA_BWD_DQ):
+            assert _lib.lib().fa_bwd_stage(a, stage, WS, 1 << 20, None) == ref
+    # workspace too small
+    a = bwd_args()
+    for stage in (_lib.FA_BWD_DELTA, _lib.FA_BWD_DKDV, _lib.FA_BWD_DQ):
+        assert _lib.lib().fa_bwd_stage(a, stage, WS, 16, None) == _lib.FA_ERR_INVALID_ARG

@@ -142,3 +142,22 @@ def test_bitwise_determinism(kind):
     b = run_gpu(q, k, v, do, kind)
     for name in ("O", "LSE", "dQ", "dK", "dV"):
         assert np.array_equal(a[name], b[name]), name
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_staged_backward_equals_fa_bwd(dtype):
+    """fa_bwd_stage DELTA, DKDV, DQ in turn writes bitwise what fa_bwd writes."""
+    import flash_attention_fa_amd as fa
+    L = 320
+    q, k, v, do = (x.cuda() for x in inputs(1, 8, 2, L, L, 64, dtype, seed=53))
+    say(f"[staged] dtype={dtype}")
+    o, lse = fa.fa_fwd(q, k, v, mask_kind=CAUSAL)
+    ref = fa.fa_bwd(q, k, v, o, lse, do, mask_kind=CAUSAL)
+    dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(q, k), dtype=torch.uint8, device="cuda")
+    # the gradient stages in the opposite order: they are independent once Delta exists
+    for stage in (fa.FA_BWD_DELTA, fa.FA_BWD_DQ, fa.FA_BWD_DKDV):
+        fa.fa_bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, mask_kind=CAUSAL)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), ref, (dq, dk, dv)):
+        assert torch.equal(a, b), name
