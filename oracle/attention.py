@@ -22,7 +22,7 @@ Sources, by page and section:
   fused kernel returns the same result as the explicit
   Q K^T -> softmax -> P V chain; only memory traffic changes.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   * scale defaults to 1/sqrt(D);
   * LSE is the natural-log logsumexp of the *scaled* scores;
   * CAUSAL with Sq != Skv is top-left aligned: key j allowed iff j <= i - shift;

@@ -13,7 +13,7 @@ joint softmax; the output is the block's weights times the step-0 values plus,
 for each step s, the weight of its extra column times that step's value at
 position i.
 
-Readings (listed in the design doc): the extra columns exist for cache steps
+Readings where the page is unclear: the extra columns exist for cache steps
 1..t only (step 0 is the causal block); ``qi`` in the page's loop is the query
 rows themselves; a padding length kv_valid removes key positions >= kv_valid
 of every step; an optional causal shift applies to the step-0 block only, as
