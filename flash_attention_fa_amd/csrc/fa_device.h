@@ -1,6 +1,6 @@
 // fa_device.h - gfx950 building blocks shared by the attention kernels.
 //
-// MFMA lane maps (checked on hardware by tests/test_lane_maps.py):
+// MFMA lane maps (measured on gfx950; every parity test depends on them):
 //   v_mfma_f32_32x32x16_bf16  C[32x32] += A[32x16] * B[16x32]
 //     A: lane l holds A[l%32][8*(l/32) + e], e = 0..7
 //     B: lane l holds B[8*(l/32) + e][l%32]
@@ -57,6 +57,18 @@ __device__ __forceinline__ float half_swap_max(float x) {
 __device__ __forceinline__ float half_swap_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// c + the sum of the eight bf16 values of x (four two-way dot products with
+// ones, accumulated in fp32).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 x, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, c, false);
+  return c;
 }
 
 __device__ __forceinline__ bf16x8 lds_read8(const bf16* p) {
@@ -242,6 +254,27 @@ __device__ __forceinline__ bool allowed(const MaskB& m, int i, int j) {
   // TTT suffix: key of a later step at the query's own position.
   const int jm = j - (j / m.L) * m.L;
   return causal | ((j >= m.L) & (jm == i) & (jm < m.kvv));
+}
+
+// Instruction-class masks of the scheduler's group barriers, and a group
+// barrier: the next `n` instructions of class `mask` in the current
+// straight-line block are placed here, in order.
+enum : int { SCHED_VALU = 0x002, SCHED_SALU = 0x004, SCHED_MFMA = 0x008, SCHED_VMEM_READ = 0x020,
+             SCHED_DS_READ = 0x100, SCHED_DS_WRITE = 0x200, SCHED_TRANS = 0x400 };
+#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
+// Places an accumulator tile in the accumulation registers at this point.
+// A value that the vector ALUs rescale on a rare path then re-enters the
+// product loop in the register class the products keep it in, instead of
+// the loop copying it between classes on every iteration.
+__device__ __forceinline__ void in_agpr(f32x16& x) {
+  asm volatile("" : "+a"(x));
+}
+
+// Makes `x` count as used here, so its computation stays in this block.
+template <typename T>
+__device__ __forceinline__ void keep(const T& x) {
+  asm volatile("" ::"v"(x));
 }
 
 // The wave index as a provably uniform (scalar) value, so everything derived

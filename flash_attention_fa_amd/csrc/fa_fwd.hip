@@ -10,24 +10,31 @@
 // O and LSE ever reach HBM (ggml flash-attn-training playbook, section 1).
 //
 // Work split.  A workgroup owns NW*32 query rows of one (batch, head); each
-// wave owns one block of 32 rows.  Keys stream through LDS in tiles of 64.
-// Scores are computed transposed, S^T = K Q^T, so each lane owns one query
-// column and 16 keys of it: the row max and row sum are in-lane reductions
-// plus one cross-half swap, and the softmax scale, max and normaliser are one
-// scalar per lane.  O^T = V^T P^T then takes P straight from the score
-// registers and V^T from a transposed copy of the V tile that the workgroup
-// writes once per tile (keys inside each 16-key MFMA step ordered the way the
-// score registers hold them), so both operands of both products are single
-// 16-byte LDS reads.
+// wave owns one block of 32 rows, two waves per SIMD.  Keys stream through
+// LDS in tiles of 64.  Scores are computed transposed, S^T = K Q^T, so each
+// lane owns one query column and 32 keys of it: the softmax scale, running
+// max and normaliser are one scalar per lane.  O^T = V^T P^T takes P straight
+// from the score registers and V^T from transposing LDS reads of the
+// row-major V tile.
+//
+// Vector-ALU budget.  At D = 128 a wave's 32 MFMAs per tile take about as long
+// as a few hundred vector instructions, so the exponentials and their
+// bookkeeping are kept to two instructions plus one exp2 per score: one FMA
+// (scale and running max), the exp2, half a bf16 pack and half a two-way dot
+// product that sums the packed P for the normaliser (so l sums exactly the P
+// the PV product uses).  No per-tile row max is taken: P is computed against
+// the running max and only when some row's tile sum exceeds kSumLimit (which
+// bounds every P in it) is the true max taken, O^T and l rescaled and P
+// recomputed.  LDS addresses are lane constants plus immediates: the loop is
+// unrolled over the four ring buffers.
 //
 // Pipeline.  Four LDS buffers hold tiles i .. i+3.  K and V rows are copied
 // HBM -> LDS asynchronously (no registers, no vector instructions) three tiles
 // ahead; iteration i issues the QK^T products of tile i+1, then the
 // exponentials of tile i (independent of those products, so the matrix cores
-// and the vector ALUs work at once inside one wave), then the PV products of
-// tile i, with V^T read transposed from the row-major V tile; the mask, max
-// and (rare) rescale of tile i+1 close the iteration.  One barrier per tile,
-// which waits only for the copies of tile i+2.
+// and the vector ALUs work at once), then the PV products of tile i; the mask
+// of tile i+1 (partial tiles only) closes the iteration.  One barrier per
+// tile, which waits only for the copies of tile i+2.
 #include "fa_device.h"
 
 namespace fa {
@@ -35,12 +42,20 @@ namespace {
 
 constexpr int TK = 64;    // keys per LDS tile
 constexpr int NBUF = 4;   // tiles in flight in LDS
+// A tile's per-row sum of P above this bound triggers the running-max refresh
+// (every P of the row is below it, so nothing overflows before the check).
+constexpr float kSumLimit = 4096.0f;
 
 template <int D>
 struct FwdLds {
   static constexpr int TILE_BYTES = TK * D * 2;          // one K or V tile, swizzled rows
   static constexpr int BUF = 2 * TILE_BYTES;             // K then V
   static constexpr int BYTES = NBUF * BUF;
+};
+
+template <int K>
+struct Buf {
+  static constexpr int value = K;
 };
 
 template <int D, int NW>
@@ -51,8 +66,10 @@ fwd_kernel(Params p) {
   constexpr int RPI = 64 / CPR;              // rows per 1 KB copy instruction
   constexpr int NINS = TK / RPI;             // copy instructions per tile per tensor
   constexpr int LPW = (2 * NINS + NW - 1) / NW;  // copy instructions per wave per tile
+  constexpr bool ALL_COPY = LPW * NW == 2 * NINS;
   constexpr int NDB = D >= 32 ? D / 32 : 1;  // 32-wide d blocks of O^T
   constexpr int NJ = D / 16;                 // 16-wide d steps of S^T
+  constexpr int ROW16 = 16 * 2 * D;          // bytes of 16 tile rows
   using L = FwdLds<D>;
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -92,10 +109,7 @@ fwd_kernel(Params p) {
   // real keys (and every row when t < 0) are fetched from key 0 instead: a
   // real row, so the values are finite, and the mask zeroes their weights.
   // (Only reached when the tile has a real key, so key 0 is real.)
-  const int my_ins = wave * LPW < 2 * NINS ? LPW : 0;   // copies per tile, this wave
   const int crow = lane / CPR, cslot = lane % CPR;
-  // Per-lane, per-copy constants: element offset of this lane's chunk inside
-  // a tile (row offset + swizzled chunk) and of the same chunk in key 0.
   int roff[LPW], zoff[LPW];
 #pragma unroll
   for (int x = 0; x < LPW; ++x) {
@@ -108,13 +122,13 @@ fwd_kernel(Params p) {
     zoff[x] = 8 * gch;
   }
   const bool ttt = m.kind == MASK_TTT;
-  auto copy_tile = [&](int t, int k) {
+  auto copy_tile = [&](int t, int k) __attribute__((always_inline)) {
     const int tb = t * TK;
     const int lim = t >= 0 ? m.kvv - tb : 0;   // rows below lim are real keys (FULL/CAUSAL)
 #pragma unroll
     for (int x = 0; x < LPW; ++x) {
       const int idx = wave * LPW + x;
-      if (idx < 2 * NINS) {
+      if (ALL_COPY || idx < 2 * NINS) {
         const int tensor = idx / NINS, ii = idx % NINS;
         const int row = ii * RPI + crow;
         const bool ok = ttt ? (t >= 0 && key_valid(m, tb + row)) : row < lim;
@@ -126,26 +140,138 @@ fwd_kernel(Params p) {
     }
   };
   // Waits until this wave's copies of all but the newest tile have landed.
-  auto wait_copies = [&]() {
+  const int my_ins = ALL_COPY ? LPW : (wave * LPW < 2 * NINS ? LPW : 0);
+  auto wait_copies = [&]() __attribute__((always_inline)) {
     if (my_ins == LPW) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
   };
 
-  // S^T of one tile: 2 key blocks of 32.
-  auto qk = [&](int k, f32x16 (&s)[2]) {
-    const unsigned char* Kt = smem + k * L::BUF;
+  // Lane-constant byte offsets into a tile: the swizzle of a row depends only
+  // on its index mod 16, so key blocks and 16-key steps are immediates.
+  int koff[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) koff[j] = swz_off<D>(l32, 16 * j + 8 * hh);
+  // Transposing reads of V: lane r of each 16-lane group points at row
+  // kbase + r/4, column dcol + 4*(r%4); lanes whose d column does not exist
+  // (D = 16) read a real column and use zeros.
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const bool d_lane_ok = D >= 32 || ((lane >> 4) & 1) == 0;
+  int voff[2][NDB];
+#pragma unroll
+  for (int c = 0; c < NDB; ++c) {
+    const int dcol = D >= 32 ? 32 * c + tr_col : (tr_col & 15);
+    voff[0][c] = swz_off<D>(4 * hh + tr_row, dcol);
+    voff[1][c] = swz_off<D>(4 * hh + tr_row + 8, dcol);
+  }
+
+  // S^T of the tile in buffer k: 2 key blocks of 32.
+  auto qk = [&](auto kc, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *FA_LDS(const bf16x8, Kt + swz_off<D>(32 * kb + l32, 16 * j + 8 * hh));
+        const bf16x8 a = *FA_LDS(const bf16x8, smem + k * L::BUF + 2 * kb * ROW16 + koff[j]);
         s[kb] = mfma32(a, qreg[j], s[kb]);
       }
   };
-  // Mask of tile t, then the running max; the accumulators are rescaled only
-  // when some row's max grows by more than kRescaleSlack powers of two.
-  auto prep = [&](int t, f32x16 (&s)[2]) {
+  // O^T += V^T P^T for the tile in buffer k; V operands are read PF
+  // products ahead of their use.
+  auto pv = [&](auto kc, const bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int NOP = 4 * NDB;   // (kb, st, c) products
+    constexpr int PF = 3;
+    const unsigned char* Vt = smem + k * L::BUF + L::TILE_BYTES;
+    auto vread = [&](int n) __attribute__((always_inline)) {
+      const int c = n % NDB, rows = (n / NDB) * ROW16;
+      bf16x8 a = cat8(lds_read_tr4(reinterpret_cast<const bf16*>(Vt + rows + voff[0][c])),
+                      lds_read_tr4(reinterpret_cast<const bf16*>(Vt + rows + voff[1][c])));
+      return d_lane_ok ? a : bf16x8{};
+    };
+    bf16x8 va[PF + 1];
+#pragma unroll
+    for (int n = 0; n < PF && n < NOP; ++n) va[n] = vread(n);
+#pragma unroll
+    for (int n = 0; n < NOP; ++n) {
+      if (n + PF < NOP) va[(n + PF) % (PF + 1)] = vread(n + PF);
+      const int c = n % NDB, ks = n / NDB;
+      acc[c] = mfma32(va[n % (PF + 1)], pb[ks >> 1][ks & 1], acc[c]);
+    }
+  };
+  // P of a tile against the running max, rounded to bf16, and its row sum
+  // over the rounded values (two-way dot products with ones).
+  auto softmax = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) e[u] = exp2_fast(s[kb][8 * st + u] * p.scale_log2 - mrun);
+        pb[kb][st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
+        ls = sum_bf16x8(pb[kb][st], ls);
+      }
+    return ls;
+  };
+  // qk() and softmax() interleaved in program order: after product n come
+  // the exponentials of score registers 2n and 2n+1 of the other tile.
+  auto qk_softmax = [&](auto kc, f32x16 (&s)[2], const f32x16 (&sp)[2], bf16x8 (&pb)[2][2])
+      __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    float e[2][2][8];
+    float ls = 0.f;
+    // K operands are read PF products ahead of their use.
+    constexpr int PF = 3;
+    auto kread = [&](int n) __attribute__((always_inline)) {
+      return *FA_LDS(const bf16x8, smem + k * L::BUF + 2 * (n & 1) * ROW16 + koff[n >> 1]);
+    };
+    bf16x8 ka[PF + 1];
+#pragma unroll
+    for (int n = 0; n < PF; ++n) ka[n] = kread(n);
+#pragma unroll
+    for (int n = 0; n < 2 * NJ; ++n) {
+      const int j = n >> 1, kb = n & 1;
+      if (n + PF < 2 * NJ) ka[(n + PF) % (PF + 1)] = kread(n + PF);
+      s[kb] = mfma32(ka[n % (PF + 1)], qreg[j], s[kb]);
+#pragma unroll
+      for (int x = 0; x < 32 / (2 * NJ); ++x) {
+        const int idx = n * (32 / (2 * NJ)) + x;   // 0..31: (kb', st', u)
+        const int kb2 = idx >> 4, st2 = (idx >> 3) & 1, u = idx & 7;
+        e[kb2][st2][u] = exp2_fast(sp[kb2][8 * st2 + u] * p.scale_log2 - mrun);
+        if (u == 7) {
+          pb[kb2][st2] = cat8(to_bf16x4(e[kb2][st2][0], e[kb2][st2][1], e[kb2][st2][2], e[kb2][st2][3]),
+                              to_bf16x4(e[kb2][st2][4], e[kb2][st2][5], e[kb2][st2][6], e[kb2][st2][7]));
+          ls = sum_bf16x8(pb[kb2][st2], ls);
+        }
+      }
+    }
+    return ls;
+  };
+  // Running-max refresh from a tile's scores (rare): O^T and l move to the
+  // new max.
+  auto refresh = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    mx = half_swap_max(mx) * p.scale_log2;
+    const float mn = fmaxf(mrun, mx);
+    const float alpha = exp2_fast(mrun - mn);
+    mrun = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int c = 0; c < NDB; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[c][i] *= alpha;
+  };
+  // Mask of tile t (partial and skipped tiles only).
+  auto mask = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
     const int k0 = t * TK;
     const int state = tile_state(m, k0, TK, wa, wb);
     if (state != TILE_FULL) {
@@ -158,30 +284,7 @@ fwd_kernel(Params p) {
           s[kb][i] = (!skip && allowed(m, qi, key)) ? s[kb][i] : -INFINITY;
         }
     }
-    float mx = s[0][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    mx = half_swap_max(mx) * p.scale_log2;
-    if (__any(mx > mrun + kRescaleSlack)) {
-      const float mn = fmaxf(mrun, mx);
-      const float alpha = exp2_fast(mrun - mn);
-      mrun = mn;
-      lsum *= alpha;
-#pragma unroll
-      for (int c = 0; c < NDB; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[c][i] *= alpha;
-    }
   };
-
-  // Transposing reads of V: lane r of each 16-lane group points at row
-  // kbase + r/4, column dcol + 4*(r%4); lanes whose d column does not exist
-  // (D = 16) read a real column and use zeros.
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const bool d_lane_ok = D >= 32 || ((lane >> 4) & 1) == 0;
 
   // Tiles i (cur) .. i+3 (nx3) of the walk.
   TileWalk cur;
@@ -194,7 +297,6 @@ fwd_kernel(Params p) {
   if (nx3.valid()) nx3.next(m, qa, qb, TK);
 
   f32x16 scur[2], snxt[2];
-  int kbuf = 0;  // LDS buffer of the current tile
   if (cur.valid()) {
     copy_tile(cur.t, 0);
     copy_tile(nx1.valid() ? nx1.t : -1, 1);
@@ -203,57 +305,39 @@ fwd_kernel(Params p) {
   }
   barrier_lds();
   if (cur.valid()) {
-    qk(0, scur);
-    prep(cur.t, scur);
+    qk(Buf<0>{}, scur);
+    mask(cur.t, scur);
   }
 
-  while (cur.valid()) {
-    const int k1 = (kbuf + 1) & (NBUF - 1);
-    copy_tile(nx3.valid() ? nx3.t : -1, (kbuf + 3) & (NBUF - 1));
+  // One iteration with tile i in buffer k; false when the walk has ended.
+  auto step = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    copy_tile(nx3.valid() ? nx3.t : -1, (k + 3) & (NBUF - 1));
     // QK^T of tile i+1 (its buffer may hold a stale tile at the end: unused).
-    qk(k1, snxt);
-    // P of tile i, rounded to bf16 for the PV product.
+    // QK^T of tile i+1 with the exponentials of tile i spread between its
+    // products (they are independent: matrix cores and vector ALUs overlap).
     bf16x8 pb[2][2];
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float e[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          e[u] = exp2_fast(scur[kb][8 * st + u] * p.scale_log2 - mrun);
-          ls += e[u];
-        }
-        pb[kb][st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
-      }
+    float ls = qk_softmax(Buf<(k + 1) & (NBUF - 1)>{}, snxt, scur, pb);
+    if (__any(!(ls <= kSumLimit))) {
+      refresh(scur);
+      ls = softmax(scur, pb);
+    }
     lsum += ls;
-    // O^T += V^T P^T.
-    const unsigned char* Vt = smem + kbuf * L::BUF + L::TILE_BYTES;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int kbase = 32 * kb + 16 * st + 4 * hh + tr_row;
-#pragma unroll
-        for (int c = 0; c < NDB; ++c) {
-          const int dcol = D >= 32 ? 32 * c + tr_col : (tr_col & 15);
-          bf16x8 a = cat8(lds_read_tr4(reinterpret_cast<const bf16*>(Vt + swz_off<D>(kbase, dcol))),
-                          lds_read_tr4(reinterpret_cast<const bf16*>(Vt + swz_off<D>(kbase + 8, dcol))));
-          if (!d_lane_ok) a = bf16x8{};
-          acc[c] = mfma32(a, pb[kb][st], acc[c]);
-        }
-      }
-    if (nx1.valid()) prep(nx1.t, snxt);
+    pv(kc, pb);
+    if (nx1.valid()) mask(nx1.t, snxt);
     wait_copies();
     barrier_lds();
     scur[0] = snxt[0];
     scur[1] = snxt[1];
-    kbuf = k1;
     cur = nx1;
     nx1 = nx2;
     nx2 = nx3;
     if (nx3.valid()) nx3.next(m, qa, qb, TK);
+    return cur.valid();
+  };
+  if (cur.valid()) {
+    while (step(Buf<0>{}) && step(Buf<1>{}) && step(Buf<2>{}) && step(Buf<3>{})) {
+    }
   }
 
   // Epilogue: O = acc / l, LSE = ln(sum exp(scaled scores)); empty rows -> 0.

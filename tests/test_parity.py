@@ -161,3 +161,35 @@ def test_staged_backward_equals_fa_bwd(dtype):
     torch.cuda.synchronize()
     for name, a, b in zip(("dQ", "dK", "dV"), ref, (dq, dk, dv)):
         assert torch.equal(a, b), name
+
+
+# Launches with at least 512 workgroups of 256 query rows (B*Hq*ceil(Sq/256))
+# take the one-wave-per-SIMD forward at D=128 and the 8-wave dQ kernel; these
+# cases reach them with ragged tiles, GQA, every mask kind and padding.
+MANY = [
+    ("causal", CAUSAL, 300, 300, 0, None),
+    ("full_kv_valid", FULL, 300, 333, 0, (333, 300, 77, 1)),
+    ("ttt_t2", TTT, 300, 900, 0, (300, 250, 1, 299)),
+    ("causal_shift5", CAUSAL, 300, 300, 5, None),
+]
+
+
+@pytest.mark.parametrize("case", MANY, ids=[c[0] for c in MANY])
+def test_bf16_many_workgroups(case):
+    name, kind, Sq, Skv, shift, kvv = case
+    q, k, v, do = inputs(4, 128, 16, Sq, Skv, 128, torch.bfloat16, seed=61)
+    check_case(q, k, v, do, kind, "bf16", shift=shift, kv_valid=kvv, label=f"bf16 many-WG {name}")
+
+
+def test_bf16_many_workgroups_nan_padding():
+    q, k, v, do = inputs(4, 128, 16, 300, 333, 128, torch.bfloat16, seed=67)
+    kv_valid = (333, 300, 77, 1)
+    say("[many-WG nan padding]")
+    clean = run_gpu(q, k, v, do, FULL, 0, kv_valid)
+    k2, v2 = k.clone(), v.clone()
+    for b, n in enumerate(kv_valid):
+        k2[b, :, n:] = float("nan")
+        v2[b, :, n:] = float("nan")
+    dirty = run_gpu(q, k2, v2, do, FULL, 0, kv_valid)
+    for nm in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(clean[nm], dirty[nm]), nm
