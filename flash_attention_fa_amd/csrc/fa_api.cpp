@@ -145,10 +145,14 @@ void fill_common(fa::Params& p, const Shape& s, float scale, const fa_mask_desc&
   p.mask.kv_valid = m.kv_valid;
 }
 
-size_t delta_bytes(const Shape& s) {
+// One float32 [B, Hq, Sq] array, rounded up to 256 bytes.
+size_t row_array_bytes(const Shape& s) {
   size_t n = (size_t)std::max(s.B, 0) * (size_t)std::max(s.Hq, 0) * (size_t)std::max(s.Sq, 0) * 4;
   return (n + 255) / 256 * 256;
 }
+
+// Backward workspace: Delta, then LSE * log2(e) (both [B, Hq, Sq] float32).
+size_t delta_bytes(const Shape& s) { return 2 * row_array_bytes(s); }
 
 }  // namespace
 
@@ -258,6 +262,7 @@ static fa_status bwd_run(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStr
   p.dout = tensor(a->dout); p.dq = tensor(a->dq); p.dk = tensor(a->dk); p.dv = tensor(a->dv);
   p.lse_in = a->lse;
   p.delta = static_cast<float*>(ws);
+  p.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + row_array_bytes(s));
   for (int stage = first_stage; stage <= last_stage; ++stage) {
     hipError_t e = s.dtype == FA_BF16 ? fa::launch_bwd_bf16(p, stage, stream)
                                       : fa::launch_bwd_f32(p, stage, stream);

@@ -20,7 +20,9 @@ namespace fa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Delta = rowsum(dO * O), fp32.  D/8 lanes per row, 16-byte loads.
+// Delta = rowsum(dO * O), fp32, and the row's LSE in log2 units (the
+// backward kernels rebuild P as exp2(scale*log2(e) * s - LSE*log2(e))).
+// D/8 lanes per row, 16-byte loads.
 template <int D>
 __global__ void __launch_bounds__(256) delta_kernel(Params p) {
   constexpr int LPR = D / 8;        // lanes per row
@@ -42,7 +44,10 @@ __global__ void __launch_bounds__(256) delta_kernel(Params p) {
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (r < rows && c == 0) p.delta[r] = acc;
+  if (r < rows && c == 0) {
+    p.delta[r] = acc;
+    p.lse2[r] = p.lse_in[r] * 1.4426950408889634f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -550,6 +555,274 @@ dkdv_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// dK/dV with asynchronous staging (D >= 32).  Same work split as dkdv_kernel
+// (8 waves: wave w owns key block w % 4 and 32-row half w / 4 of each 64-row
+// query tile, natural scores S = Q K^T, a lane per key column), but the
+// workgroup's K and V rows and every step's Q and dO tiles are copied
+// HBM -> LDS by the asynchronous LDS copies of the forward, into unpadded
+// XOR-swizzled rows, double-buffered (one barrier per step).  dO^T and Q^T,
+// the A operands of dV^T += dO^T P and dK^T += Q^T dS, are read straight from
+// those row-major tiles with transposing LDS reads, so no transposed copy is
+// written at all.  Rows past Sq are copied from row 0 (finite) and masked.
+template <int D>
+struct KvDma {
+  static constexpr int NKB = 4;                        // 32-key blocks per workgroup
+  static constexpr int TKW = NKB * 32;                 // keys per workgroup
+  static constexpr int TQ = 64;                        // query rows per step
+  static constexpr int TILE = TQ * D * 2;              // one Q or dO tile (bytes)
+  static constexpr int STAGE = 2 * TILE + 2 * TQ * 4;  // Q, dO, LSE*log2(e), Delta
+  static constexpr int KVB = TKW * D * 2;              // the K (or V) rows
+  static constexpr int NDB = D / 32;
+  static constexpr int XBYTES = NKB * NDB * 16 * 64 * 4;   // one partial exchange
+  static constexpr int MAIN = 2 * STAGE + 2 * KVB;
+  static constexpr int BYTES = MAIN > XBYTES ? MAIN : XBYTES;
+};
+
+template <int D>
+__global__ void __launch_bounds__(512)
+dkdv_dma_kernel(Params p) {
+  using L = KvDma<D>;
+  constexpr int NKB = L::NKB, TKW = L::TKW, TQ = L::TQ, NDB = L::NDB;
+  constexpr int NW = 2 * NKB;
+  constexpr int NJ = D / 16;
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;         // rows per copy instruction
+  constexpr int QINS = TQ / RPI;        // copy instructions per Q (or dO) tile
+  constexpr int QLPW = 2 * QINS / NW;   // per wave per step
+  constexpr int KINS = TKW / RPI;       // copy instructions for the K (or V) rows
+  constexpr int KLPW = 2 * KINS / NW;
+  constexpr int ROW16 = 16 * 2 * D;     // bytes of 16 rows
+  static_assert(D >= 32 && QLPW * NW == 2 * QINS && KLPW * NW == 2 * KINS, "copy split");
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* const Ks = smem + 2 * L::STAGE;
+  unsigned char* const Vs = Ks + L::KVB;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int kblk = wave % NKB, qhalf = wave / NKB;
+
+  const int nkt = (p.Skv + TKW - 1) / TKW;
+  int col, rank;
+  map_block(blockIdx.x, p.B * p.Hkv, nkt, col, rank);
+  const int b = col / p.Hkv, hk = col % p.Hkv;
+  const MaskB m = resolve_mask(p, b);
+  const int ka = rank * TKW, kbnd = min(p.Skv, ka + TKW);
+  const int kw = ka + kblk * 32, kwe = min(p.Skv, kw + 32);
+  const int key = kw + l32;
+
+  const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
+  const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
+
+  // Copy-lane geometry (the same for every tile): lane -> (row in its 1 KB
+  // run, swizzled chunk).
+  const int crow = lane / CPR, cslot = lane % CPR;
+
+  // The workgroup's K and V rows; keys that are not real are copied from key
+  // 0 (finite values; their weights are masked to zero).
+#pragma unroll
+  for (int x = 0; x < KLPW; ++x) {
+    const int idx = wave * KLPW + x;
+    const int tensor = idx / KINS, ii = idx % KINS;
+    const int row = ii * RPI + crow;
+    const int kk = ka + row;
+    const bool ok = key_valid_nb(m, kk);
+    const int ch = 8 * (cslot ^ swz<D>(row));
+    const bf16* base = tensor == 0 ? Kg : Vg;
+    const int64_t ss = tensor == 0 ? p.k.ss : p.v.ss;
+    lds_dma16(base + (ok ? (int64_t)kk * ss + ch : (int64_t)ch), (tensor == 0 ? Ks : Vs) + ii * 1024);
+  }
+
+  int qlo, qhi;
+  query_hull(m, ka, kbnd, qlo, qhi);
+  const int t_first = qlo < qhi ? qlo / TQ : 0;
+  const int t_last = qlo < qhi ? (qhi + TQ - 1) / TQ : 0;
+  const int ntile = t_last - t_first;
+  // (query tile, head) pairs: tiles from the last down, the group's heads
+  // inside, so the workgroups sharing an XCD read the same Q / dO tiles at
+  // about the same time and its L2 serves them all.
+  const int nsteps = ntile * p.G;
+
+  // Stage s: Q and dO tiles by asynchronous copy; LSE*log2(e) and Delta of
+  // its rows through registers (64 threads, bounds-checked), written to LDS
+  // at the end of the previous step.
+  const bool stage_g = wave >= NW / 2;     // this wave copies dO rows (else Q)
+  auto stage_rows = [&](int step, int buf) __attribute__((always_inline)) {
+    const int h = hk * p.G + step % p.G;
+    const int q0 = (t_last - 1 - step / p.G) * TQ;
+    const bf16* Sg = stage_g ? static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh
+                             : static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
+    const int64_t sss = stage_g ? p.dout.ss : p.q.ss;
+    unsigned char* dst = smem + buf * L::STAGE + (stage_g ? L::TILE : 0);
+#pragma unroll
+    for (int x = 0; x < QLPW; ++x) {
+      const int ii = (wave % (NW / 2)) * QLPW + x;
+      const int row = ii * RPI + crow;
+      const int q = q0 + row;
+      const int ch = 8 * (cslot ^ swz<D>(row));
+      lds_dma16(Sg + (q < p.Sq ? (int64_t)q * sss + ch : (int64_t)ch), dst + ii * 1024);
+    }
+  };
+  float lrow = 0.f, drow = 0.f;
+  auto fetch_rowvals = [&](int step) __attribute__((always_inline)) {
+    if (tid < TQ) {
+      const int h = hk * p.G + step % p.G;
+      const int q = (t_last - 1 - step / p.G) * TQ + tid;
+      const int64_t rb = ((int64_t)b * p.Hq + h) * p.Sq;
+      lrow = q < p.Sq ? p.lse2[rb + q] : 0.f;
+      drow = q < p.Sq ? p.delta[rb + q] : 0.f;
+    }
+  };
+  auto store_rowvals = [&](int buf) __attribute__((always_inline)) {
+    float* Ls = reinterpret_cast<float*>(smem + buf * L::STAGE + 2 * L::TILE);
+    if (tid < TQ) { Ls[tid] = lrow; Ls[TQ + tid] = drow; }
+  };
+
+  if (nsteps > 0) {
+    stage_rows(0, 0);
+    fetch_rowvals(0);
+    wait_vmcnt<0>();
+    store_rowvals(0);
+  } else {
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+
+  // Lane-constant offsets: row reads (16 rows repeat their swizzle) and the
+  // transposing reads of dO^T / Q^T (as the forward reads V^T).
+  int roff[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) roff[j] = swz_off<D>(l32, 16 * j + 8 * hh);
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int toff[2][NDB];
+#pragma unroll
+  for (int c = 0; c < NDB; ++c) {
+    toff[0][c] = swz_off<D>(4 * hh + tr_row, 32 * c + tr_col);
+    toff[1][c] = swz_off<D>(4 * hh + tr_row + 8, 32 * c + tr_col);
+  }
+  const int qrow0 = 32 * qhalf * 2 * D;      // byte offset of this wave's 32 query rows
+  const unsigned char* Kw = Ks + kblk * 32 * 2 * D;
+  const unsigned char* Vw = Vs + kblk * 32 * 2 * D;
+
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int c = 0; c < NDB; ++c) { dka[c] = f32x16{}; dva[c] = f32x16{}; }
+
+  for (int step = 0; step < nsteps; ++step) {
+    const int buf = step & 1;
+    const bool more = step + 1 < nsteps;
+    if (more) {
+      stage_rows(step + 1, buf ^ 1);
+      fetch_rowvals(step + 1);
+    }
+    const unsigned char* Qt = smem + buf * L::STAGE;
+    const unsigned char* Gt = Qt + L::TILE;
+    const float* Ls = reinterpret_cast<const float*>(Qt + 2 * L::TILE) + 32 * qhalf;
+    const float* Ds = Ls + TQ;
+    const int q0 = (t_last - 1 - step / p.G) * TQ;
+    const int qa = q0 + 32 * qhalf;
+    int state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + 32));
+    if (state == TILE_FULL && qa + 32 > p.Sq) state = TILE_PART;   // rows past Sq
+    if (state != TILE_SKIP) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bf16x8 aq = *FA_LDS(const bf16x8, Qt + qrow0 + roff[j]);
+        const bf16x8 ag = *FA_LDS(const bf16x8, Gt + qrow0 + roff[j]);
+        const bf16x8 bk = *FA_LDS(const bf16x8, Kw + roff[j]);
+        const bf16x8 bv = *FA_LDS(const bf16x8, Vw + roff[j]);
+        s = mfma32(aq, bk, s);
+        dp = mfma32(ag, bv, dp);
+      }
+      // Per-register query rows: q = qa + 8*(i/4) + 4*hh + i%4.
+      if (state == TILE_PART) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qi = qa + 8 * (i >> 2) + 4 * hh + (i & 3);
+          s[i] = (allowed(m, qi, key) & (qi < p.Sq)) ? s[i] : -INFINITY;
+        }
+      }
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float pe[8], de[8];
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g = 2 * st + g2;
+          const f32x4 l4 = *FA_LDS(const f32x4, Ls + 8 * g + 4 * hh);
+          const f32x4 d4 = *FA_LDS(const f32x4, Ds + 8 * g + 4 * hh);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = 4 * g + u;
+            const float pr = exp2_fast(s[i] * p.scale_log2 - l4[u]);
+            pe[4 * g2 + u] = pr;
+            de[4 * g2 + u] = pr * (dp[i] - d4[u]);
+          }
+        }
+        pb[st] = cat8(to_bf16x4(pe[0], pe[1], pe[2], pe[3]), to_bf16x4(pe[4], pe[5], pe[6], pe[7]));
+        dsb[st] = cat8(to_bf16x4(de[0], de[1], de[2], de[3]), to_bf16x4(de[4], de[5], de[6], de[7]));
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dS: A operands read transposed from the
+      // row-major tiles (rows 16 st + (4 hh + r) and + 8, the order the score
+      // registers hold the rows in).
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int rows = qrow0 + st * ROW16;
+#pragma unroll
+        for (int c = 0; c < NDB; ++c) {
+          const bf16x8 ag = cat8(lds_read_tr4(reinterpret_cast<const bf16*>(Gt + rows + toff[0][c])),
+                                 lds_read_tr4(reinterpret_cast<const bf16*>(Gt + rows + toff[1][c])));
+          const bf16x8 aq = cat8(lds_read_tr4(reinterpret_cast<const bf16*>(Qt + rows + toff[0][c])),
+                                 lds_read_tr4(reinterpret_cast<const bf16*>(Qt + rows + toff[1][c])));
+          dva[c] = mfma32(ag, pb[st], dva[c]);
+          dka[c] = mfma32(aq, dsb[st], dka[c]);
+        }
+      }
+    }
+    if (more) store_rowvals(buf ^ 1);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  // Pair reduction through LDS (the loop's last barrier freed it), then
+  // dK = s * (dK^T)^T, dV = (dV^T)^T; lane (key, hh) holds d = 32c + 8g + 4hh + u.
+  float* X = reinterpret_cast<float*>(smem);
+  bf16* DKg = static_cast<bf16*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh;
+  bf16* DVg = static_cast<bf16*>(const_cast<void*>(p.dv.ptr)) + b * p.dv.sb + hk * p.dv.sh;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    f32x16* acc = which == 0 ? dka : dva;
+    if (qhalf == 1) {
+#pragma unroll
+      for (int c = 0; c < NDB; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) X[((kblk * NDB + c) * 16 + i) * 64 + lane] = acc[c][i];
+    }
+    __syncthreads();
+    if (qhalf == 0) {
+#pragma unroll
+      for (int c = 0; c < NDB; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[c][i] += X[((kblk * NDB + c) * 16 + i) * 64 + lane];
+      if (key < p.Skv) {
+        const float sc = which == 0 ? p.scale : 1.0f;
+        bf16* dst_row = (which == 0 ? DKg + (int64_t)key * p.dk.ss : DVg + (int64_t)key * p.dv.ss);
+#pragma unroll
+        for (int c = 0; c < NDB; ++c)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d = 32 * c + 8 * g + 4 * hh;
+            *reinterpret_cast<bf16x4*>(dst_row + d) =
+                to_bf16x4(acc[c][4 * g] * sc, acc[c][4 * g + 1] * sc, acc[c][4 * g + 2] * sc,
+                          acc[c][4 * g + 3] * sc);
+          }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <typename K>
 hipError_t set_lds(K k, int bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -575,7 +848,16 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (stage == STAGE_DKDV) {
+  if (stage == STAGE_DKDV && D == 128) {
+    using LD = KvDma<D == 128 ? D : 128>;
+    const int64_t nblk = (int64_t)p.B * p.Hkv * ((p.Skv + LD::TKW - 1) / LD::TKW);
+    if (nblk > 0) {
+      auto k = dkdv_dma_kernel<D == 128 ? D : 128>;
+      if ((e = set_lds(k, LD::BYTES)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(512), LD::BYTES, stream, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  } else if (stage == STAGE_DKDV) {
     constexpr int NKB = 4, TKW = NKB * 32;
     constexpr bool KLDS = D >= 128;
     const int64_t nblk = (int64_t)p.B * p.Hkv * ((p.Skv + TKW - 1) / TKW);

@@ -290,6 +290,12 @@ __device__ __forceinline__ bool key_valid(const MaskB& m, int j) {
   return j < m.kvv;
 }
 
+// key_valid without branches on the lane's key (the mask kind is uniform).
+__device__ __forceinline__ bool key_valid_nb(const MaskB& m, int j) {
+  const int jm = m.kind == MASK_TTT ? j - (j / m.L) * m.L : j;
+  return (j < m.Skv) & (jm < m.kvv);
+}
+
 __device__ __forceinline__ int num_segments(const MaskB& m) {
   return m.kind == MASK_TTT ? (m.L > 0 ? m.Skv / m.L : 0) : 1;
 }

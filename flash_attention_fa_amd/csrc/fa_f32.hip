@@ -109,6 +109,7 @@ __global__ void __launch_bounds__(256) delta_f32_kernel(Params p) {
   float acc = 0.f;
   for (int d = 0; d < D; ++d) acc = fmaf(orow[d], grow[d], acc);
   p.delta[r] = acc;
+  p.lse2[r] = p.lse_in[r] * 1.4426950408889634f;
 }
 
 template <int D>

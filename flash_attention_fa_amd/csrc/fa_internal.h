@@ -28,7 +28,8 @@ struct Params {
   Tensor dq, dk, dv;   // backward outputs
   float* lse;          // forward output
   const float* lse_in; // backward input
-  float* delta;        // backward workspace [B, Hq, Sq]
+  float* delta;        // backward workspace: Delta [B, Hq, Sq]
+  float* lse2;         // backward workspace: LSE * log2(e) [B, Hq, Sq]
 };
 
 // Launchers (one translation unit per kernel family).  Each returns the

@@ -119,9 +119,9 @@ typedef struct {
 /* Forward: writes O and LSE.  Asynchronous on `stream` (0 = null stream). */
 fa_status fa_fwd(const fa_fwd_args* args, hipStream_t stream);
 
-/* Bytes of device scratch fa_bwd needs for these arguments (Delta, a float32
- * [B, Hq, Sq] array, rounded up to 256 bytes): linear in Sq, never S x S.
- * Returns 0 when args is NULL. */
+/* Bytes of device scratch fa_bwd needs for these arguments: two float32
+ * [B, Hq, Sq] arrays (Delta, and LSE in log2 units), each rounded up to 256
+ * bytes; linear in Sq, never S x S.  Returns 0 when args is NULL. */
 size_t fa_bwd_workspace_bytes(const fa_bwd_args* args);
 
 /* Backward: writes dQ, dK, dV; bitwise identical on every rerun (fixed
@@ -134,14 +134,14 @@ fa_status fa_bwd(const fa_bwd_args* args, void* ws, size_t ws_bytes,
 typedef enum {
   FA_BWD_DELTA = 0,  /* Delta_i = sum_d dO_id O_id into the workspace (the row
                         term of dS = P * (dP - Delta); CS336 "Flash Attention
-                        (Triton)", backward pass) */
+                        (Triton)", backward pass), beside LSE_i * log2(e) */
   FA_BWD_DKDV = 1,   /* dK, dV: one workgroup per key block, summing over the
                         group's query heads in a fixed order */
   FA_BWD_DQ = 2      /* dQ: one workgroup per query block */
 } fa_bwd_stage_id;
 
 /* Runs one stage of fa_bwd with the same arguments, validation and workspace.
- * DKDV and DQ read the Delta that a DELTA stage left in `ws` (on the same
+ * DKDV and DQ read what a DELTA stage left in `ws` (on the same
  * stream, or ordered after it by the caller); given that, running DELTA,
  * DKDV, DQ in turn writes bitwise the same dQ, dK, dV as fa_bwd.  For callers
  * that overlap the two gradient kernels on separate streams or time them one

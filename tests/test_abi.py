@@ -161,7 +161,7 @@ def test_forward_empty_is_a_noop():
 def test_backward_validation():
     a = bwd_args()
     need = _lib.lib().fa_bwd_workspace_bytes(a)
-    assert need == (1 * 4 * 64 * 4 + 255) // 256 * 256
+    assert need == 2 * ((1 * 4 * 64 * 4 + 255) // 256 * 256)
     assert _lib.lib().fa_bwd_workspace_bytes(None) == 0
     st, msg = bwd(a, ws_bytes=need - 1)
     assert st == _lib.FA_ERR_INVALID_ARG and "workspace too small" in msg
@@ -186,7 +186,7 @@ def test_backward_validation():
 def test_workspace_is_linear_in_sequence_length():
     sizes = [_lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=s, Skv=s, D=128))
              for s in (16384, 32768)]
-    assert sizes[1] == 2 * sizes[0] == 2 * 32 * 16384 * 4
+    assert sizes[1] == 2 * sizes[0] == 2 * 2 * 32 * 16384 * 4
 
 
 def test_bwd_stage_rejects_unknown_stage():
