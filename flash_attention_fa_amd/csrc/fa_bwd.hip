@@ -19,6 +19,11 @@
 namespace fa {
 namespace {
 
+template <int K>
+struct Buf {
+  static constexpr int value = K;
+};
+
 // ---------------------------------------------------------------------------
 // Delta = rowsum(dO * O), fp32, and the row's LSE in log2 units (the
 // backward kernels rebuild P as exp2(scale*log2(e) * s - LSE*log2(e))).
@@ -271,6 +276,222 @@ dq_kernel(Params p) {
           }
         }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ with asynchronous staging (D >= 32): the forward's pipeline with a third
+// product.  Key tiles of K and V rows are copied HBM -> LDS into a ring of
+// four XOR-swizzled buffers three tiles ahead; per tile, S^T = K Q^T and
+// dP^T = V dO^T (Q and dO in registers, K and V rows from LDS), dS^T =
+// P^T (dP^T - Delta) with P^T = exp2(scale log2(e) S^T - LSE log2(e)), and
+// dQ^T += K^T dS^T with K^T read transposed from the row-major K tile.
+constexpr int DQ_NBUF = 4;
+
+template <int D>
+struct DqDma {
+  static constexpr int TILE = DQ_TK * D * 2;   // K or V rows of one tile
+  static constexpr int BUF = 2 * TILE;
+  static constexpr int BYTES = DQ_NBUF * BUF;
+};
+
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64, 2)
+dq_dma_kernel(Params p) {
+  using L = DqDma<D>;
+  constexpr int TQ = NW * 32;
+  constexpr int TK = DQ_TK;
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 64 / CPR;
+  constexpr int NINS = TK / RPI;
+  constexpr int LPW = (2 * NINS + NW - 1) / NW;
+  constexpr bool ALL_COPY = LPW * NW == 2 * NINS;
+  constexpr int NDB = D / 32;
+  constexpr int NJ = D / 16;
+  constexpr int ROW16 = 16 * 2 * D;
+  static_assert(D >= 32, "transposing reads need D >= 32");
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int l32 = lane & 31, hh = lane >> 5;
+  (void)tid;
+
+  const int nq = (p.Sq + TQ - 1) / TQ;
+  int col, rank;
+  map_block(blockIdx.x, p.B * p.Hq, nq, col, rank);
+  const int b = col / p.Hq, h = col % p.Hq, hk = h / p.G;
+  const int qtile = p.mask.kind == MASK_FULL ? rank : nq - 1 - rank;
+  const MaskB m = resolve_mask(p, b);
+  const int qa = qtile * TQ, qb = min(p.Sq, qa + TQ);
+  const int wa = qa + wave * 32, wb = min(p.Sq, wa + 32);
+  const int qi = wa + l32;
+
+  const bf16* Qg = static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
+  const bf16* Gg = static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh;
+  const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
+  const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
+  const int64_t rowbase = ((int64_t)b * p.Hq + h) * p.Sq;
+
+  // Q^T and dO^T as B operands; LSE (log2 units) and Delta one per lane.
+  bf16x8 qreg[NJ], greg[NJ];
+  const bool qok = qi < p.Sq;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    qreg[j] = qok ? *reinterpret_cast<const bf16x8*>(Qg + (int64_t)qi * p.q.ss + 16 * j + 8 * hh) : bf16x8{};
+    greg[j] = qok ? *reinterpret_cast<const bf16x8*>(Gg + (int64_t)qi * p.dout.ss + 16 * j + 8 * hh) : bf16x8{};
+  }
+  const float l2 = qok ? p.lse2[rowbase + qi] : 0.f;
+  const float dlt = qok ? p.delta[rowbase + qi] : 0.f;
+  wait_vmcnt<0>();
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int c = 0; c < NDB; ++c) acc[c] = f32x16{};
+
+  const int crow = lane / CPR, cslot = lane % CPR;
+  int roff[LPW];
+#pragma unroll
+  for (int x = 0; x < LPW; ++x) {
+    const int idx = wave * LPW + x;
+    const int ii = idx % NINS;
+    const int row = ii * RPI + crow;
+    const int64_t ss = idx / NINS == 0 ? p.k.ss : p.v.ss;
+    roff[x] = (int)(row * ss) + 8 * (cslot ^ swz<D>(row));
+  }
+  // Key tile t (K rows then V rows) into buffer k; keys that are not real
+  // (and every key when t < 0) come from key 0: finite, and masked.
+  auto copy_tile = [&](int t, int k) __attribute__((always_inline)) {
+    const int tb = t * TK;
+#pragma unroll
+    for (int x = 0; x < LPW; ++x) {
+      const int idx = wave * LPW + x;
+      if (ALL_COPY || idx < 2 * NINS) {
+        const int tensor = idx / NINS, ii = idx % NINS;
+        const int row = ii * RPI + crow;
+        const bool ok = (t >= 0) & key_valid_nb(m, tb + row);
+        const bf16* base = tensor == 0 ? Kg : Vg;
+        const int64_t ss = tensor == 0 ? p.k.ss : p.v.ss;
+        const int64_t o_real = (int64_t)tb * ss + roff[x];
+        const int64_t o_key0 = 8 * (cslot ^ swz<D>(row));
+        lds_dma16(base + (ok ? o_real : o_key0), smem + k * L::BUF + tensor * L::TILE + ii * 1024);
+      }
+    }
+  };
+  const int my_ins = ALL_COPY ? LPW : (wave * LPW < 2 * NINS ? LPW : 0);
+  auto wait_copies = [&]() __attribute__((always_inline)) {
+    if (my_ins == LPW) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
+  };
+
+  int koff[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) koff[j] = swz_off<D>(l32, 16 * j + 8 * hh);
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int toff[2][NDB];
+#pragma unroll
+  for (int c = 0; c < NDB; ++c) {
+    toff[0][c] = swz_off<D>(4 * hh + tr_row, 32 * c + tr_col);
+    toff[1][c] = swz_off<D>(4 * hh + tr_row + 8, 32 * c + tr_col);
+  }
+
+  TileWalk cur;
+  cur.start(m, qa, qb, TK);
+  TileWalk nx1 = cur;
+  if (nx1.valid()) nx1.next(m, qa, qb, TK);
+  TileWalk nx2 = nx1;
+  if (nx2.valid()) nx2.next(m, qa, qb, TK);
+  TileWalk nx3 = nx2;
+  if (nx3.valid()) nx3.next(m, qa, qb, TK);
+  if (cur.valid()) {
+    copy_tile(cur.t, 0);
+    copy_tile(nx1.valid() ? nx1.t : -1, 1);
+    copy_tile(nx2.valid() ? nx2.t : -1, 2);
+    wait_copies();
+  }
+  barrier_lds();
+
+  auto step = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    copy_tile(nx3.valid() ? nx3.t : -1, (k + 3) % DQ_NBUF);
+    const int k0 = cur.t * TK;
+    const int state = tile_state(m, k0, TK, wa, wb);
+    if (state != TILE_SKIP) {
+      const unsigned char* Kt = smem + k * L::BUF;
+      const unsigned char* Vt = Kt + L::TILE;
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 ak = *FA_LDS(const bf16x8, Kt + 2 * kb * ROW16 + koff[j]);
+          const bf16x8 av = *FA_LDS(const bf16x8, Vt + 2 * kb * ROW16 + koff[j]);
+          s[kb] = mfma32(ak, qreg[j], s[kb]);
+          dp[kb] = mfma32(av, greg[j], dp[kb]);
+        }
+      if (state == TILE_PART) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
+            s[kb][i] = allowed(m, qi, key) ? s[kb][i] : -INFINITY;
+          }
+      }
+      // dS^T = P^T (dP^T - Delta), rounded to bf16 for the K^T dS^T product.
+      bf16x8 dsb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          float e[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = 8 * st + u;
+            e[u] = exp2_fast(s[kb][i] * p.scale_log2 - l2) * (dp[kb][i] - dlt);
+          }
+          dsb[kb][st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
+        }
+      // dQ^T += K^T dS^T, K^T read transposed from the K rows.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int rows = (2 * kb + st) * ROW16;
+#pragma unroll
+          for (int c = 0; c < NDB; ++c) {
+            const bf16x8 a = cat8(lds_read_tr4(reinterpret_cast<const bf16*>(Kt + rows + toff[0][c])),
+                                  lds_read_tr4(reinterpret_cast<const bf16*>(Kt + rows + toff[1][c])));
+            acc[c] = mfma32(a, dsb[kb][st], acc[c]);
+          }
+        }
+    }
+    wait_copies();
+    barrier_lds();
+    cur = nx1;
+    nx1 = nx2;
+    nx2 = nx3;
+    if (nx3.valid()) nx3.next(m, qa, qb, TK);
+    return cur.valid();
+  };
+  if (cur.valid()) {
+    while (step(Buf<0>{}) && step(Buf<1>{}) && step(Buf<2>{}) && step(Buf<3>{})) {
+    }
+  }
+  wait_vmcnt<0>();   // copies of tiles past the end
+
+  bf16* Dg = static_cast<bf16*>(const_cast<void*>(p.dq.ptr)) + b * p.dq.sb + h * p.dq.sh;
+  if (qok) {
+#pragma unroll
+    for (int c = 0; c < NDB; ++c)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * c + 8 * g + 4 * hh;
+        const float sc = p.scale;
+        *reinterpret_cast<bf16x4*>(Dg + (int64_t)qi * p.dq.ss + d) =
+            to_bf16x4(acc[c][4 * g] * sc, acc[c][4 * g + 1] * sc, acc[c][4 * g + 2] * sc, acc[c][4 * g + 3] * sc);
+      }
   }
 }
 
@@ -848,14 +1069,16 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (stage == STAGE_DKDV && D == 128) {
-    using LD = KvDma<D == 128 ? D : 128>;
-    const int64_t nblk = (int64_t)p.B * p.Hkv * ((p.Skv + LD::TKW - 1) / LD::TKW);
-    if (nblk > 0) {
-      auto k = dkdv_dma_kernel<D == 128 ? D : 128>;
-      if ((e = set_lds(k, LD::BYTES)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(512), LD::BYTES, stream, p);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+  if constexpr (D == 128) {
+    if (stage == STAGE_DKDV) {
+      using LD = KvDma<D>;
+      const int64_t nblk = (int64_t)p.B * p.Hkv * ((p.Skv + LD::TKW - 1) / LD::TKW);
+      if (nblk > 0) {
+        auto k = dkdv_dma_kernel<D>;
+        if ((e = set_lds(k, LD::BYTES)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(512), LD::BYTES, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
     }
   } else if (stage == STAGE_DKDV) {
     constexpr int NKB = 4, TKW = NKB * 32;
@@ -872,8 +1095,17 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
   if (stage == STAGE_DQ && p.B > 0 && p.Sq > 0) {
     // 8-wave workgroups when there are enough to fill the chip twice over
     const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
-    if ((e = wg8 >= 512 ? launch_dq<D, 1, 8>(p, stream) : launch_dq<D, 1, 4>(p, stream)) != hipSuccess)
-      return e;
+    if constexpr (D == 128) {
+      auto k = wg8 >= 512 ? dq_dma_kernel<D, 8> : dq_dma_kernel<D, 4>;
+      const int nw = wg8 >= 512 ? 8 : 4;
+      const int64_t nblk = (int64_t)p.B * p.Hq * ((p.Sq + nw * 32 - 1) / (nw * 32));
+      if ((e = set_lds(k, DqDma<D>::BYTES)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(nw * 64), DqDma<D>::BYTES, stream, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+      if ((e = wg8 >= 512 ? launch_dq<D, 1, 8>(p, stream) : launch_dq<D, 1, 4>(p, stream)) != hipSuccess)
+        return e;
+    }
   }
   return hipSuccess;
 }

@@ -251,9 +251,10 @@ __device__ __forceinline__ bool allowed(const MaskB& m, int i, int j) {
   if (m.kind == MASK_FULL) return valid;
   const bool causal = (j <= i - m.shift) & valid;
   if (m.kind == MASK_CAUSAL) return causal;
-  // TTT suffix: key of a later step at the query's own position.
+  // TTT suffix: key of a later step at the query's own position (keys past
+  // Skv in a ragged last tile are not keys of any step).
   const int jm = j - (j / m.L) * m.L;
-  return causal | ((j >= m.L) & (jm == i) & (jm < m.kvv));
+  return causal | ((j >= m.L) & (j < m.Skv) & (jm == i) & (jm < m.kvv));
 }
 
 // Instruction-class masks of the scheduler's group barriers, and a group

@@ -339,6 +339,7 @@ fwd_kernel(Params p) {
     while (step(Buf<0>{}) && step(Buf<1>{}) && step(Buf<2>{}) && step(Buf<3>{})) {
     }
   }
+  wait_vmcnt<0>();   // copies of tiles past the end land before the workgroup ends
 
   // Epilogue: O = acc / l, LSE = ln(sum exp(scaled scores)); empty rows -> 0.
   bf16* Og = static_cast<bf16*>(const_cast<void*>(p.o.ptr)) + b * p.o.sb + h * p.o.sh;

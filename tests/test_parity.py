@@ -79,7 +79,10 @@ def test_bf16_causal_sq_ne_skv():
 
 @pytest.mark.parametrize("L,t,shift,kvv", [
     (256, 2, 0, None), (130, 1, 0, None), (130, 2, 2, None), (100, 2, 0, (70,)),
-    (300, 0, 0, None), (96, 3, 1, (90,))])
+    (300, 0, 0, None), (96, 3, 1, (90,)),
+    # short steps: the ragged last key tile reaches past Skv into positions
+    # that the rows of one 32-row block would match
+    (40, 1, 0, None), (20, 2, 0, None), (50, 3, 1, (45,))])
 def test_bf16_ttt(L, t, shift, kvv):
     q, k, v, do = inputs(1, 8, 2, L, (t + 1) * L, 128, torch.bfloat16, seed=L + t)
     check_case(q, k, v, do, TTT, "bf16", shift=shift, kv_valid=kvv,
