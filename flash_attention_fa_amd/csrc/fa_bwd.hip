@@ -14,6 +14,8 @@
 // dK/dV are owned by key tiles and dQ by query tiles, so every output element
 // is summed by exactly one workgroup in a fixed order: reruns are bitwise
 // identical.  Keys no query may attend get exact zeros.
+#include <climits>
+
 #include "fa_device.h"
 
 namespace fa {
@@ -866,30 +868,45 @@ dkdv_dma_kernel(Params p) {
 
   // Stage s: Q and dO tiles by asynchronous copy; LSE*log2(e) and Delta of
   // its rows through registers (64 threads, bounds-checked), written to LDS
-  // at the end of the previous step.
+  // at the end of the previous step.  Step s is (tile t_last-1 - s/G, head
+  // hk*G + s%G); StepPos walks that order without divisions.
   const bool stage_g = wave >= NW / 2;     // this wave copies dO rows (else Q)
-  auto stage_rows = [&](int step, int buf) __attribute__((always_inline)) {
-    const int h = hk * p.G + step % p.G;
-    const int q0 = (t_last - 1 - step / p.G) * TQ;
-    const bf16* Sg = stage_g ? static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh
-                             : static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
-    const int64_t sss = stage_g ? p.dout.ss : p.q.ss;
+  const bf16* const Sbase = stage_g ? static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb
+                                    : static_cast<const bf16*>(p.q.ptr) + b * p.q.sb;
+  const int64_t ssh = stage_g ? p.dout.sh : p.q.sh;
+  const int64_t sss = stage_g ? p.dout.ss : p.q.ss;
+  // this lane's element offsets inside a tile (row * stride + swizzled chunk)
+  int64_t soff[QLPW];
+  int srow[QLPW];
+#pragma unroll
+  for (int x = 0; x < QLPW; ++x) {
+    const int ii = (wave % (NW / 2)) * QLPW + x;
+    srow[x] = ii * RPI + crow;
+    soff[x] = (int64_t)srow[x] * sss + 8 * (cslot ^ swz<D>(srow[x]));
+  }
+  struct StepPos {
+    int hs, q0;   // head slot in the group, first query row of the tile
+  };
+  auto advance = [&](StepPos& sp) __attribute__((always_inline)) {
+    if (++sp.hs == p.G) { sp.hs = 0; sp.q0 -= TQ; }
+  };
+  auto stage_rows = [&](const StepPos& sp, int buf) __attribute__((always_inline)) {
+    const bf16* Sg = Sbase + (int64_t)(hk * p.G + sp.hs) * ssh + (int64_t)sp.q0 * sss;
     unsigned char* dst = smem + buf * L::STAGE + (stage_g ? L::TILE : 0);
+    const bool whole = sp.q0 + TQ <= p.Sq;   // every row real: no per-lane select
 #pragma unroll
     for (int x = 0; x < QLPW; ++x) {
       const int ii = (wave % (NW / 2)) * QLPW + x;
-      const int row = ii * RPI + crow;
-      const int q = q0 + row;
-      const int ch = 8 * (cslot ^ swz<D>(row));
-      lds_dma16(Sg + (q < p.Sq ? (int64_t)q * sss + ch : (int64_t)ch), dst + ii * 1024);
+      const bool ok = whole || sp.q0 + srow[x] < p.Sq;
+      // rows past Sq are copied from the tile's first row (real, finite)
+      lds_dma16(Sg + (ok ? soff[x] : soff[x] - (int64_t)srow[x] * sss), dst + ii * 1024);
     }
   };
   float lrow = 0.f, drow = 0.f;
-  auto fetch_rowvals = [&](int step) __attribute__((always_inline)) {
+  auto fetch_rowvals = [&](const StepPos& sp) __attribute__((always_inline)) {
     if (tid < TQ) {
-      const int h = hk * p.G + step % p.G;
-      const int q = (t_last - 1 - step / p.G) * TQ + tid;
-      const int64_t rb = ((int64_t)b * p.Hq + h) * p.Sq;
+      const int q = sp.q0 + tid;
+      const int64_t rb = ((int64_t)b * p.Hq + hk * p.G + sp.hs) * p.Sq;
       lrow = q < p.Sq ? p.lse2[rb + q] : 0.f;
       drow = q < p.Sq ? p.delta[rb + q] : 0.f;
     }
@@ -898,10 +915,13 @@ dkdv_dma_kernel(Params p) {
     float* Ls = reinterpret_cast<float*>(smem + buf * L::STAGE + 2 * L::TILE);
     if (tid < TQ) { Ls[tid] = lrow; Ls[TQ + tid] = drow; }
   };
+  StepPos cur{0, (t_last - 1) * TQ};
+  StepPos nxt = cur;
+  if (nsteps > 0) advance(nxt);
 
   if (nsteps > 0) {
-    stage_rows(0, 0);
-    fetch_rowvals(0);
+    stage_rows(cur, 0);
+    fetch_rowvals(cur);
     wait_vmcnt<0>();
     store_rowvals(0);
   } else {
@@ -930,21 +950,30 @@ dkdv_dma_kernel(Params p) {
 #pragma unroll
   for (int c = 0; c < NDB; ++c) { dka[c] = f32x16{}; dva[c] = f32x16{}; }
 
+  // Rows from qfull on see every key of this wave's block (CAUSAL / FULL):
+  // their tiles need no mask and no classification.
+  int qfull = INT_MAX;
+  if (kwe <= m.kvv && kw < kwe) {
+    if (m.kind == MASK_FULL) qfull = 0;
+    else if (m.kind == MASK_CAUSAL) qfull = kwe - 1 + m.shift;
+  }
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
     const bool more = step + 1 < nsteps;
     if (more) {
-      stage_rows(step + 1, buf ^ 1);
-      fetch_rowvals(step + 1);
+      stage_rows(nxt, buf ^ 1);
+      fetch_rowvals(nxt);
     }
     const unsigned char* Qt = smem + buf * L::STAGE;
     const unsigned char* Gt = Qt + L::TILE;
     const float* Ls = reinterpret_cast<const float*>(Qt + 2 * L::TILE) + 32 * qhalf;
     const float* Ds = Ls + TQ;
-    const int q0 = (t_last - 1 - step / p.G) * TQ;
-    const int qa = q0 + 32 * qhalf;
-    int state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + 32));
-    if (state == TILE_FULL && qa + 32 > p.Sq) state = TILE_PART;   // rows past Sq
+    const int qa = cur.q0 + 32 * qhalf;
+    int state = TILE_FULL;
+    if (!(qa >= qfull && qa + 32 <= p.Sq)) {
+      state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + 32));
+      if (state == TILE_FULL && qa + 32 > p.Sq) state = TILE_PART;   // rows past Sq
+    }
     if (state != TILE_SKIP) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -1004,6 +1033,8 @@ dkdv_dma_kernel(Params p) {
     if (more) store_rowvals(buf ^ 1);
     wait_vmcnt<0>();
     __syncthreads();
+    cur = nxt;
+    advance(nxt);
   }
 
   // Pair reduction through LDS (the loop's last barrier freed it), then
