@@ -262,7 +262,7 @@ def main():
                 "pct_of_peak": round(100 * tf(f_bwd, bwd_med) / PEAK_BF16_TFLOPS, 2)},
         "gflop_per_step": round((f_fwd + f_bwd) / 1e9, 3),
         "kernels": kernels,
-        "roofline": {"kernel": "dkdv_kernel (fa_bwd_stage FA_BWD_DKDV: one launch)",
+        "roofline": {"kernel": "dK/dV kernel (fa_bwd_stage FA_BWD_DKDV: one launch)",
                      "bound": "mfma", "achieved": round(dkdv_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
