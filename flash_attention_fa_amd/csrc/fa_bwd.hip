@@ -396,6 +396,8 @@ dq_dma_kernel(Params p) {
     toff[1][c] = swz_off<D>(4 * hh + tr_row + 8, 32 * c + tr_col);
   }
 
+  // tiles below full_end: every key allowed for every row of this wave
+  const int full_end = full_tiles_below(m, wa, TK);
   TileWalk cur;
   cur.start(m, qa, qb, TK);
   TileWalk nx1 = cur;
@@ -416,7 +418,7 @@ dq_dma_kernel(Params p) {
     constexpr int k = decltype(kc)::value;
     copy_tile(nx3.valid() ? nx3.t : -1, (k + 3) % DQ_NBUF);
     const int k0 = cur.t * TK;
-    const int state = tile_state(m, k0, TK, wa, wb);
+    const int state = cur.t < full_end ? TILE_FULL : tile_state(m, k0, TK, wa, wb);
     if (state != TILE_SKIP) {
       const unsigned char* Kt = smem + k * L::BUF;
       const unsigned char* Vt = Kt + L::TILE;

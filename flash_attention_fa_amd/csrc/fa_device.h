@@ -341,6 +341,15 @@ __device__ __forceinline__ int rect_state(const MaskB& m, int k0, int k1, int qa
   return TILE_SKIP;
 }
 
+// Number of leading TK-key tiles that every query row >= qa may attend in
+// full (keys below kv_valid and, unless FULL, at most qa - shift): tiles
+// [0, result) need neither classification nor a mask for rows >= qa.
+__device__ __forceinline__ int full_tiles_below(const MaskB& m, int qa, int TK) {
+  int lim = m.kvv;
+  if (m.kind != MASK_FULL) lim = min(lim, qa - m.shift + 1);
+  return lim > 0 ? lim / TK : 0;
+}
+
 __device__ __forceinline__ int tile_state(const MaskB& m, int k0, int TK, int qa, int qb) {
   return rect_state(m, k0, k0 + TK, qa, qb);
 }

@@ -122,9 +122,10 @@ fwd_kernel(Params p) {
     zoff[x] = 8 * gch;
   }
   const bool ttt = m.kind == MASK_TTT;
+  const int whole_lim = ttt ? 0 : m.kvv;      // tiles ending at or below it hold only real keys
   auto copy_tile = [&](int t, int k) __attribute__((always_inline)) {
     const int tb = t * TK;
-    const int lim = t >= 0 ? m.kvv - tb : 0;   // rows below lim are real keys (FULL/CAUSAL)
+    const int lim = t >= 0 ? (tb + TK <= whole_lim ? TK : m.kvv - tb) : 0;   // rows below lim are real keys
 #pragma unroll
     for (int x = 0; x < LPW; ++x) {
       const int idx = wave * LPW + x;
@@ -271,7 +272,11 @@ fwd_kernel(Params p) {
       for (int i = 0; i < 16; ++i) acc[c][i] *= alpha;
   };
   // Mask of tile t (partial and skipped tiles only).
+  // Tiles below full_end hold only keys every row of this wave may attend
+  // (the causal part's interior): no classification, no mask.
+  const int full_end = full_tiles_below(m, wa, TK);
   auto mask = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    if (t < full_end) return;
     const int k0 = t * TK;
     const int state = tile_state(m, k0, TK, wa, wb);
     if (state != TILE_FULL) {

@@ -174,6 +174,8 @@ MANY = [
     ("full_kv_valid", FULL, 300, 333, 0, (333, 300, 77, 1)),
     ("ttt_t2", TTT, 300, 900, 0, (300, 250, 1, 299)),
     ("causal_shift5", CAUSAL, 300, 300, 5, None),
+    # short TTT steps: a ragged last key tile reaching past Skv
+    ("ttt_short", TTT, 40, 120, 0, (40, 33, 1, 40)),
 ]
 
 
