@@ -181,11 +181,12 @@ def main():
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
     ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(qg, kg)), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(1, fa.fa_fwd_workspace_bytes(qg, kg)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     kw = dict(mask_kind=w.kind, causal_shift=w.shift, kv_valid=kvv, scale=w.scale, stream=stream)
 
     def fwd():
-        fa.fa_fwd(qg, kg, vg, out=o, lse=lse, **kw)
+        fa.fa_fwd(qg, kg, vg, out=o, lse=lse, workspace=fws, **kw)
 
     def bwd(marks=None):
         # fa_bwd's three stages, in fa_bwd's order, with an optional event after each
@@ -226,7 +227,7 @@ def main():
     value = tf(f_fwd + f_bwd, ms_step)
     peak_mem = torch.cuda.max_memory_allocated(dev)
     # inputs + outputs + workspace resident during the step
-    resident = sum(t.numel() * t.element_size() for t in (qg, kg, vg, dog, o, lse, dq, dk, dv, ws))
+    resident = sum(t.numel() * t.element_size() for t in (qg, kg, vg, dog, o, lse, dq, dk, dv, ws, fws))
 
     kf = kernel_flops(w)
     k_avg = {"fwd": fwd_avg, **{n: float(np.mean(v)) for n, v in stage_ms.items()}}

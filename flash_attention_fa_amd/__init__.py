@@ -5,6 +5,7 @@ computation runs in the library's HIP kernels; PyTorch only provides device
 memory and the current stream.  The functions mirror the C entry points:
 
     fa_fwd(q, k, v, ...)                     -> (o, lse)
+    fa_fwd_workspace_bytes(q, k, ...)        -> int
     fa_bwd(q, k, v, o, lse, dout, ...)       -> (dq, dk, dv)
     fa_bwd_stage(stage, q, k, v, ..., dq, dk, dv, workspace)   (one stage of fa_bwd)
     fa_bwd_workspace_bytes(q, k, ...)        -> int
@@ -30,8 +31,8 @@ from ._lib import (FAError, FA_BF16, FA_F32, FA_MASK_FULL, FA_MASK_CAUSAL,  # no
 
 FULL, CAUSAL, TTT = FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_TTT
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes", "fa_last_error",
-           "FA_BWD_DELTA", "FA_BWD_DKDV", "FA_BWD_DQ",
+__all__ = ["fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes",
+           "fa_last_error", "FA_BWD_DELTA", "FA_BWD_DKDV", "FA_BWD_DQ",
            "attention", "FAError", "FULL", "CAUSAL", "TTT"]
 
 
@@ -74,17 +75,31 @@ def _shape(q, k):
     return int(B), int(Hq), int(Hkv), int(Sq), int(Skv), int(D)
 
 
+def _fwd_shape_args(q, k):
+    B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
+    a = _lib.fa_fwd_args()
+    a.dtype = _dtype_code(q)
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
+    return a
+
+
+def fa_fwd_workspace_bytes(q, k):
+    """Scratch bytes fa_fwd needs for these shapes (bf16: a transposed V, linear in Skv)."""
+    return int(_lib.lib().fa_fwd_workspace_bytes(_fwd_shape_args(q, k)))
+
+
 def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None,
-           out=None, lse=None, stream=None):
-    """Forward attention.  Returns (O [B,Hq,Sq,D] in q's dtype, LSE [B,Hq,Sq] fp32)."""
+           out=None, lse=None, workspace=None, stream=None):
+    """Forward attention.  Returns (O [B,Hq,Sq,D] in q's dtype, LSE [B,Hq,Sq] fp32).
+
+    ``workspace`` (uint8 device tensor of at least ``fa_fwd_workspace_bytes``
+    bytes) is allocated when not given."""
     B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    a = _lib.fa_fwd_args()
-    a.dtype = _dtype_code(q)
-    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
+    a = _fwd_shape_args(q, k)
     a.scale = 0.0 if scale is None else float(scale)
     a.q, a.k, a.v, a.o = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
     a.lse = lse.data_ptr()
@@ -92,7 +107,11 @@ def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None
     for t in (k, v, out):
         if t.dtype != q.dtype:
             raise FAError(_lib.FA_ERR_INVALID_ARG, "q, k, v and out must share one dtype")
-    _lib.check(_lib.lib().fa_fwd(a, _stream(q, stream)))
+    need = int(_lib.lib().fa_fwd_workspace_bytes(a))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(_lib.lib().fa_fwd(a, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 _stream(q, stream)))
     return out, lse
 
 

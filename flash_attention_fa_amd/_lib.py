@@ -24,7 +24,8 @@ FA_MASK_FULL = 0
 FA_MASK_CAUSAL = 1
 FA_MASK_TTT = 2
 
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes", "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes",
+            "fa_last_error")
 
 
 FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2
@@ -78,8 +79,11 @@ def lib():
                 f"{LIB_PATH} is missing: build it with "
                 "`python -m flash_attention_fa_amd.build` (there is no fallback)")
         L = ctypes.CDLL(LIB_PATH)
-        L.fa_fwd.argtypes = [ctypes.POINTER(fa_fwd_args), ctypes.c_void_p]
+        L.fa_fwd.argtypes = [ctypes.POINTER(fa_fwd_args), ctypes.c_void_p,
+                             ctypes.c_size_t, ctypes.c_void_p]
         L.fa_fwd.restype = ctypes.c_int
+        L.fa_fwd_workspace_bytes.argtypes = [ctypes.POINTER(fa_fwd_args)]
+        L.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.fa_bwd.argtypes = [ctypes.POINTER(fa_bwd_args), ctypes.c_void_p,
                              ctypes.c_size_t, ctypes.c_void_p]
         L.fa_bwd.restype = ctypes.c_int

@@ -154,13 +154,41 @@ size_t row_array_bytes(const Shape& s) {
 // Backward workspace: Delta, then LSE * log2(e) (both [B, Hq, Sq] float32).
 size_t delta_bytes(const Shape& s) { return 2 * row_array_bytes(s); }
 
+// Forward workspace (bf16 only): V^T, bfloat16 [B, Hkv, D, vt_keys(s)].
+int64_t vt_keys(const Shape& s) {
+  return ((int64_t)std::max(s.Skv, 0) + fa::kVtTile - 1) / fa::kVtTile * fa::kVtTile;
+}
+size_t fwd_ws_bytes(const Shape& s) {
+  if (s.dtype != FA_BF16) return 0;
+  size_t n = (size_t)std::max(s.B, 0) * (size_t)std::max(s.Hkv, 0) * (size_t)std::max(s.D, 0) *
+             (size_t)vt_keys(s) * 2;
+  return (n + 255) / 256 * 256;
+}
+
+// A caller workspace of `need` bytes: present, large enough, 256-byte aligned.
+fa_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return FA_OK;
+  if (ws == nullptr) return fail(FA_ERR_INVALID_ARG, "workspace: NULL pointer (%zu bytes needed)", need);
+  if (ws_bytes < need)
+    return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(FA_ERR_ALIGNMENT, "workspace pointer %p is not 256-byte aligned", ws);
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* fa_last_error(void) { return g_error.c_str(); }
 
-fa_status fa_fwd(const fa_fwd_args* a, hipStream_t stream) {
+size_t fa_fwd_workspace_bytes(const fa_fwd_args* a) {
+  if (!a) return 0;
+  Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
+  return fwd_ws_bytes(s);
+}
+
+fa_status fa_fwd(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!a) return fail(FA_ERR_INVALID_ARG, "fa_fwd: args is NULL");
   Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
   fa_status st = check_shape(s, a->mask);
@@ -179,11 +207,19 @@ fa_status fa_fwd(const fa_fwd_args* a, hipStream_t stream) {
         rv = span(a->v, s.B, s.Hkv, s.Skv, s.D, eb), ro = span(a->o, s.B, s.Hq, s.Sq, s.D, eb);
   Range rl{reinterpret_cast<uintptr_t>(a->lse),
            reinterpret_cast<uintptr_t>(a->lse) + (size_t)s.B * s.Hq * s.Sq * 4, !rows};
+  if (s.dtype == FA_BF16 && vt_keys(s) >= (int64_t(1) << 24))
+    return fail(FA_ERR_UNSUPPORTED, "Skv=%d is too large (limit 2^24 - 64)", s.Skv);
+  const size_t need = fwd_ws_bytes(s);
+  if ((st = check_ws(ws, ws_bytes, need))) return st;
+  Range rw{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + need, need == 0};
   for (const Range* in : {&rq, &rk, &rv}) {
     if (overlap(ro, *in)) return fail(FA_ERR_ALIAS, "o overlaps an input tensor");
     if (overlap(rl, *in)) return fail(FA_ERR_ALIAS, "lse overlaps an input tensor");
+    if (overlap(rw, *in)) return fail(FA_ERR_ALIAS, "workspace overlaps an input tensor");
   }
   if (overlap(ro, rl)) return fail(FA_ERR_ALIAS, "o overlaps lse");
+  if (overlap(rw, ro)) return fail(FA_ERR_ALIAS, "workspace overlaps o");
+  if (overlap(rw, rl)) return fail(FA_ERR_ALIAS, "workspace overlaps lse");
   if (a->mask.kv_valid && reinterpret_cast<uintptr_t>(a->mask.kv_valid) % 4 != 0)
     return fail(FA_ERR_ALIGNMENT, "kv_valid: pointer is not 4-byte aligned");
   if (!rows) return FA_OK;  // nothing to compute
@@ -193,6 +229,8 @@ fa_status fa_fwd(const fa_fwd_args* a, hipStream_t stream) {
   fill_common(p, s, a->scale, a->mask);
   p.q = tensor(a->q); p.k = tensor(a->k); p.v = tensor(a->v); p.o = tensor(a->o);
   p.lse = a->lse;
+  p.vt = ws;
+  p.vt_ss = vt_keys(s);
   hipError_t e = s.dtype == FA_BF16 ? fa::launch_fwd_bf16(p, stream) : fa::launch_fwd_f32(p, stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd launch failed: %s", hipGetErrorString(e));
   return FA_OK;
@@ -225,13 +263,7 @@ static fa_status bwd_run(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStr
   if (rows && reinterpret_cast<uintptr_t>(a->lse) % 4 != 0)
     return fail(FA_ERR_ALIGNMENT, "lse: pointer is not 4-byte aligned");
   const size_t need = delta_bytes(s);
-  if (need > 0) {
-    if (ws == nullptr) return fail(FA_ERR_INVALID_ARG, "workspace: NULL pointer (%zu bytes needed)", need);
-    if (ws_bytes < need)
-      return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
-    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
-      return fail(FA_ERR_ALIGNMENT, "workspace pointer %p is not 256-byte aligned", ws);
-  }
+  if ((st = check_ws(ws, ws_bytes, need))) return st;
   if (a->mask.kv_valid && reinterpret_cast<uintptr_t>(a->mask.kv_valid) % 4 != 0)
     return fail(FA_ERR_ALIGNMENT, "kv_valid: pointer is not 4-byte aligned");
 

@@ -14,8 +14,10 @@
 // LDS in tiles of 64.  Scores are computed transposed, S^T = K Q^T, so each
 // lane owns one query column and 32 keys of it: the softmax scale, running
 // max and normaliser are one scalar per lane.  O^T = V^T P^T takes P straight
-// from the score registers and V^T from transposing LDS reads of the
-// row-major V tile.
+// from the score registers and V^T from a transposed copy of V that a small
+// pre-pass writes into the caller's workspace (vt_kernel): 16-byte LDS reads
+// serve it, where the row-major V tile would need transposing reads that
+// move half as many bytes per instruction at about half the rate.
 //
 // Vector-ALU budget.  At D = 128 a wave's 32 MFMAs per tile take about as long
 // as a few hundred vector instructions, so the exponentials and their
@@ -28,30 +30,82 @@
 // recomputed.  LDS addresses are lane constants plus immediates: the loop is
 // unrolled over the four ring buffers.
 //
-// Pipeline.  Four LDS buffers hold tiles i .. i+3.  K and V rows are copied
+// Pipeline.  Four LDS buffers hold tiles i .. i+3.  K and V^T rows are copied
 // HBM -> LDS asynchronously (no registers, no vector instructions) three tiles
 // ahead; iteration i issues the QK^T products of tile i+1, then the
 // exponentials of tile i (independent of those products, so the matrix cores
 // and the vector ALUs work at once), then the PV products of tile i; the mask
 // of tile i+1 (partial tiles only) closes the iteration.  One barrier per
 // tile, which waits only for the copies of tile i+2.
+#include <algorithm>
+
 #include "fa_device.h"
 
 namespace fa {
 namespace {
 
 constexpr int TK = 64;    // keys per LDS tile
+static_assert(TK == kVtTile, "the V^T workspace is laid out in forward key tiles");
 constexpr int NBUF = 4;   // tiles in flight in LDS
 // A tile's per-row sum of P above this bound triggers the running-max refresh
 // (every P of the row is below it, so nothing overflows before the check).
 constexpr float kSumLimit = 4096.0f;
 
+// LDS: the NBUF K tiles (64 swizzled rows of D), then the NBUF V^T tiles (D
+// swizzled rows of 64 keys), so every operand address of a ring buffer is a
+// lane constant plus an immediate below 64 KB.
 template <int D>
 struct FwdLds {
-  static constexpr int TILE_BYTES = TK * D * 2;          // one K or V tile, swizzled rows
-  static constexpr int BUF = 2 * TILE_BYTES;             // K then V
-  static constexpr int BYTES = NBUF * BUF;
+  static constexpr int TILE_BYTES = TK * D * 2;          // one K or V^T tile
+  static constexpr int VT_BASE = NBUF * TILE_BYTES;
+  static constexpr int BYTES = 2 * NBUF * TILE_BYTES;
 };
+
+// V^T row d of a key tile is 64 keys (128 bytes, eight 16-byte chunks);
+// chunk c of row d sits at slot c ^ vt_swz(d), so the 16 rows one 16-lane
+// group of a 16-byte read touches cover all 64 banks.
+__device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 7; }
+
+// Stored position of key tile offset j in a V^T row: within each group of 16
+// keys, bits 2 and 3 of the offset swap places.  The PV product's B operand
+// is P^T straight from the transposed score registers, where lane half hh
+// holds keys 4hh..4hh+3 and 8+4hh..8+4hh+3 of each 16-key step in its eight
+// k slots; with this order those eight keys are one 16-byte run of V^T.
+__host__ __device__ constexpr int vt_pos(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
+
+// V^T pre-pass: vt[b, hk, d, tile*64 + vt_pos(j)] = V[b, hk, tile*64 + j, d]
+// for real keys and 0 for every other position of the padded key range
+// (past Skv, or not valid under the mask), so the forward's copies need no
+// per-row selection and masked keys add 0 * 0.  A block converts one
+// (b, hk, tile) at a time, striding over all of them.
+template <int D>
+__global__ void __launch_bounds__(256) vt_kernel(Params p, int64_t nblk) {
+  __shared__ bf16 tile[TK][D + 8];
+  const int ntile = (int)(p.vt_ss / TK);
+  constexpr int CPR = D / 8;
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int t = (int)(blk % ntile), bh = (int)(blk / ntile);
+    const int b = bh / p.Hkv, hk = bh % p.Hkv;
+    const MaskB m = resolve_mask(p, b);
+    const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
+    __syncthreads();   // the previous tile's reads of `tile` are done
+    for (int i = threadIdx.x; i < TK * CPR; i += 256) {
+      const int r = i / CPR, c = i % CPR, j = t * TK + r;
+      bf16x8 x = {};
+      if (key_valid(m, j)) x = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)j * p.v.ss + 8 * c);
+      *reinterpret_cast<bf16x8*>(&tile[r][8 * c]) = x;
+    }
+    __syncthreads();
+    bf16* Vt = static_cast<bf16*>(p.vt) + (int64_t)bh * D * p.vt_ss + (int64_t)t * TK;
+    for (int i = threadIdx.x; i < D * (TK / 8); i += 256) {
+      const int d = i / (TK / 8), c = i % (TK / 8);
+      bf16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = tile[vt_pos(8 * c + e)][d];
+      *reinterpret_cast<bf16x8*>(Vt + (int64_t)d * p.vt_ss + 8 * c) = y;
+    }
+  }
+}
 
 template <int K>
 struct Buf {
@@ -70,6 +124,7 @@ fwd_kernel(Params p) {
   constexpr int NDB = D >= 32 ? D / 32 : 1;  // 32-wide d blocks of O^T
   constexpr int NJ = D / 16;                 // 16-wide d steps of S^T
   constexpr int ROW16 = 16 * 2 * D;          // bytes of 16 tile rows
+  static_assert(NINS == D / 8, "a V^T tile takes as many copy instructions as a K tile");
   using L = FwdLds<D>;
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -89,7 +144,7 @@ fwd_kernel(Params p) {
 
   const bf16* Qg = static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
   const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
-  const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
+  const bf16* VTg = static_cast<const bf16*>(p.vt) + (int64_t)(b * p.Hkv + hk) * D * p.vt_ss;
 
   // Q^T as the B operand: lane (q = l32, half hh) holds Q[q][16j + 8hh .. +8].
   bf16x8 qreg[NJ];
@@ -104,22 +159,29 @@ fwd_kernel(Params p) {
   for (int c = 0; c < NDB; ++c) acc[c] = f32x16{};
   float mrun = kMaxInit, lsum = 0.f;
 
-  // Asynchronous copy of key tile t into buffer k: this wave's share of the
-  // 2 * NINS instructions (K rows first, then V rows).  Rows that are not
-  // real keys (and every row when t < 0) are fetched from key 0 instead: a
-  // real row, so the values are finite, and the mask zeroes their weights.
-  // (Only reached when the tile has a real key, so key 0 is real.)
+  // Asynchronous copy of key tile t into ring buffer k: this wave's share of
+  // the 2 * NINS instructions (K rows first, then V^T rows; which kind a
+  // wave copies is uniform).  K rows that are not real keys (and every row
+  // when t < 0) are fetched from key 0 instead: a real row, so the scores
+  // stay finite, and the mask drops them.  (Only reached when the walk has
+  // a tile, so key 0 is real.)  V^T rows need no selection: the pre-pass
+  // zeroed every position that is not a real key, and t < 0 reads tile 0.
   const int crow = lane / CPR, cslot = lane % CPR;
   int roff[LPW], zoff[LPW];
 #pragma unroll
   for (int x = 0; x < LPW; ++x) {
     const int idx = wave * LPW + x;
-    const int ii = idx % NINS;
-    const int row = ii * RPI + crow;
-    const int gch = cslot ^ swz<D>(row);
-    const int64_t ss = idx / NINS == 0 ? p.k.ss : p.v.ss;
-    roff[x] = (int)(row * ss) + 8 * gch;
-    zoff[x] = 8 * gch;
+    if (idx < NINS) {
+      const int row = idx * RPI + crow;
+      const int gch = cslot ^ swz<D>(row);
+      roff[x] = (int)(row * p.k.ss) + 8 * gch;
+      zoff[x] = 8 * gch;
+    } else {
+      const int row = (idx - NINS) * (64 / (TK / 8)) + lane / (TK / 8);   // d row of V^T
+      const int slot = lane % (TK / 8);
+      roff[x] = (int)(row * p.vt_ss) + 8 * (slot ^ vt_swz(row));
+      zoff[x] = roff[x];
+    }
   }
   const bool ttt = m.kind == MASK_TTT;
   const int whole_lim = ttt ? 0 : m.kvv;      // tiles ending at or below it hold only real keys
@@ -130,13 +192,15 @@ fwd_kernel(Params p) {
     for (int x = 0; x < LPW; ++x) {
       const int idx = wave * LPW + x;
       if (ALL_COPY || idx < 2 * NINS) {
-        const int tensor = idx / NINS, ii = idx % NINS;
-        const int row = ii * RPI + crow;
-        const bool ok = ttt ? (t >= 0 && key_valid(m, tb + row)) : row < lim;
-        const bf16* base = tensor == 0 ? Kg : Vg;
-        const int64_t ss = tensor == 0 ? p.k.ss : p.v.ss;
-        const bf16* g = ok ? base + (int64_t)tb * ss + roff[x] : base + zoff[x];
-        lds_dma16(g, smem + k * L::BUF + tensor * L::TILE_BYTES + ii * 1024);
+        if (idx < NINS) {
+          const int row = idx * RPI + crow;
+          const bool ok = ttt ? (t >= 0 && key_valid(m, tb + row)) : row < lim;
+          const bf16* g = ok ? Kg + (int64_t)tb * p.k.ss + roff[x] : Kg + zoff[x];
+          lds_dma16(g, smem + k * L::TILE_BYTES + idx * 1024);
+        } else {
+          lds_dma16(VTg + (t >= 0 ? tb : 0) + roff[x],
+                    smem + L::VT_BASE + k * L::TILE_BYTES + (idx - NINS) * 1024);
+        }
       }
     }
   };
@@ -151,19 +215,15 @@ fwd_kernel(Params p) {
   int koff[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) koff[j] = swz_off<D>(l32, 16 * j + 8 * hh);
-  // Transposing reads of V: lane r of each 16-lane group points at row
-  // kbase + r/4, column dcol + 4*(r%4); lanes whose d column does not exist
-  // (D = 16) read a real column and use zeros.
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const bool d_lane_ok = D >= 32 || ((lane >> 4) & 1) == 0;
-  int voff[2][NDB];
+  // V^T operand of 16-key step st: lane (l32, hh) reads row 32c + l32 of
+  // the V^T tile, stored keys 16st + 8hh .. +8 (one 16-byte chunk).  Lanes
+  // whose d row does not exist (D = 16) read a real row and use zeros.
+  const bool d_lane_ok = D >= 32 || l32 < 16;
+  const int vrow = D >= 32 ? l32 : (l32 & 15);
+  int vto[TK / 16];
 #pragma unroll
-  for (int c = 0; c < NDB; ++c) {
-    const int dcol = D >= 32 ? 32 * c + tr_col : (tr_col & 15);
-    voff[0][c] = swz_off<D>(4 * hh + tr_row, dcol);
-    voff[1][c] = swz_off<D>(4 * hh + tr_row + 8, dcol);
-  }
+  for (int st = 0; st < TK / 16; ++st)
+    vto[st] = L::VT_BASE + vrow * (2 * TK) + 16 * ((2 * st + hh) ^ vt_swz(vrow));
 
   // S^T of the tile in buffer k: 2 key blocks of 32.
   auto qk = [&](auto kc, f32x16 (&s)[2]) __attribute__((always_inline)) {
@@ -174,7 +234,7 @@ fwd_kernel(Params p) {
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *FA_LDS(const bf16x8, smem + k * L::BUF + 2 * kb * ROW16 + koff[j]);
+        const bf16x8 a = *FA_LDS(const bf16x8, smem + k * L::TILE_BYTES + 2 * kb * ROW16 + koff[j]);
         s[kb] = mfma32(a, qreg[j], s[kb]);
       }
   };
@@ -184,11 +244,9 @@ fwd_kernel(Params p) {
     constexpr int k = decltype(kc)::value;
     constexpr int NOP = 4 * NDB;   // (kb, st, c) products
     constexpr int PF = 3;
-    const unsigned char* Vt = smem + k * L::BUF + L::TILE_BYTES;
     auto vread = [&](int n) __attribute__((always_inline)) {
-      const int c = n % NDB, rows = (n / NDB) * ROW16;
-      bf16x8 a = cat8(lds_read_tr4(reinterpret_cast<const bf16*>(Vt + rows + voff[0][c])),
-                      lds_read_tr4(reinterpret_cast<const bf16*>(Vt + rows + voff[1][c])));
+      const int c = n % NDB, st = n / NDB;
+      const bf16x8 a = *FA_LDS(const bf16x8, smem + k * L::TILE_BYTES + c * 32 * (2 * TK) + vto[st]);
       return d_lane_ok ? a : bf16x8{};
     };
     bf16x8 va[PF + 1];
@@ -229,7 +287,7 @@ fwd_kernel(Params p) {
     // K operands are read PF products ahead of their use.
     constexpr int PF = 3;
     auto kread = [&](int n) __attribute__((always_inline)) {
-      return *FA_LDS(const bf16x8, smem + k * L::BUF + 2 * (n & 1) * ROW16 + koff[n >> 1]);
+      return *FA_LDS(const bf16x8, smem + k * L::TILE_BYTES + 2 * (n & 1) * ROW16 + koff[n >> 1]);
     };
     bf16x8 ka[PF + 1];
 #pragma unroll
@@ -373,6 +431,13 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   const int nq = (p.Sq + TQ - 1) / TQ;
   const int64_t nblk = (int64_t)p.B * p.Hq * nq;
   if (nblk == 0) return hipSuccess;
+  const int64_t nvt = (int64_t)p.B * p.Hkv * (p.vt_ss / TK);
+  if (nvt > 0) {
+    const unsigned grid = (unsigned)std::min<int64_t>(nvt, 1 << 20);
+    hipLaunchKernelGGL(vt_kernel<D>, dim3(grid), dim3(256), 0, stream, p, nvt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int lds = FwdLds<D>::BYTES;
   auto k = fwd_kernel<D, NW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),

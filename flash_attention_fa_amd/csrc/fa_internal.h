@@ -17,6 +17,9 @@ struct Mask {
   const int* kv_valid; // device [B] or nullptr
 };
 
+// Keys per V^T tile of the forward workspace (the forward's key tile).
+constexpr int kVtTile = 64;
+
 // Everything a kernel needs.  Built once per call by the dispatcher.
 struct Params {
   int B, Hq, Hkv, G, Sq, Skv, D;
@@ -27,6 +30,8 @@ struct Params {
   Tensor dout;         // backward: dO
   Tensor dq, dk, dv;   // backward outputs
   float* lse;          // forward output
+  void* vt;            // forward workspace (bf16): V^T [B, Hkv, D, vt_ss]
+  int64_t vt_ss;       // keys per V^T row: Skv rounded up to a whole key tile
   const float* lse_in; // backward input
   float* delta;        // backward workspace: Delta [B, Hq, Sq]
   float* lse2;         // backward workspace: LSE * log2(e) [B, Hq, Sq]

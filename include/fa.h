@@ -39,8 +39,8 @@
  * storage, float32 accumulation; O, dQ, dK, dV rounded to nearest even) or
  * FA_F32 (float32 throughout).
  *
- * Ownership.  The caller owns every buffer, including the backward
- * workspace.  The library allocates no device memory, keeps no state between
+ * Ownership.  The caller owns every buffer, including the forward and
+ * backward workspaces.  The library allocates no device memory, keeps no state between
  * calls, launches on the caller's stream and never synchronises the host.
  *
  * Errors.  All arguments are validated before anything is launched; on a
@@ -116,8 +116,19 @@ typedef struct {
   fa_mask_desc mask;         /* must equal the forward's */
 } fa_bwd_args;
 
-/* Forward: writes O and LSE.  Asynchronous on `stream` (0 = null stream). */
-fa_status fa_fwd(const fa_fwd_args* args, hipStream_t stream);
+/* Bytes of device scratch fa_fwd needs for these arguments.  FA_BF16: one
+ * transposed copy of V, bfloat16 [B, Hkv, D, Skv rounded up to 64], rounded
+ * up to 256 bytes (the PV product, O^T = V^T P^T of CS336 "Flash Attention
+ * (Triton)", contracts over keys; stored key-minor, V^T feeds the matrix
+ * cores with plain 16-byte reads).  FA_F32: 0.  Linear in Skv, never S x S.
+ * Returns 0 when args is NULL. */
+size_t fa_fwd_workspace_bytes(const fa_fwd_args* args);
+
+/* Forward: writes O and LSE.  `ws` is caller-owned device memory of at least
+ * fa_fwd_workspace_bytes(args) bytes, 256-byte aligned (may be NULL when that
+ * is 0); its contents on return are unspecified.  Asynchronous on `stream`
+ * (0 = null stream). */
+fa_status fa_fwd(const fa_fwd_args* args, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Bytes of device scratch fa_bwd needs for these arguments: two float32
  * [B, Hq, Sq] arrays (Delta, and LSE in log2 units), each rounded up to 256

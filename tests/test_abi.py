@@ -72,8 +72,8 @@ def bwd_args(B=1, Hq=4, Hkv=2, Sq=64, Skv=64, D=64, dtype=_lib.FA_BF16, kind=1):
 WS = BASE + 9 * GAP
 
 
-def fwd(a):
-    st = _lib.lib().fa_fwd(a, None)
+def fwd(a, ws=WS, ws_bytes=1 << 24):
+    st = _lib.lib().fa_fwd(a, ws, ws_bytes, None)
     return st, _lib.last_error()
 
 
@@ -147,8 +147,35 @@ def test_forward_pointer_alignment_alias_and_null():
     a.o.stride_s = 32                         # output rows overlap each other (D = 64)
     st, msg = fwd(a)
     assert st == _lib.FA_ERR_INVALID_ARG and "overlap" in msg
-    st = _lib.lib().fa_fwd(None, None)
+    st = _lib.lib().fa_fwd(None, WS, 1 << 24, None)
     assert st == _lib.FA_ERR_INVALID_ARG
+
+
+def test_forward_workspace():
+    a = fwd_args(B=2, Hkv=2, Skv=100, D=64)
+    need = _lib.lib().fa_fwd_workspace_bytes(a)
+    # V^T: [B, Hkv, D, Skv rounded up to 64] bfloat16, rounded up to 256 bytes
+    assert need == (2 * 2 * 64 * 128 * 2 + 255) // 256 * 256
+    assert _lib.lib().fa_fwd_workspace_bytes(None) == 0
+    assert _lib.lib().fa_fwd_workspace_bytes(fwd_args(dtype=_lib.FA_F32)) == 0
+    a = fwd_args(Skv=64, Sq=64)
+    need = _lib.lib().fa_fwd_workspace_bytes(a)
+    st, msg = fwd(a, ws_bytes=need - 1)
+    assert st == _lib.FA_ERR_INVALID_ARG and "workspace too small" in msg
+    st, msg = fwd(a, ws=None)
+    assert st == _lib.FA_ERR_INVALID_ARG and "workspace" in msg
+    st, msg = fwd(a, ws=WS + 16)
+    assert st == _lib.FA_ERR_ALIGNMENT and "workspace" in msg
+    st, msg = fwd(a, ws=a.v.data)             # workspace on an input
+    assert st == _lib.FA_ERR_ALIAS and "workspace" in msg
+    st, msg = fwd(a, ws=a.o.data)             # workspace on the output
+    assert st == _lib.FA_ERR_ALIAS and "workspace" in msg
+    # fp32 needs none: a NULL workspace is accepted (and fails only for want of a device)
+    st, msg = fwd(fwd_args(dtype=_lib.FA_F32), ws=None, ws_bytes=0)
+    assert st in (_lib.FA_OK, _lib.FA_ERR_HIP), msg
+    # key counts whose V^T rows would not fit 32-bit offsets are refused
+    st, msg = fwd(fwd_args(B=1, Hq=1, Hkv=1, Sq=64, Skv=1 << 24, kind=0), ws_bytes=1 << 40)
+    assert st == _lib.FA_ERR_UNSUPPORTED and "Skv" in msg
 
 
 def test_forward_empty_is_a_noop():
@@ -187,6 +214,9 @@ def test_workspace_is_linear_in_sequence_length():
     sizes = [_lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=s, Skv=s, D=128))
              for s in (16384, 32768)]
     assert sizes[1] == 2 * sizes[0] == 2 * 2 * 32 * 16384 * 4
+    sizes = [_lib.lib().fa_fwd_workspace_bytes(fwd_args(B=1, Hq=32, Hkv=4, Sq=s, Skv=s, D=128))
+             for s in (16384, 32768)]
+    assert sizes[1] == 2 * sizes[0] == 2 * 4 * 128 * 16384 * 2
 
 
 def test_bwd_stage_rejects_unknown_stage():
