@@ -877,14 +877,12 @@ dkdv_dma_kernel(Params p) {
                                     : static_cast<const bf16*>(p.q.ptr) + b * p.q.sb;
   const int64_t ssh = stage_g ? p.dout.sh : p.q.sh;
   const int64_t sss = stage_g ? p.dout.ss : p.q.ss;
-  // this lane's element offsets inside a tile (row * stride + swizzled chunk)
-  int64_t soff[QLPW];
-  int srow[QLPW];
+  // this lane's swizzled chunk (element offset) in each of its tile rows
+  int schunk[QLPW];
 #pragma unroll
   for (int x = 0; x < QLPW; ++x) {
     const int ii = (wave % (NW / 2)) * QLPW + x;
-    srow[x] = ii * RPI + crow;
-    soff[x] = (int64_t)srow[x] * sss + 8 * (cslot ^ swz<D>(srow[x]));
+    schunk[x] = 8 * (cslot ^ swz<D>(ii * RPI + crow));
   }
   struct StepPos {
     int hs, q0;   // head slot in the group, first query row of the tile
@@ -899,9 +897,11 @@ dkdv_dma_kernel(Params p) {
 #pragma unroll
     for (int x = 0; x < QLPW; ++x) {
       const int ii = (wave % (NW / 2)) * QLPW + x;
-      const bool ok = whole || sp.q0 + srow[x] < p.Sq;
-      // rows past Sq are copied from the tile's first row (real, finite)
-      lds_dma16(Sg + (ok ? soff[x] : soff[x] - (int64_t)srow[x] * sss), dst + ii * 1024);
+      const int row = ii * RPI + crow;
+      const bool ok = whole || sp.q0 + row < p.Sq;
+      // rows past Sq are copied from the tile's first row (real, finite);
+      // row * stride < 2^30 (strides are below 2^24 elements)
+      lds_dma16(Sg + ((ok ? row * (int)sss : 0) + schunk[x]), dst + ii * 1024);
     }
   };
   float lrow = 0.f, drow = 0.f;
@@ -945,7 +945,11 @@ dkdv_dma_kernel(Params p) {
     toff[1][c] = swz_off<D>(4 * hh + tr_row + 8, 32 * c + tr_col);
   }
   const int qrow0 = 32 * qhalf * 2 * D;      // byte offset of this wave's 32 query rows
-  const unsigned char* Kw = Ks + kblk * 32 * 2 * D;
+  // This wave's 32 K rows stay in registers (the B operand of S every
+  // step); its V rows (dP's) are read from LDS.
+  bf16x8 kreg[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) kreg[j] = *FA_LDS(const bf16x8, Ks + kblk * 32 * 2 * D + roff[j]);
   const unsigned char* Vw = Vs + kblk * 32 * 2 * D;
 
   f32x16 dka[NDB], dva[NDB];
@@ -982,10 +986,8 @@ dkdv_dma_kernel(Params p) {
       for (int j = 0; j < NJ; ++j) {
         const bf16x8 aq = *FA_LDS(const bf16x8, Qt + qrow0 + roff[j]);
         const bf16x8 ag = *FA_LDS(const bf16x8, Gt + qrow0 + roff[j]);
-        const bf16x8 bk = *FA_LDS(const bf16x8, Kw + roff[j]);
-        const bf16x8 bv = *FA_LDS(const bf16x8, Vw + roff[j]);
-        s = mfma32(aq, bk, s);
-        dp = mfma32(ag, bv, dp);
+        s = mfma32(aq, kreg[j], s);
+        dp = mfma32(ag, *FA_LDS(const bf16x8, Vw + roff[j]), dp);
       }
       // Per-register query rows: q = qa + 8*(i/4) + 4*hh + i%4.
       if (state == TILE_PART) {
