@@ -297,7 +297,9 @@ struct DqDma {
   static constexpr int BYTES = DQ_NBUF * BUF;
 };
 
-template <int D, int NW>
+// TTT: instantiated for the EAGLE3 mask; the other instance knows the kind
+// is FULL or CAUSAL, which drops the TTT arms of the tile walk and the mask.
+template <int D, int NW, bool TTT>
 __global__ void __launch_bounds__(NW * 64, 2)
 dq_dma_kernel(Params p) {
   using L = DqDma<D>;
@@ -323,7 +325,8 @@ dq_dma_kernel(Params p) {
   map_block(blockIdx.x, p.B * p.Hq, nq, col, rank);
   const int b = col / p.Hq, h = col % p.Hq, hk = h / p.G;
   const int qtile = p.mask.kind == MASK_FULL ? rank : nq - 1 - rank;
-  const MaskB m = resolve_mask(p, b);
+  MaskB m = resolve_mask(p, b);
+  m.kind = TTT ? MASK_TTT : (m.kind == MASK_FULL ? MASK_FULL : MASK_CAUSAL);
   const int qa = qtile * TQ, qb = min(p.Sq, qa + TQ);
   const int wa = qa + wave * 32, wb = min(p.Sq, wa + 32);
   const int qi = wa + l32;
@@ -1131,7 +1134,9 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     // 8-wave workgroups when there are enough to fill the chip twice over
     const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
     if constexpr (D == 128) {
-      auto k = wg8 >= 512 ? dq_dma_kernel<D, 8> : dq_dma_kernel<D, 4>;
+      const bool ttt = p.mask.kind == MASK_TTT;
+      auto k = wg8 >= 512 ? (ttt ? dq_dma_kernel<D, 8, true> : dq_dma_kernel<D, 8, false>)
+                          : (ttt ? dq_dma_kernel<D, 4, true> : dq_dma_kernel<D, 4, false>);
       const int nw = wg8 >= 512 ? 8 : 4;
       const int64_t nblk = (int64_t)p.B * p.Hq * ((p.Sq + nw * 32 - 1) / (nw * 32));
       if ((e = set_lds(k, DqDma<D>::BYTES)) != hipSuccess) return e;

@@ -112,7 +112,9 @@ struct Buf {
   static constexpr int value = K;
 };
 
-template <int D, int NW>
+// TTT: instantiated for the EAGLE3 mask; the other instance may assume
+// FULL or CAUSAL, which drops the TTT arms of the tile walk and the mask.
+template <int D, int NW, bool TTT>
 __global__ void __launch_bounds__(NW * 64, 2)
 fwd_kernel(Params p) {
   constexpr int TQ = NW * 32;
@@ -136,7 +138,9 @@ fwd_kernel(Params p) {
   map_block(blockIdx.x, p.B * p.Hq, nq, col, rank);
   const int b = col / p.Hq, h = col % p.Hq, hk = h / p.G;
   const int qtile = p.mask.kind == MASK_FULL ? rank : nq - 1 - rank;
-  const MaskB m = resolve_mask(p, b);
+  MaskB m = resolve_mask(p, b);
+  // the instance's kind, visibly to the compiler (FULL or CAUSAL, or TTT)
+  m.kind = TTT ? MASK_TTT : (m.kind == MASK_FULL ? MASK_FULL : MASK_CAUSAL);
 
   const int qa = qtile * TQ, qb = min(p.Sq, qa + TQ);
   const int wa = qa + wave * 32, wb = min(p.Sq, wa + 32);
@@ -439,7 +443,7 @@ hipError_t launch(const Params& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const int lds = FwdLds<D>::BYTES;
-  auto k = fwd_kernel<D, NW>;
+  auto k = p.mask.kind == MASK_TTT ? fwd_kernel<D, NW, true> : fwd_kernel<D, NW, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
