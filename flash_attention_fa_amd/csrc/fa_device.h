@@ -257,27 +257,6 @@ __device__ __forceinline__ bool allowed(const MaskB& m, int i, int j) {
   return causal | ((j >= m.L) & (j < m.Skv) & (jm == i) & (jm < m.kvv));
 }
 
-// Instruction-class masks of the scheduler's group barriers, and a group
-// barrier: the next `n` instructions of class `mask` in the current
-// straight-line block are placed here, in order.
-enum : int { SCHED_VALU = 0x002, SCHED_SALU = 0x004, SCHED_MFMA = 0x008, SCHED_VMEM_READ = 0x020,
-             SCHED_DS_READ = 0x100, SCHED_DS_WRITE = 0x200, SCHED_TRANS = 0x400 };
-#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
-
-// Places an accumulator tile in the accumulation registers at this point.
-// A value that the vector ALUs rescale on a rare path then re-enters the
-// product loop in the register class the products keep it in, instead of
-// the loop copying it between classes on every iteration.
-__device__ __forceinline__ void in_agpr(f32x16& x) {
-  asm volatile("" : "+a"(x));
-}
-
-// Makes `x` count as used here, so its computation stays in this block.
-template <typename T>
-__device__ __forceinline__ void keep(const T& x) {
-  asm volatile("" ::"v"(x));
-}
-
 // The wave index as a provably uniform (scalar) value, so everything derived
 // from it (tile ranges, tile states, loop bounds) stays in scalar registers.
 __device__ __forceinline__ int wave_id() {
