@@ -11,7 +11,7 @@ Prints one JSON line: the metric, the per-step time, fwd / bwd / fwd+bwd
 TFLOP/s and their fraction of the 2516.6 TFLOP/s dense bf16 peak, the time of
 each kernel (the backward runs as its three stages, Delta, dK/dV and dQ, with
 HIP events between them on the launch stream), the roofline of the dominant
-kernel (dK/dV), the peak device memory, and the fp64 oracle timed on a
+kernel (the dK/dV stage), the peak device memory, and the fp64 oracle timed on a
 bounded sample of the same workload on the host CPU.
 
 Algorithmic work per allowed pair, by kernel: forward 4*D (S = QK^T, PV);
@@ -19,9 +19,13 @@ dK/dV 8*D (S, dP = dO V^T, dV += P^T dO, dK += dS^T Q); dQ 2*D (dQ += dS K;
 its recomputation of S and dP is overhead and is not counted); Delta reads
 O and dO (4*D bytes per query row in bf16) and does no contraction.
 
-The roofline's ``traffic`` (HBM bytes per launch of the dK/dV kernel) comes
-from a committed rocprofv3 counter summary (FETCH_SIZE, WRITE_SIZE) whose
-recorded source hash must match the current kernel sources, else it is null.
+The dK/dV stage is two launches: dkdv_split_kernel (the products; each key
+block's query steps split between two workgroups that write float32 partial
+sums) and dkdv_reduce_kernel (adds the two halves, about 1 % of the stage's
+time); the roofline times them together, as one unit of work.  Its
+``traffic`` (HBM bytes per stage) comes from a committed rocprofv3 counter
+summary (FETCH_SIZE, WRITE_SIZE of both kernels) whose recorded source hash
+must match the current kernel sources, else it is null.
 
     python bench.py --copy-calibration
 
@@ -263,12 +267,12 @@ def main():
                 "pct_of_peak": round(100 * tf(f_bwd, bwd_med) / PEAK_BF16_TFLOPS, 2)},
         "gflop_per_step": round((f_fwd + f_bwd) / 1e9, 3),
         "kernels": kernels,
-        "roofline": {"kernel": "dK/dV kernel (fa_bwd_stage FA_BWD_DKDV: one launch)",
+        "roofline": {"kernel": "dK/dV stage (fa_bwd_stage FA_BWD_DKDV: dkdv_split_kernel + dkdv_reduce_kernel)",
                      "bound": "mfma", "achieved": round(dkdv_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, "
-                                     "copy-calibrated)"},
+                     "traffic_unit": "HBM bytes per stage (FETCH_SIZE x2 + WRITE_SIZE x1, "
+                                     "copy-calibrated, both kernels)"},
         "memory": {"peak_allocated_bytes": int(peak_mem), "resident_bytes": int(resident),
                    "baseline_bytes": int(mem0)},
         "wall_s_timed": round(wall, 3),

@@ -151,8 +151,18 @@ size_t row_array_bytes(const Shape& s) {
   return (n + 255) / 256 * 256;
 }
 
-// Backward workspace: Delta, then LSE * log2(e) (both [B, Hq, Sq] float32).
-size_t delta_bytes(const Shape& s) { return 2 * row_array_bytes(s); }
+// The dK/dV kernel's partial sums (bf16, D = 128): two halves of float32
+// dK^T and dV^T, [2][2][B, Hkv, Skv, D], rounded up to 256 bytes.
+size_t part_bytes(const Shape& s) {
+  if (s.dtype != FA_BF16 || s.D != 128) return 0;
+  size_t n = (size_t)4 * std::max(s.B, 0) * (size_t)std::max(s.Hkv, 0) * (size_t)std::max(s.Skv, 0) *
+             (size_t)s.D * 4;
+  return (n + 255) / 256 * 256;
+}
+
+// Backward workspace: Delta, then LSE * log2(e) (both [B, Hq, Sq] float32),
+// then the dK/dV partial sums.
+size_t delta_bytes(const Shape& s) { return 2 * row_array_bytes(s) + part_bytes(s); }
 
 // Forward workspace (bf16 only): V^T, bfloat16 [B, Hkv, D, vt_keys(s)].
 int64_t vt_keys(const Shape& s) {
@@ -295,6 +305,7 @@ static fa_status bwd_run(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStr
   p.lse_in = a->lse;
   p.delta = static_cast<float*>(ws);
   p.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + row_array_bytes(s));
+  p.dkv_part = part_bytes(s) ? reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * row_array_bytes(s)) : nullptr;
   for (int stage = first_stage; stage <= last_stage; ++stage) {
     hipError_t e = s.dtype == FA_BF16 ? fa::launch_bwd_bf16(p, stage, stream)
                                       : fa::launch_bwd_f32(p, stage, stream);

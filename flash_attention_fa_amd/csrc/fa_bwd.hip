@@ -784,114 +784,126 @@ dkdv_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV with asynchronous staging (D >= 32).  Same work split as dkdv_kernel
-// (8 waves: wave w owns key block w % 4 and 32-row half w / 4 of each 64-row
-// query tile, natural scores S = Q K^T, a lane per key column), but the
-// workgroup's K and V rows and every step's Q and dO tiles are copied
-// HBM -> LDS by the asynchronous LDS copies of the forward, into unpadded
-// XOR-swizzled rows, double-buffered (one barrier per step).  dO^T and Q^T,
-// the A operands of dV^T += dO^T P and dK^T += Q^T dS, are read straight from
-// those row-major tiles with transposing LDS reads, so no transposed copy is
-// written at all.  Rows past Sq are copied from row 0 (finite) and masked.
+// dK/dV with asynchronous staging (D = 128).  A workgroup owns 256 keys of
+// one (batch, kv head) and one half of their (query tile, head) steps; wave
+// w owns keys 32w .. 32w+31 outright.  Its K rows stay in registers (the B
+// operand of S = Q K^T, natural orientation, a lane per key column); the
+// workgroup's V rows sit in LDS.  Each step stages one 32-row query tile of
+// one head (Q, dO, LSE*log2(e), Delta) by the asynchronous LDS copies of the
+// forward into unpadded XOR-swizzled rows, the next step's during this one
+// (double-buffered, one barrier per step).  dO^T and Q^T, the A operands of
+// dV^T += dO^T P and dK^T += Q^T dS, are read straight from those row-major
+// tiles with transposing LDS reads.  Rows past Sq are copied from the tile's
+// first row (finite) and masked.
+//
+// 256 keys per workgroup let each staged query row serve twice the matrix
+// work of a 128-key block (the copies into LDS are the kernel's costliest
+// non-matrix work); splitting each key block's steps between two workgroups
+// keeps enough workgroups to balance the causal triangle (the halves are the
+// two halves of the group's heads, or of the steps when the group is odd).
+// Each half writes its float32 sums to the workspace and dkdv_reduce_kernel
+// adds the two halves, always half 0 + half 1, so reruns are bitwise
+// identical.
 template <int D>
-struct KvDma {
-  static constexpr int NKB = 4;                        // 32-key blocks per workgroup
-  static constexpr int TKW = NKB * 32;                 // keys per workgroup
-  static constexpr int TQ = 64;                        // query rows per step
+struct KvSplit {
+  static constexpr int NW = 8;
+  static constexpr int TKW = NW * 32;                  // keys per workgroup
+  static constexpr int TQ = 32;                        // query rows per step
   static constexpr int TILE = TQ * D * 2;              // one Q or dO tile (bytes)
   static constexpr int STAGE = 2 * TILE + 2 * TQ * 4;  // Q, dO, LSE*log2(e), Delta
-  static constexpr int KVB = TKW * D * 2;              // the K (or V) rows
-  static constexpr int NDB = D / 32;
-  static constexpr int XBYTES = NKB * NDB * 16 * 64 * 4;   // one partial exchange
-  static constexpr int MAIN = 2 * STAGE + 2 * KVB;
-  static constexpr int BYTES = MAIN > XBYTES ? MAIN : XBYTES;
+  static constexpr int VB = TKW * D * 2;               // the V rows
+  static constexpr int BYTES = 2 * STAGE + VB;
 };
 
 template <int D>
 __global__ void __launch_bounds__(512)
-dkdv_dma_kernel(Params p) {
-  using L = KvDma<D>;
-  constexpr int NKB = L::NKB, TKW = L::TKW, TQ = L::TQ, NDB = L::NDB;
-  constexpr int NW = 2 * NKB;
-  constexpr int NJ = D / 16;
+dkdv_split_kernel(Params p) {
+  using L = KvSplit<D>;
+  constexpr int NW = L::NW, TKW = L::TKW, TQ = L::TQ;
+  constexpr int NJ = D / 16, NDB = D / 32;
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;         // rows per copy instruction
   constexpr int QINS = TQ / RPI;        // copy instructions per Q (or dO) tile
   constexpr int QLPW = 2 * QINS / NW;   // per wave per step
-  constexpr int KINS = TKW / RPI;       // copy instructions for the K (or V) rows
-  constexpr int KLPW = 2 * KINS / NW;
+  constexpr int VINS = TKW / RPI;       // copy instructions for the V rows
+  constexpr int VLPW = VINS / NW;
   constexpr int ROW16 = 16 * 2 * D;     // bytes of 16 rows
-  static_assert(D >= 32 && QLPW * NW == 2 * QINS && KLPW * NW == 2 * KINS, "copy split");
+  static_assert(D == 128 && QLPW * NW == 2 * QINS && QINS % QLPW == 0 && VLPW * NW == VINS,
+                "copy split");
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* const Ks = smem + 2 * L::STAGE;
-  unsigned char* const Vs = Ks + L::KVB;
+  unsigned char* const Vs = smem + 2 * L::STAGE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hh = lane >> 5;
-  const int kblk = wave % NKB, qhalf = wave / NKB;
 
+  // Block -> (batch, kv head, half of the steps) column and key-block rank.
   const int nkt = (p.Skv + TKW - 1) / TKW;
   int col, rank;
-  map_block(blockIdx.x, p.B * p.Hkv, nkt, col, rank);
-  const int b = col / p.Hkv, hk = col % p.Hkv;
+  map_block(blockIdx.x, p.B * p.Hkv * 2, nkt, col, rank);
+  const int half = col & 1, bh = col >> 1;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
   const MaskB m = resolve_mask(p, b);
   const int ka = rank * TKW, kbnd = min(p.Skv, ka + TKW);
-  const int kw = ka + kblk * 32, kwe = min(p.Skv, kw + 32);
+  const int kw = ka + wave * 32, kwe = min(p.Skv, kw + 32);
   const int key = kw + l32;
 
   const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
   const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
-
-  // Copy-lane geometry (the same for every tile): lane -> (row in its 1 KB
-  // run, swizzled chunk).
   const int crow = lane / CPR, cslot = lane % CPR;
 
-  // The workgroup's K and V rows; keys that are not real are copied from key
-  // 0 (finite values; their weights are masked to zero).
+  // The workgroup's V rows; keys that are not real are copied from key 0
+  // (finite values; their weights are masked to zero).
 #pragma unroll
-  for (int x = 0; x < KLPW; ++x) {
-    const int idx = wave * KLPW + x;
-    const int tensor = idx / KINS, ii = idx % KINS;
+  for (int x = 0; x < VLPW; ++x) {
+    const int ii = wave * VLPW + x;
     const int row = ii * RPI + crow;
     const int kk = ka + row;
-    const bool ok = key_valid_nb(m, kk);
     const int ch = 8 * (cslot ^ swz<D>(row));
-    const bf16* base = tensor == 0 ? Kg : Vg;
-    const int64_t ss = tensor == 0 ? p.k.ss : p.v.ss;
-    lds_dma16(base + (ok ? (int64_t)kk * ss + ch : (int64_t)ch), (tensor == 0 ? Ks : Vs) + ii * 1024);
+    lds_dma16(Vg + (key_valid_nb(m, kk) ? (int64_t)kk * p.v.ss + ch : (int64_t)ch), Vs + ii * 1024);
+  }
+  // This wave's K rows as the B operand of S: lane (key, hh) holds
+  // d = 16j + 8hh .. +8; keys that are not real hold zeros (and are masked).
+  bf16x8 kreg[NJ];
+  {
+    const bool kok = key_valid_nb(m, key);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      kreg[j] = kok ? *reinterpret_cast<const bf16x8*>(Kg + (int64_t)key * p.k.ss + 16 * j + 8 * hh) : bf16x8{};
   }
 
   int qlo, qhi;
   query_hull(m, ka, kbnd, qlo, qhi);
   const int t_first = qlo < qhi ? qlo / TQ : 0;
   const int t_last = qlo < qhi ? (qhi + TQ - 1) / TQ : 0;
+  // The block's (query tile, head) steps, tiles from the last down with the
+  // group's heads inside (so the workgroups sharing an XCD read the same
+  // tiles at about the same time).  With an even group each half takes half
+  // of the heads over every tile (each Q/dO tile is then read by one half
+  // only, on one XCD); with an odd one, half of the steps in that order.
   const int ntile = t_last - t_first;
-  // (query tile, head) pairs: tiles from the last down, the group's heads
-  // inside, so the workgroups sharing an XCD read the same Q / dO tiles at
-  // about the same time and its L2 serves them all.
-  const int nsteps = ntile * p.G;
+  const bool by_head = (p.G & 1) == 0;
+  const int hbeg = by_head ? half * (p.G / 2) : 0;
+  const int hend = by_head ? hbeg + p.G / 2 : p.G;
+  const int nall = ntile * p.G;
+  const int s0 = by_head || half == 0 ? 0 : (nall + 1) / 2;
+  const int nsteps = by_head ? ntile * (p.G / 2) : (half == 0 ? (nall + 1) / 2 : nall - (nall + 1) / 2);
 
-  // Stage s: Q and dO tiles by asynchronous copy; LSE*log2(e) and Delta of
-  // its rows through registers (64 threads, bounds-checked), written to LDS
-  // at the end of the previous step.  Step s is (tile t_last-1 - s/G, head
-  // hk*G + s%G); StepPos walks that order without divisions.
-  const bool stage_g = wave >= NW / 2;     // this wave copies dO rows (else Q)
+  // Waves 0..NW/2-1 copy the Q rows, the others the dO rows (a run of QLPW
+  // 1 KB copies each); LSE*log2(e) and Delta come through wave 0's registers.
+  const int cidx0 = wave * QLPW;
+  const bool stage_g = cidx0 >= QINS;
   const bf16* const Sbase = stage_g ? static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb
                                     : static_cast<const bf16*>(p.q.ptr) + b * p.q.sb;
   const int64_t ssh = stage_g ? p.dout.sh : p.q.sh;
   const int64_t sss = stage_g ? p.dout.ss : p.q.ss;
-  // this lane's swizzled chunk (element offset) in each of its tile rows
   int schunk[QLPW];
 #pragma unroll
-  for (int x = 0; x < QLPW; ++x) {
-    const int ii = (wave % (NW / 2)) * QLPW + x;
-    schunk[x] = 8 * (cslot ^ swz<D>(ii * RPI + crow));
-  }
+  for (int x = 0; x < QLPW; ++x) schunk[x] = 8 * (cslot ^ swz<D>((cidx0 % QINS + x) * RPI + crow));
   struct StepPos {
     int hs, q0;   // head slot in the group, first query row of the tile
   };
   auto advance = [&](StepPos& sp) __attribute__((always_inline)) {
-    if (++sp.hs == p.G) { sp.hs = 0; sp.q0 -= TQ; }
+    if (++sp.hs == hend) { sp.hs = hbeg; sp.q0 -= TQ; }
   };
   auto stage_rows = [&](const StepPos& sp, int buf) __attribute__((always_inline)) {
     const bf16* Sg = Sbase + (int64_t)(hk * p.G + sp.hs) * ssh + (int64_t)sp.q0 * sss;
@@ -899,7 +911,7 @@ dkdv_dma_kernel(Params p) {
     const bool whole = sp.q0 + TQ <= p.Sq;   // every row real: no per-lane select
 #pragma unroll
     for (int x = 0; x < QLPW; ++x) {
-      const int ii = (wave % (NW / 2)) * QLPW + x;
+      const int ii = cidx0 % QINS + x;
       const int row = ii * RPI + crow;
       const bool ok = whole || sp.q0 + row < p.Sq;
       // rows past Sq are copied from the tile's first row (real, finite);
@@ -920,22 +932,17 @@ dkdv_dma_kernel(Params p) {
     float* Ls = reinterpret_cast<float*>(smem + buf * L::STAGE + 2 * L::TILE);
     if (tid < TQ) { Ls[tid] = lrow; Ls[TQ + tid] = drow; }
   };
-  StepPos cur{0, (t_last - 1) * TQ};
+  StepPos cur{by_head ? hbeg : s0 % p.G, (t_last - 1 - (by_head ? 0 : s0 / p.G)) * TQ};
   StepPos nxt = cur;
   if (nsteps > 0) advance(nxt);
-
   if (nsteps > 0) {
     stage_rows(cur, 0);
     fetch_rowvals(cur);
-    wait_vmcnt<0>();
-    store_rowvals(0);
-  } else {
-    wait_vmcnt<0>();
   }
+  wait_vmcnt<0>();
+  if (nsteps > 0) store_rowvals(0);
   __syncthreads();
 
-  // Lane-constant offsets: row reads (16 rows repeat their swizzle) and the
-  // transposing reads of dO^T / Q^T (as the forward reads V^T).
   int roff[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) roff[j] = swz_off<D>(l32, 16 * j + 8 * hh);
@@ -947,13 +954,7 @@ dkdv_dma_kernel(Params p) {
     toff[0][c] = swz_off<D>(4 * hh + tr_row, 32 * c + tr_col);
     toff[1][c] = swz_off<D>(4 * hh + tr_row + 8, 32 * c + tr_col);
   }
-  const int qrow0 = 32 * qhalf * 2 * D;      // byte offset of this wave's 32 query rows
-  // This wave's 32 K rows stay in registers (the B operand of S every
-  // step); its V rows (dP's) are read from LDS.
-  bf16x8 kreg[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) kreg[j] = *FA_LDS(const bf16x8, Ks + kblk * 32 * 2 * D + roff[j]);
-  const unsigned char* Vw = Vs + kblk * 32 * 2 * D;
+  const unsigned char* Vw = Vs + wave * 32 * 2 * D;
 
   f32x16 dka[NDB], dva[NDB];
 #pragma unroll
@@ -975,20 +976,20 @@ dkdv_dma_kernel(Params p) {
     }
     const unsigned char* Qt = smem + buf * L::STAGE;
     const unsigned char* Gt = Qt + L::TILE;
-    const float* Ls = reinterpret_cast<const float*>(Qt + 2 * L::TILE) + 32 * qhalf;
+    const float* Ls = reinterpret_cast<const float*>(Qt + 2 * L::TILE);
     const float* Ds = Ls + TQ;
-    const int qa = cur.q0 + 32 * qhalf;
+    const int qa = cur.q0;
     int state = TILE_FULL;
-    if (!(qa >= qfull && qa + 32 <= p.Sq)) {
-      state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + 32));
-      if (state == TILE_FULL && qa + 32 > p.Sq) state = TILE_PART;   // rows past Sq
+    if (!(qa >= qfull && qa + TQ <= p.Sq)) {
+      state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + TQ));
+      if (state == TILE_FULL && qa + TQ > p.Sq) state = TILE_PART;   // rows past Sq
     }
     if (state != TILE_SKIP) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const bf16x8 aq = *FA_LDS(const bf16x8, Qt + qrow0 + roff[j]);
-        const bf16x8 ag = *FA_LDS(const bf16x8, Gt + qrow0 + roff[j]);
+        const bf16x8 aq = *FA_LDS(const bf16x8, Qt + roff[j]);
+        const bf16x8 ag = *FA_LDS(const bf16x8, Gt + roff[j]);
         s = mfma32(aq, kreg[j], s);
         dp = mfma32(ag, *FA_LDS(const bf16x8, Vw + roff[j]), dp);
       }
@@ -1025,7 +1026,7 @@ dkdv_dma_kernel(Params p) {
       // registers hold the rows in).
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int rows = qrow0 + st * ROW16;
+        const int rows = st * ROW16;
 #pragma unroll
         for (int c = 0; c < NDB; ++c) {
           const bf16x8 ag = cat8(lds_read_tr4(reinterpret_cast<const bf16*>(Gt + rows + toff[0][c])),
@@ -1044,41 +1045,49 @@ dkdv_dma_kernel(Params p) {
     advance(nxt);
   }
 
-  // Pair reduction through LDS (the loop's last barrier freed it), then
-  // dK = s * (dK^T)^T, dV = (dV^T)^T; lane (key, hh) holds d = 32c + 8g + 4hh + u.
-  float* X = reinterpret_cast<float*>(smem);
-  bf16* DKg = static_cast<bf16*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh;
-  bf16* DVg = static_cast<bf16*>(const_cast<void*>(p.dv.ptr)) + b * p.dv.sb + hk * p.dv.sh;
+  // This half's sums dK^T / dV^T as float32 rows of the workspace (unscaled);
+  // lane (key, hh) holds d = 32c + 8g + 4hh + u.
+  if (key < p.Skv) {
+    const int64_t n = (int64_t)p.B * p.Hkv * p.Skv * D;
+    const int64_t row = ((int64_t)bh * p.Skv + key) * D;
+    float* PK = p.dkv_part + (int64_t)half * 2 * n + row;
+    float* PV = PK + n;
 #pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    f32x16* acc = which == 0 ? dka : dva;
-    if (qhalf == 1) {
+    for (int c = 0; c < NDB; ++c)
 #pragma unroll
-      for (int c = 0; c < NDB; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) X[((kblk * NDB + c) * 16 + i) * 64 + lane] = acc[c][i];
-    }
-    __syncthreads();
-    if (qhalf == 0) {
-#pragma unroll
-      for (int c = 0; c < NDB; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[c][i] += X[((kblk * NDB + c) * 16 + i) * 64 + lane];
-      if (key < p.Skv) {
-        const float sc = which == 0 ? p.scale : 1.0f;
-        bf16* dst_row = (which == 0 ? DKg + (int64_t)key * p.dk.ss : DVg + (int64_t)key * p.dv.ss);
-#pragma unroll
-        for (int c = 0; c < NDB; ++c)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d = 32 * c + 8 * g + 4 * hh;
-            *reinterpret_cast<bf16x4*>(dst_row + d) =
-                to_bf16x4(acc[c][4 * g] * sc, acc[c][4 * g + 1] * sc, acc[c][4 * g + 2] * sc,
-                          acc[c][4 * g + 3] * sc);
-          }
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * c + 8 * g + 4 * hh;
+        *reinterpret_cast<f32x4*>(PK + d) = f32x4{dka[c][4 * g], dka[c][4 * g + 1], dka[c][4 * g + 2], dka[c][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(PV + d) = f32x4{dva[c][4 * g], dva[c][4 * g + 1], dva[c][4 * g + 2], dva[c][4 * g + 3]};
       }
-    }
-    __syncthreads();
+  }
+}
+
+// dK = scale * (half 0 + half 1), dV = half 0 + half 1, rounded to bf16; 8
+// consecutive d of one key per thread.
+template <int D>
+__global__ void __launch_bounds__(256) dkdv_reduce_kernel(Params p) {
+  const int64_t n = (int64_t)p.B * p.Hkv * p.Skv * D;
+  const int64_t i8 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i8 >= n) return;
+  const int64_t row = i8 / D;
+  const int d = (int)(i8 % D);
+  const int key = (int)(row % p.Skv);
+  const int bh = (int)(row / p.Skv);
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const float* P = p.dkv_part + i8;
+  bf16* DK = static_cast<bf16*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh + (int64_t)key * p.dk.ss + d;
+  bf16* DV = static_cast<bf16*>(const_cast<void*>(p.dv.ptr)) + b * p.dv.sb + hk * p.dv.sh + (int64_t)key * p.dv.ss + d;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(P + t * n);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(P + t * n + 4);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(P + 2 * n + t * n);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(P + 2 * n + t * n + 4);
+    const float sc = t == 0 ? p.scale : 1.0f;
+    const bf16x8 o = cat8(to_bf16x4((a0[0] + b0[0]) * sc, (a0[1] + b0[1]) * sc, (a0[2] + b0[2]) * sc, (a0[3] + b0[3]) * sc),
+                          to_bf16x4((a1[0] + b1[0]) * sc, (a1[1] + b1[1]) * sc, (a1[2] + b1[2]) * sc, (a1[3] + b1[3]) * sc));
+    *reinterpret_cast<bf16x8*>(t == 0 ? DK : DV) = o;
   }
 }
 
@@ -1109,12 +1118,15 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
   }
   if constexpr (D == 128) {
     if (stage == STAGE_DKDV) {
-      using LD = KvDma<D>;
-      const int64_t nblk = (int64_t)p.B * p.Hkv * ((p.Skv + LD::TKW - 1) / LD::TKW);
+      using LD = KvSplit<D>;
+      const int64_t nblk = (int64_t)p.B * p.Hkv * 2 * ((p.Skv + LD::TKW - 1) / LD::TKW);
       if (nblk > 0) {
-        auto k = dkdv_dma_kernel<D>;
+        auto k = dkdv_split_kernel<D>;
         if ((e = set_lds(k, LD::BYTES)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(512), LD::BYTES, stream, p);
+        hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(LD::NW * 64), LD::BYTES, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int64_t n8 = (int64_t)p.B * p.Hkv * p.Skv * D / 8;
+        hipLaunchKernelGGL(dkdv_reduce_kernel<D>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
     }

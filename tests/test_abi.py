@@ -213,7 +213,12 @@ def test_backward_validation():
 def test_workspace_is_linear_in_sequence_length():
     sizes = [_lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=s, Skv=s, D=128))
              for s in (16384, 32768)]
-    assert sizes[1] == 2 * sizes[0] == 2 * 2 * 32 * 16384 * 4
+    # Delta and LSE*log2(e) [B, Hq, Sq], then the dK/dV halves' float32 sums 4 x [B, Hkv, Skv, D]
+    assert sizes[1] == 2 * sizes[0] == 2 * (2 * 32 * 16384 * 4 + 4 * 4 * 16384 * 128 * 4)
+    # other head dims and fp32 need no partial sums
+    assert _lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=64)) == 2 * 32 * 256 * 4
+    assert _lib.lib().fa_bwd_workspace_bytes(
+        bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=128, dtype=_lib.FA_F32)) == 2 * 32 * 256 * 4
     sizes = [_lib.lib().fa_fwd_workspace_bytes(fwd_args(B=1, Hq=32, Hkv=4, Sq=s, Skv=s, D=128))
              for s in (16384, 32768)]
     assert sizes[1] == 2 * sizes[0] == 2 * 4 * 128 * 16384 * 2
