@@ -788,8 +788,9 @@ dkdv_kernel(Params p) {
 // one (batch, kv head) and one half of their (query tile, head) steps; wave
 // w owns keys 32w .. 32w+31 outright.  Its K rows stay in registers (the B
 // operand of S = Q K^T, natural orientation, a lane per key column); the
-// workgroup's V rows sit in LDS.  Each step stages one 32-row query tile of
-// one head (Q, dO, LSE*log2(e), Delta) by the asynchronous LDS copies of the
+// workgroup's V rows sit in LDS.  Each step stages one 64-row query tile of
+// one head (Q, dO, LSE*log2(e), Delta), worked through as two 32-row
+// sub-tiles, by the asynchronous LDS copies of the
 // forward into unpadded XOR-swizzled rows, the next step's during this one
 // (double-buffered, one barrier per step).  dO^T and Q^T, the A operands of
 // dV^T += dO^T P and dK^T += Q^T dS, are read straight from those row-major
@@ -808,7 +809,7 @@ template <int D>
 struct KvSplit {
   static constexpr int NW = 8;
   static constexpr int TKW = NW * 32;                  // keys per workgroup
-  static constexpr int TQ = 32;                        // query rows per step
+  static constexpr int TQ = 64;                        // query rows per step (two 32-row sub-tiles)
   static constexpr int TILE = TQ * D * 2;              // one Q or dO tile (bytes)
   static constexpr int STAGE = 2 * TILE + 2 * TQ * 4;  // Q, dO, LSE*log2(e), Delta
   static constexpr int VB = TKW * D * 2;               // the V rows
@@ -978,18 +979,20 @@ dkdv_split_kernel(Params p) {
     const unsigned char* Gt = Qt + L::TILE;
     const float* Ls = reinterpret_cast<const float*>(Qt + 2 * L::TILE);
     const float* Ds = Ls + TQ;
-    const int qa = cur.q0;
+#pragma unroll 1
+    for (int h = 0; h < TQ / 32; ++h) {   // 32-row sub-tiles, one at a time
+    const int qa = cur.q0 + 32 * h;
     int state = TILE_FULL;
-    if (!(qa >= qfull && qa + TQ <= p.Sq)) {
-      state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + TQ));
-      if (state == TILE_FULL && qa + TQ > p.Sq) state = TILE_PART;   // rows past Sq
+    if (!(qa >= qfull && qa + 32 <= p.Sq)) {
+      state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + 32));
+      if (state == TILE_FULL && qa + 32 > p.Sq) state = TILE_PART;   // rows past Sq
     }
     if (state != TILE_SKIP) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const bf16x8 aq = *FA_LDS(const bf16x8, Qt + roff[j]);
-        const bf16x8 ag = *FA_LDS(const bf16x8, Gt + roff[j]);
+        const bf16x8 aq = *FA_LDS(const bf16x8, Qt + h * 32 * 2 * D + roff[j]);
+        const bf16x8 ag = *FA_LDS(const bf16x8, Gt + h * 32 * 2 * D + roff[j]);
         s = mfma32(aq, kreg[j], s);
         dp = mfma32(ag, *FA_LDS(const bf16x8, Vw + roff[j]), dp);
       }
@@ -1008,8 +1011,8 @@ dkdv_split_kernel(Params p) {
 #pragma unroll
         for (int g2 = 0; g2 < 2; ++g2) {
           const int g = 2 * st + g2;
-          const f32x4 l4 = *FA_LDS(const f32x4, Ls + 8 * g + 4 * hh);
-          const f32x4 d4 = *FA_LDS(const f32x4, Ds + 8 * g + 4 * hh);
+          const f32x4 l4 = *FA_LDS(const f32x4, Ls + 32 * h + 8 * g + 4 * hh);
+          const f32x4 d4 = *FA_LDS(const f32x4, Ds + 32 * h + 8 * g + 4 * hh);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int i = 4 * g + u;
@@ -1026,7 +1029,7 @@ dkdv_split_kernel(Params p) {
       // registers hold the rows in).
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int rows = st * ROW16;
+        const int rows = h * 32 * 2 * D + st * ROW16;
 #pragma unroll
         for (int c = 0; c < NDB; ++c) {
           const bf16x8 ag = cat8(lds_read_tr4(reinterpret_cast<const bf16*>(Gt + rows + toff[0][c])),
@@ -1037,6 +1040,7 @@ dkdv_split_kernel(Params p) {
           dka[c] = mfma32(aq, dsb[st], dka[c]);
         }
       }
+    }
     }
     if (more) store_rowvals(buf ^ 1);
     wait_vmcnt<0>();
