@@ -40,6 +40,14 @@ def test_bf16_gqa_causal(G):
     check_case(q, k, v, do, CAUSAL, "bf16", label=f"bf16 gqa G={G}")
 
 
+@pytest.mark.parametrize("G", [2, 3])
+def test_bf16_gqa_group_split(G):
+    # D = 128 dK/dV splits each key block's work between two workgroups: by
+    # halves of the group's heads when G is even, by halves of the steps when odd
+    q, k, v, do = inputs(2, 2 * G, 2, 300, 300, 128, torch.bfloat16, seed=13 + G)
+    check_case(q, k, v, do, CAUSAL, "bf16", label=f"bf16 gqa split G={G}")
+
+
 def test_bf16_cross_attention_padded_keys():
     # Sq != Skv, per-batch valid key counts that are not tile multiples
     q, k, v, do = inputs(2, 4, 4, 200, 333, 64, torch.bfloat16, seed=11)
@@ -147,13 +155,14 @@ def test_bitwise_determinism(kind):
         assert np.array_equal(a[name], b[name]), name
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_staged_backward_equals_fa_bwd(dtype):
-    """fa_bwd_stage DELTA, DKDV, DQ in turn writes bitwise what fa_bwd writes."""
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 64), (torch.bfloat16, 128), (torch.float32, 64)])
+def test_staged_backward_equals_fa_bwd(dtype, D):
+    """fa_bwd_stage DELTA, DKDV, DQ in turn writes bitwise what fa_bwd writes
+    (at D = 128 the dK/dV stage is the split kernel and its reduction)."""
     import flash_attention_fa_amd as fa
     L = 320
-    q, k, v, do = (x.cuda() for x in inputs(1, 8, 2, L, L, 64, dtype, seed=53))
-    say(f"[staged] dtype={dtype}")
+    q, k, v, do = (x.cuda() for x in inputs(1, 8, 2, L, L, D, dtype, seed=53))
+    say(f"[staged] dtype={dtype} D={D}")
     o, lse = fa.fa_fwd(q, k, v, mask_kind=CAUSAL)
     ref = fa.fa_bwd(q, k, v, o, lse, do, mask_kind=CAUSAL)
     dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
@@ -167,7 +176,7 @@ def test_staged_backward_equals_fa_bwd(dtype):
 
 
 # Launches with at least 512 workgroups of 256 query rows (B*Hq*ceil(Sq/256))
-# take the one-wave-per-SIMD forward at D=128 and the 8-wave dQ kernel; these
+# take the 8-wave forward and dQ kernels (256 query rows per workgroup); these
 # cases reach them with ragged tiles, GQA, every mask kind and padding.
 MANY = [
     ("causal", CAUSAL, 300, 300, 0, None),
