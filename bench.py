@@ -31,6 +31,15 @@ must match the current kernel sources, else it is null.
 
 runs one 256 MiB device-to-device copy: its FETCH_SIZE/WRITE_SIZE readings
 give the factor that turns those counters into bytes.
+
+    python bench.py --sweep [--steps K] [--warmup W]
+
+times every named workload in turn (the tiny fp32 cases, the batch-8 grid,
+16K/32K long GQA, the TTT step-2 call, DiT self- and cross-attention) and
+prints one JSON line per workload: fwd / bwd / step times, TFLOP/s, the
+fraction of the dense peak of the arithmetic type, the attainable rate
+min(peak, AI x 8 TB/s) from the algorithmic bytes, and the peak device memory
+of one fwd+bwd.  No oracle timing.
 """
 import argparse
 import hashlib
@@ -48,6 +57,7 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0
 
 
@@ -73,6 +83,17 @@ def pair_count(w):
 def flops(w):
     pairs = sum(pair_count(w)) * w.Hq
     return 4 * w.D * pairs, 10 * w.D * pairs
+
+
+def algorithmic_bytes(w):
+    """HBM bytes the forward and the backward must move at least: the forward
+    reads Q, K, V and writes O and LSE; the backward reads Q, K, V, O, dO and
+    LSE, writes dQ, dK, dV, and writes and reads Delta."""
+    e = 2 if w.dtype == "bf16" else 4
+    qsz, kvsz, rows = w.B * w.Hq * w.Sq * w.D, w.B * w.Hkv * w.Skv * w.D, w.B * w.Hq * w.Sq
+    fwd = e * (2 * qsz + 2 * kvsz) + 4 * rows
+    bwd = e * (4 * qsz + 4 * kvsz) + 4 * rows + 8 * rows
+    return fwd, bwd
 
 
 def kernel_flops(w):
@@ -155,32 +176,21 @@ def cpu_baseline(w, q, k, v, do, nheads):
                       f"host nproc {os.cpu_count()})"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=W.HEADLINE.name)
-    ap.add_argument("--cpu-heads", type=int, default=2,
-                    help="query heads of batch 0 the oracle baseline computes")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="run one 256 MiB device copy (counter calibration) and exit")
-    a = ap.parse_args()
-    if a.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
-              "(one process drives one GPU; the library does not shard across GPUs)", file=sys.stderr)
-        return 2
+def dkdv_label(w):
+    if w.dtype == "bf16" and w.D == 128:
+        return "dK/dV stage (fa_bwd_stage FA_BWD_DKDV: dkdv_split_kernel + dkdv_reduce_kernel)"
+    return "dK/dV stage (fa_bwd_stage FA_BWD_DKDV: one kernel)"
 
-    if a.copy_calibration:
-        return copy_calibration()
-    import flash_attention_fa_amd as fa
-    w = find_workload(a.workload)
-    dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", 0)))
-    torch.cuda.set_device(dev)
-    q, k, v, do = W.make_inputs(w, seed=0)
-    qg, kg, vg, dog = (x.to(dev) for x in (q, k, v, do))
+
+def measure(fa, w, dev, steps, warmup, inputs):
+    """Times `steps` fwd+bwd steps of workload w after `warmup` untimed ones,
+    with HIP events on the launch stream around the forward and after each
+    backward stage."""
+    qg, kg, vg, dog = (x.to(dev) for x in inputs)
     kvv = W.kv_valid_tensor(w, dev)
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
     o = torch.empty_like(qg)
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
@@ -199,19 +209,18 @@ def main():
             if marks is not None:
                 marks[i].record(stream)
 
-    torch.cuda.synchronize()
-    mem0 = torch.cuda.memory_allocated(dev)
-    torch.cuda.reset_peak_memory_stats(dev)
-    for _ in range(a.warmup):
+    for _ in range(warmup):
         fwd()
         bwd()
     torch.cuda.synchronize()
+    # peak over outputs, workspaces and one fwd+bwd, above the resident inputs
+    peak_mem = torch.cuda.max_memory_allocated(dev) - mem0
 
     # events: step start, fwd end, Delta end, dK/dV end, dQ end (= step end)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(a.steps):
+    for s in range(steps):
         ev[s][0].record(stream)
         fwd()
         ev[s][1].record(stream)
@@ -219,19 +228,79 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     span = lambda i, j: [e[i].elapsed_time(e[j]) for e in ev]
-    fwd_ms = span(0, 1)
-    bwd_ms = span(1, 4)
-    stage_ms = {"delta": span(1, 2), "dkdv": span(2, 3), "dq": span(3, 4)}
-    total_ms = ev[0][0].elapsed_time(ev[-1][4])
-    ms_step = total_ms / a.steps
+    # inputs + outputs + workspace resident during the step
+    resident = sum(t.numel() * t.element_size() for t in (qg, kg, vg, dog, o, lse, dq, dk, dv, ws, fws))
+    return {"fwd_ms": span(0, 1), "bwd_ms": span(1, 4),
+            "stage_ms": {"delta": span(1, 2), "dkdv": span(2, 3), "dq": span(3, 4)},
+            "ms_step": ev[0][0].elapsed_time(ev[-1][4]) / steps,
+            "peak_mem": int(peak_mem), "resident": int(resident), "mem0": int(mem0), "wall": wall}
+
+
+def sweep(fa, dev, steps, warmup):
+    """One JSON line per named workload (see the module docstring)."""
+    for w in W.all_workloads():
+        print(json.dumps({"sweep_case": w.name}), flush=True)
+        r = measure(fa, w, dev, steps, warmup, W.make_inputs(w, seed=0))
+        f_fwd, f_bwd = flops(w)
+        b_fwd, b_bwd = algorithmic_bytes(w)
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        fwd_med, bwd_med = float(np.median(r["fwd_ms"])), float(np.median(r["bwd_ms"]))
+        tf = lambda f, ms: f / (ms * 1e-3) / 1e12
+        att = lambda f, b: min(peak, f / b * PEAK_HBM_GBS / 1e3)
+        row = {"workload": w.name, "dtype": w.dtype,
+               "config": {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Skv": w.Skv, "D": w.D,
+                          "mask": W.KIND_NAMES[w.kind], "kv_valid": w.kv_valid},
+               "peak_tflops": peak}
+        for name, f, b, ms in (("fwd", f_fwd, b_fwd, fwd_med), ("bwd", f_bwd, b_bwd, bwd_med),
+                               ("step", f_fwd + f_bwd, b_fwd + b_bwd, r["ms_step"])):
+            row[name] = {"ms": round(ms, 4), "tflops": round(tf(f, ms), 2),
+                         "pct_of_peak": round(100 * tf(f, ms) / peak, 2),
+                         "ai_flop_per_byte": round(f / b, 1),
+                         "attainable_tflops": round(att(f, b), 1),
+                         "pct_of_attainable": round(100 * tf(f, ms) / att(f, b), 2)}
+        row["stages_ms_mean"] = {n: round(float(np.mean(v)), 4) for n, v in r["stage_ms"].items()}
+        row["peak_mem_bytes"] = r["peak_mem"]
+        print(json.dumps(row), flush=True)
+        torch.cuda.empty_cache()
+    return 0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=W.HEADLINE.name)
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="query heads of batch 0 the oracle baseline computes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every named workload, one JSON line each, and exit")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 256 MiB device copy (counter calibration) and exit")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(one process drives one GPU; the library does not shard across GPUs)", file=sys.stderr)
+        return 2
+
+    if a.copy_calibration:
+        return copy_calibration()
+    import flash_attention_fa_amd as fa
+    dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", 0)))
+    torch.cuda.set_device(dev)
+    if a.sweep:
+        return sweep(fa, dev, a.steps, a.warmup)
+    w = find_workload(a.workload)
+    q, k, v, do = W.make_inputs(w, seed=0)
+    r = measure(fa, w, dev, a.steps, a.warmup, (q, k, v, do))
+    fwd_ms, bwd_ms, stage_ms, ms_step = r["fwd_ms"], r["bwd_ms"], r["stage_ms"], r["ms_step"]
     f_fwd, f_bwd = flops(w)
     fwd_med, bwd_med = float(np.median(fwd_ms)), float(np.median(bwd_ms))
     fwd_avg = float(np.mean(fwd_ms))
     tf = lambda f, ms: f / (ms * 1e-3) / 1e12
     value = tf(f_fwd + f_bwd, ms_step)
-    peak_mem = torch.cuda.max_memory_allocated(dev)
-    # inputs + outputs + workspace resident during the step
-    resident = sum(t.numel() * t.element_size() for t in (qg, kg, vg, dog, o, lse, dq, dk, dv, ws, fws))
+    peak_mem, resident, mem0, wall = r["peak_mem"], r["resident"], r["mem0"], r["wall"]
 
     kf = kernel_flops(w)
     k_avg = {"fwd": fwd_avg, **{n: float(np.mean(v)) for n, v in stage_ms.items()}}
@@ -267,14 +336,14 @@ def main():
                 "pct_of_peak": round(100 * tf(f_bwd, bwd_med) / PEAK_BF16_TFLOPS, 2)},
         "gflop_per_step": round((f_fwd + f_bwd) / 1e9, 3),
         "kernels": kernels,
-        "roofline": {"kernel": "dK/dV stage (fa_bwd_stage FA_BWD_DKDV: dkdv_split_kernel + dkdv_reduce_kernel)",
+        "roofline": {"kernel": dkdv_label(w),
                      "bound": "mfma", "achieved": round(dkdv_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
                      "traffic_unit": "HBM bytes per stage (FETCH_SIZE x2 + WRITE_SIZE x1, "
                                      "copy-calibrated, both kernels)"},
-        "memory": {"peak_allocated_bytes": int(peak_mem), "resident_bytes": int(resident),
-                   "baseline_bytes": int(mem0)},
+        "memory": {"peak_above_inputs_bytes": int(peak_mem), "resident_bytes": int(resident),
+                   "inputs_bytes": int(mem0)},
         "wall_s_timed": round(wall, 3),
     }
     if not a.no_cpu_baseline:
