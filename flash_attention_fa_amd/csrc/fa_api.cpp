@@ -151,10 +151,10 @@ size_t row_array_bytes(const Shape& s) {
   return (n + 255) / 256 * 256;
 }
 
-// The dK/dV kernel's partial sums (bf16, D = 128): two halves of float32
+// The dK/dV kernel's partial sums (bf16, D >= 32): two halves of float32
 // dK^T and dV^T, [2][2][B, Hkv, Skv, D], rounded up to 256 bytes.
 size_t part_bytes(const Shape& s) {
-  if (s.dtype != FA_BF16 || s.D != 128) return 0;
+  if (s.dtype != FA_BF16 || s.D < 32) return 0;
   size_t n = (size_t)4 * std::max(s.B, 0) * (size_t)std::max(s.Hkv, 0) * (size_t)std::max(s.Skv, 0) *
              (size_t)s.D * 4;
   return (n + 255) / 256 * 256;

@@ -511,15 +511,15 @@ dq_dma_kernel(Params p) {
 //
 // Two waves share each 32-key block: wave w takes key block w % NKB and the
 // (w / NKB)-th 32-row half of every 64-row query tile, so a SIMD runs two
-// waves and one hides the other's latency.  K^T stays in registers (or, at
-// D = 128, in LDS beside V) and V^T is read from an LDS copy of the
-// workgroup's V rows.  Each query tile is staged row-major and transposed, so
+// waves and one hides the other's latency.  K^T stays in registers and V^T
+// is read from an LDS copy of the workgroup's V rows (this kernel serves
+// D = 16; wider heads take dkdv_split_kernel).  Each query tile is staged row-major and transposed, so
 // every MFMA operand is one 16-byte LDS read.  At the end the second
 // wave of each pair hands its partial dK/dV to the first through LDS, which
 // adds it to its own (always in that order) and writes the result.
 constexpr int KV_TQ = 64;
 
-template <int D, int NKB, bool KLDS>
+template <int D, int NKB>
 struct KvLds {
   static constexpr int STR = D + 8;
   static constexpr int TILE = KV_TQ * STR;                    // Q or dO rows
@@ -527,7 +527,7 @@ struct KvLds {
   // one stage: Q rows, Q^T, dO rows, dO^T (bf16), then LSE and Delta (fp32)
   static constexpr int STAGE = 2 * (TILE + TT) * 2 + 2 * KV_TQ * 4;
   static constexpr int VROWS = NKB * 32;
-  static constexpr int VBYTES = VROWS * STR * 2 * (KLDS ? 2 : 1);  // V rows (then K rows)
+  static constexpr int VBYTES = VROWS * STR * 2;                // V rows
   static constexpr int NDB = D >= 32 ? D / 32 : 1;
   static constexpr int XBYTES = NKB * NDB * 16 * 64 * 4;      // one partial exchange
   // double-buffer the stage when it fits next to the K/V rows
@@ -536,7 +536,7 @@ struct KvLds {
   static constexpr int BYTES = MAIN > XBYTES ? MAIN : XBYTES;
 };
 
-template <int D, int NKB, bool KLDS>
+template <int D, int NKB>
 __global__ void __launch_bounds__(NKB * 2 * 64)
 dkdv_kernel(Params p) {
   constexpr int NW = 2 * NKB;
@@ -549,10 +549,9 @@ dkdv_kernel(Params p) {
   constexpr int PER_T = (UNITS + HALF - 1) / HALF;
   constexpr int NDB = D >= 32 ? D / 32 : 1;
   constexpr int NJ = D / 16;
-  using L = KvLds<D, NKB, KLDS>;
+  using L = KvLds<D, NKB>;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* Vs = reinterpret_cast<bf16*>(smem + L::NBUF * L::STAGE);
-  bf16* Ksh = Vs + L::VROWS * L::STR;  // K rows, when K^T is read from LDS
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hh = lane >> 5;
@@ -571,8 +570,8 @@ dkdv_kernel(Params p) {
   const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
 
   // K^T as the B operand: lane (key = l32, hh) holds K[key][16j + 8hh .. +8].
-  bf16x8 kreg[KLDS ? 1 : NJ];
-  if constexpr (!KLDS) {
+  bf16x8 kreg[NJ];
+  {
     const int key = kw + l32;
     const bool ok = key_valid(m, key);
 #pragma unroll
@@ -580,17 +579,13 @@ dkdv_kernel(Params p) {
       kreg[j] = ok ? *reinterpret_cast<const bf16x8*>(Kg + (int64_t)key * p.k.ss + 16 * j + 8 * hh)
                    : bf16x8{};
   }
-  // The workgroup's V (and K) rows, zero for keys that are not real.
+  // The workgroup's V rows, zero for keys that are not real.
   for (int c = tid; c < TKW * DC; c += NT) {
     const int r = c / DC, c8 = c % DC;
     const int key = ka + r;
     const bool ok = key_valid(m, key);
     const i32x4 val = ok ? *reinterpret_cast<const i32x4*>(Vg + (int64_t)key * p.v.ss + 8 * c8) : i32x4{};
     lds_write16(Vs + r * L::STR + 8 * c8, val);
-    if constexpr (KLDS) {
-      const i32x4 kv = ok ? *reinterpret_cast<const i32x4*>(Kg + (int64_t)key * p.k.ss + 8 * c8) : i32x4{};
-      lds_write16(Ksh + r * L::STR + 8 * c8, kv);
-    }
   }
 
   f32x16 dka[NDB], dva[NDB];
@@ -664,7 +659,6 @@ dkdv_kernel(Params p) {
   const int t_row = d_lane_ok ? l32 : 0;
   const int key = kw + l32;
   const bf16* Vrow = Vs + (kblk * 32 + l32) * L::STR + 8 * hh;
-  const bf16* Krow = Ksh + (kblk * 32 + l32) * L::STR + 8 * hh;
 
   for (int step = 0; step < nsteps; ++step) {
     if (step + 1 < nsteps) fetch(step + 1);
@@ -685,9 +679,7 @@ dkdv_kernel(Params p) {
         const bf16x8 aq = lds_read8(Qs + l32 * L::STR + 16 * j + 8 * hh);
         const bf16x8 ag = lds_read8(Gs + l32 * L::STR + 16 * j + 8 * hh);
         const bf16x8 bv = lds_read8(Vrow + 16 * j);
-        bf16x8 bk;
-        if constexpr (KLDS) bk = lds_read8(Krow + 16 * j); else bk = kreg[j];
-        s = mfma32(aq, bk, s);
+        s = mfma32(aq, kreg[j], s);
         dp = mfma32(ag, bv, dp);
       }
       // Per-register query rows: q = qa + 8*(i/4) + 4*hh + i%4.
@@ -784,7 +776,7 @@ dkdv_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV with asynchronous staging (D = 128).  A workgroup owns 256 keys of
+// dK/dV with asynchronous staging (D >= 32).  A workgroup owns 256 keys of
 // one (batch, kv head) and one half of their (query tile, head) steps; wave
 // w owns keys 32w .. 32w+31 outright.  Its K rows stay in registers (the B
 // operand of S = Q K^T, natural orientation, a lane per key column); the
@@ -829,7 +821,7 @@ dkdv_split_kernel(Params p) {
   constexpr int VINS = TKW / RPI;       // copy instructions for the V rows
   constexpr int VLPW = VINS / NW;
   constexpr int ROW16 = 16 * 2 * D;     // bytes of 16 rows
-  static_assert(D == 128 && QLPW * NW == 2 * QINS && QINS % QLPW == 0 && VLPW * NW == VINS,
+  static_assert(D >= 32 && QLPW * NW == 2 * QINS && QINS % QLPW == 0 && VLPW * NW == VINS,
                 "copy split");
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* const Vs = smem + 2 * L::STAGE;
@@ -1120,7 +1112,7 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if constexpr (D == 128) {
+  if constexpr (D >= 32) {
     if (stage == STAGE_DKDV) {
       using LD = KvSplit<D>;
       const int64_t nblk = (int64_t)p.B * p.Hkv * 2 * ((p.Skv + LD::TKW - 1) / LD::TKW);
@@ -1136,11 +1128,10 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     }
   } else if (stage == STAGE_DKDV) {
     constexpr int NKB = 4, TKW = NKB * 32;
-    constexpr bool KLDS = D >= 128;
     const int64_t nblk = (int64_t)p.B * p.Hkv * ((p.Skv + TKW - 1) / TKW);
     if (nblk > 0) {
-      auto k = dkdv_kernel<D, NKB, KLDS>;
-      constexpr int lds = KvLds<D, NKB, KLDS>::BYTES;
+      auto k = dkdv_kernel<D, NKB>;
+      constexpr int lds = KvLds<D, NKB>::BYTES;
       if ((e = set_lds(k, lds)) != hipSuccess) return e;
       hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NKB * 2 * 64), lds, stream, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1149,7 +1140,7 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
   if (stage == STAGE_DQ && p.B > 0 && p.Sq > 0) {
     // 8-wave workgroups when there are enough to fill the chip twice over
     const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
-    if constexpr (D == 128) {
+    if constexpr (D >= 32) {
       const bool ttt = p.mask.kind == MASK_TTT;
       auto k = wg8 >= 512 ? (ttt ? dq_dma_kernel<D, 8, true> : dq_dma_kernel<D, 8, false>)
                           : (ttt ? dq_dma_kernel<D, 4, true> : dq_dma_kernel<D, 4, false>);

@@ -35,7 +35,7 @@ struct Params {
   const float* lse_in; // backward input
   float* delta;        // backward workspace: Delta [B, Hq, Sq]
   float* lse2;         // backward workspace: LSE * log2(e) [B, Hq, Sq]
-  float* dkv_part;     // backward workspace (bf16, D = 128): two halves' float32
+  float* dkv_part;     // backward workspace (bf16, D >= 32): two halves' float32
                        // sums [2][dK^T, dV^T][B, Hkv, Skv, D]
 };
 

@@ -132,7 +132,7 @@ fa_status fa_fwd(const fa_fwd_args* args, void* ws, size_t ws_bytes, hipStream_t
 
 /* Bytes of device scratch fa_bwd needs for these arguments: two float32
  * [B, Hq, Sq] arrays (Delta, and LSE in log2 units), each rounded up to 256
- * bytes, and for FA_BF16 with D = 128 the dK/dV kernel's float32 partial
+ * bytes, and for FA_BF16 with D >= 32 the dK/dV kernel's float32 partial
  * sums, four [B, Hkv, Skv, D] arrays (two halves of each key block's query
  * steps, dK and dV), rounded up to 256 bytes; linear in Sq and Skv, never
  * S x S.  Returns 0 when args is NULL. */

@@ -188,7 +188,8 @@ def test_forward_empty_is_a_noop():
 def test_backward_validation():
     a = bwd_args()
     need = _lib.lib().fa_bwd_workspace_bytes(a)
-    assert need == 2 * ((1 * 4 * 64 * 4 + 255) // 256 * 256)
+    # Delta and LSE*log2(e) [B, Hq, Sq], then the dK/dV halves' float32 sums 4 x [B, Hkv, Skv, D]
+    assert need == 2 * ((1 * 4 * 64 * 4 + 255) // 256 * 256) + 4 * 1 * 2 * 64 * 64 * 4
     assert _lib.lib().fa_bwd_workspace_bytes(None) == 0
     st, msg = bwd(a, ws_bytes=need - 1)
     assert st == _lib.FA_ERR_INVALID_ARG and "workspace too small" in msg
@@ -215,8 +216,12 @@ def test_workspace_is_linear_in_sequence_length():
              for s in (16384, 32768)]
     # Delta and LSE*log2(e) [B, Hq, Sq], then the dK/dV halves' float32 sums 4 x [B, Hkv, Skv, D]
     assert sizes[1] == 2 * sizes[0] == 2 * (2 * 32 * 16384 * 4 + 4 * 4 * 16384 * 128 * 4)
-    # other head dims and fp32 need no partial sums
-    assert _lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=64)) == 2 * 32 * 256 * 4
+    # bf16 at D = 32 and 64 holds the partial sums too; D = 16 and fp32 need none
+    assert _lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=64)) == \
+        2 * 32 * 256 * 4 + 4 * 4 * 256 * 64 * 4
+    assert _lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=32)) == \
+        2 * 32 * 256 * 4 + 4 * 4 * 256 * 32 * 4
+    assert _lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=16)) == 2 * 32 * 256 * 4
     assert _lib.lib().fa_bwd_workspace_bytes(
         bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=128, dtype=_lib.FA_F32)) == 2 * 32 * 256 * 4
     sizes = [_lib.lib().fa_fwd_workspace_bytes(fwd_args(B=1, Hq=32, Hkv=4, Sq=s, Skv=s, D=128))

@@ -40,12 +40,13 @@ def test_bf16_gqa_causal(G):
     check_case(q, k, v, do, CAUSAL, "bf16", label=f"bf16 gqa G={G}")
 
 
+@pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("G", [2, 3])
-def test_bf16_gqa_group_split(G):
-    # D = 128 dK/dV splits each key block's work between two workgroups: by
+def test_bf16_gqa_group_split(G, D):
+    # The D >= 32 dK/dV splits each key block's work between two workgroups: by
     # halves of the group's heads when G is even, by halves of the steps when odd
-    q, k, v, do = inputs(2, 2 * G, 2, 300, 300, 128, torch.bfloat16, seed=13 + G)
-    check_case(q, k, v, do, CAUSAL, "bf16", label=f"bf16 gqa split G={G}")
+    q, k, v, do = inputs(2, 2 * G, 2, 300, 300, D, torch.bfloat16, seed=13 + G + D)
+    check_case(q, k, v, do, CAUSAL, "bf16", label=f"bf16 gqa split G={G} D={D}")
 
 
 def test_bf16_cross_attention_padded_keys():
@@ -95,6 +96,12 @@ def test_bf16_ttt(L, t, shift, kvv):
     q, k, v, do = inputs(1, 8, 2, L, (t + 1) * L, 128, torch.bfloat16, seed=L + t)
     check_case(q, k, v, do, TTT, "bf16", shift=shift, kv_valid=kvv,
                label=f"bf16 ttt L={L} t={t} shift={shift}")
+
+
+@pytest.mark.parametrize("D", [32, 64])
+def test_bf16_ttt_small_head_dim(D):
+    q, k, v, do = inputs(1, 4, 2, 130, 390, D, torch.bfloat16, seed=D + 5)
+    check_case(q, k, v, do, TTT, "bf16", kv_valid=(100,), label=f"bf16 ttt D={D}")
 
 
 def test_bf16_bshd_strided_views():
@@ -155,10 +162,11 @@ def test_bitwise_determinism(kind):
         assert np.array_equal(a[name], b[name]), name
 
 
-@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 64), (torch.bfloat16, 128), (torch.float32, 64)])
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 16), (torch.bfloat16, 64), (torch.bfloat16, 128),
+                                     (torch.float32, 64)])
 def test_staged_backward_equals_fa_bwd(dtype, D):
     """fa_bwd_stage DELTA, DKDV, DQ in turn writes bitwise what fa_bwd writes
-    (at D = 128 the dK/dV stage is the split kernel and its reduction)."""
+    (at D >= 32 the dK/dV stage is the split kernel and its reduction)."""
     import flash_attention_fa_amd as fa
     L = 320
     q, k, v, do = (x.cuda() for x in inputs(1, 8, 2, L, L, D, dtype, seed=53))
@@ -193,6 +201,14 @@ def test_bf16_many_workgroups(case):
     name, kind, Sq, Skv, shift, kvv = case
     q, k, v, do = inputs(4, 128, 16, Sq, Skv, 128, torch.bfloat16, seed=61)
     check_case(q, k, v, do, kind, "bf16", shift=shift, kv_valid=kvv, label=f"bf16 many-WG {name}")
+
+
+@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("case", MANY[:3], ids=[c[0] for c in MANY[:3]])
+def test_bf16_many_workgroups_small_head_dim(case, D):
+    name, kind, Sq, Skv, shift, kvv = case
+    q, k, v, do = inputs(4, 128, 16, Sq, Skv, D, torch.bfloat16, seed=71 + D)
+    check_case(q, k, v, do, kind, "bf16", shift=shift, kv_valid=kvv, label=f"bf16 many-WG {name} D={D}")
 
 
 def test_bf16_many_workgroups_nan_padding():
