@@ -152,17 +152,19 @@ size_t row_array_bytes(const Shape& s) {
 }
 
 // The dK/dV kernel's partial sums (bf16, D >= 32): two halves of float32
-// dK^T and dV^T, [2][2][B, Hkv, Skv, D], rounded up to 256 bytes.
-size_t part_bytes(const Shape& s) {
+// dK^T and dV^T, [2][2][B, Hkv, keys, D], rounded up to 256 bytes, over the
+// keys the tile kernel owns (all Skv, or under TTT the Sq step-0 keys).
+size_t part_bytes(const Shape& s, int kind) {
   if (s.dtype != FA_BF16 || s.D < 32) return 0;
-  size_t n = (size_t)4 * std::max(s.B, 0) * (size_t)std::max(s.Hkv, 0) * (size_t)std::max(s.Skv, 0) *
+  const int keys = kind == FA_MASK_TTT && s.Sq < s.Skv ? s.Sq : s.Skv;
+  size_t n = (size_t)4 * std::max(s.B, 0) * (size_t)std::max(s.Hkv, 0) * (size_t)std::max(keys, 0) *
              (size_t)s.D * 4;
   return (n + 255) / 256 * 256;
 }
 
 // Backward workspace: Delta, then LSE * log2(e) (both [B, Hq, Sq] float32),
 // then the dK/dV partial sums.
-size_t delta_bytes(const Shape& s) { return 2 * row_array_bytes(s) + part_bytes(s); }
+size_t delta_bytes(const Shape& s, int kind) { return 2 * row_array_bytes(s) + part_bytes(s, kind); }
 
 // Forward workspace (bf16 only): V^T, bfloat16 [B, Hkv, D, vt_keys(s)].
 int64_t vt_keys(const Shape& s) {
@@ -249,7 +251,7 @@ fa_status fa_fwd(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t st
 size_t fa_bwd_workspace_bytes(const fa_bwd_args* a) {
   if (!a) return 0;
   Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
-  return delta_bytes(s);
+  return delta_bytes(s, a->mask.kind);
 }
 
 // Validates a backward call and launches the requested stages in order.
@@ -272,7 +274,7 @@ static fa_status bwd_run(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStr
   if (rows && a->lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse: NULL pointer");
   if (rows && reinterpret_cast<uintptr_t>(a->lse) % 4 != 0)
     return fail(FA_ERR_ALIGNMENT, "lse: pointer is not 4-byte aligned");
-  const size_t need = delta_bytes(s);
+  const size_t need = delta_bytes(s, a->mask.kind);
   if ((st = check_ws(ws, ws_bytes, need))) return st;
   if (a->mask.kv_valid && reinterpret_cast<uintptr_t>(a->mask.kv_valid) % 4 != 0)
     return fail(FA_ERR_ALIGNMENT, "kv_valid: pointer is not 4-byte aligned");
@@ -305,7 +307,8 @@ static fa_status bwd_run(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStr
   p.lse_in = a->lse;
   p.delta = static_cast<float*>(ws);
   p.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + row_array_bytes(s));
-  p.dkv_part = part_bytes(s) ? reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * row_array_bytes(s)) : nullptr;
+  p.dkv_part = part_bytes(s, a->mask.kind) ? reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * row_array_bytes(s))
+                                            : nullptr;
   for (int stage = first_stage; stage <= last_stage; ++stage) {
     hipError_t e = s.dtype == FA_BF16 ? fa::launch_bwd_bf16(p, stage, stream)
                                       : fa::launch_bwd_f32(p, stage, stream);

@@ -297,8 +297,10 @@ struct DqDma {
   static constexpr int BYTES = DQ_NBUF * BUF;
 };
 
-// TTT: instantiated for the EAGLE3 mask; the other instance knows the kind
-// is FULL or CAUSAL, which drops the TTT arms of the tile walk and the mask.
+// TTT: instantiated for the EAGLE3 mask.  As in the forward, both instances
+// walk FULL or CAUSAL tiles only (the TTT instance its step-0 keys, which the
+// causal mask describes), and the TTT instance adds the single key s*L + i of
+// each later step s to row i's dQ with vector arithmetic (ttt_fold).
 template <int D, int NW, bool TTT>
 __global__ void __launch_bounds__(NW * 64, 2)
 dq_dma_kernel(Params p) {
@@ -326,7 +328,8 @@ dq_dma_kernel(Params p) {
   const int b = col / p.Hq, h = col % p.Hq, hk = h / p.G;
   const int qtile = p.mask.kind == MASK_FULL ? rank : nq - 1 - rank;
   MaskB m = resolve_mask(p, b);
-  m.kind = TTT ? MASK_TTT : (m.kind == MASK_FULL ? MASK_FULL : MASK_CAUSAL);
+  m.kind = !TTT && m.kind == MASK_FULL ? MASK_FULL : MASK_CAUSAL;
+  if (TTT) m.Skv = min(m.Skv, m.L);
   const int qa = qtile * TQ, qb = min(p.Sq, qa + TQ);
   const int wa = qa + wave * 32, wb = min(p.Sq, wa + 32);
   const int qi = wa + l32;
@@ -352,6 +355,41 @@ dq_dma_kernel(Params p) {
   f32x16 acc[NDB];
 #pragma unroll
   for (int c = 0; c < NDB; ++c) acc[c] = f32x16{};
+
+  if constexpr (TTT) {
+    // ttt_fold: for key j = s*L + i of each later step s (row i below
+    // kv_valid), P = exp2(scale log2(e) q_i.k_j - LSE_i log2(e)), dP =
+    // dO_i.v_j, dS = P (dP - Delta_i) and dQ_i^T += k_j dS, in fp32, before
+    // the tile loop.  Each lane half holds half of every dot product (the d
+    // of qreg / greg), summed across the halves.
+    const int nseg = p.Skv / p.Sq;
+    const bool rok = qok && qi < m.kvv;
+#pragma unroll 1
+    for (int s = 1; s < nseg; ++s) {
+      const int64_t j = (int64_t)s * p.Sq + (rok ? qi : 0);
+      const bf16* kr = Kg + j * p.k.ss;
+      const bf16* vr = Vg + j * p.v.ss + 8 * hh;
+      float sd = 0.f, pd = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        sd = dot_bf16x8(qreg[jj], *reinterpret_cast<const bf16x8*>(kr + 8 * hh + 16 * jj), sd);
+        pd = dot_bf16x8(greg[jj], *reinterpret_cast<const bf16x8*>(vr + 16 * jj), pd);
+      }
+      sd = half_swap_sum(sd);
+      pd = half_swap_sum(pd);
+      const float pr = rok ? exp2_fast(sd * p.scale_log2 - l2) : 0.f;
+      const float ds = pr * (pd - dlt);
+      const bf16* kd = kr + 4 * hh;
+#pragma unroll
+      for (int c = 0; c < NDB; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(kd + 32 * c + 8 * g);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[c][4 * g + u] += ds * (float)k4[u];
+        }
+    }
+  }
 
   const int crow = lane / CPR, cslot = lane % CPR;
   int roff[LPW];
@@ -797,6 +835,12 @@ dkdv_kernel(Params p) {
 // Each half writes its float32 sums to the workspace and dkdv_reduce_kernel
 // adds the two halves, always half 0 + half 1, so reruns are bitwise
 // identical.
+// Keys the tile kernels of the dK/dV stage own: all of them, or under TTT
+// the step-0 keys (the later steps' keys each meet one query row).
+__device__ __host__ __forceinline__ int dkdv_tile_keys(const Params& p) {
+  return p.mask.kind == MASK_TTT && p.Sq < p.Skv ? p.Sq : p.Skv;
+}
+
 template <int D>
 struct KvSplit {
   static constexpr int NW = 8;
@@ -830,14 +874,20 @@ dkdv_split_kernel(Params p) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   // Block -> (batch, kv head, half of the steps) column and key-block rank.
-  const int nkt = (p.Skv + TKW - 1) / TKW;
+  // Under TTT this kernel takes the step-0 keys (below L = Sq), which the
+  // causal mask with the same shift and kv_valid describes; ttt_dkdv_kernel
+  // takes the keys of the later steps.
+  const int nkeys = dkdv_tile_keys(p);
+  const int nkt = (nkeys + TKW - 1) / TKW;
   int col, rank;
   map_block(blockIdx.x, p.B * p.Hkv * 2, nkt, col, rank);
   const int half = col & 1, bh = col >> 1;
   const int b = bh / p.Hkv, hk = bh % p.Hkv;
-  const MaskB m = resolve_mask(p, b);
-  const int ka = rank * TKW, kbnd = min(p.Skv, ka + TKW);
-  const int kw = ka + wave * 32, kwe = min(p.Skv, kw + 32);
+  MaskB m = resolve_mask(p, b);
+  m.kind = m.kind == MASK_FULL ? MASK_FULL : MASK_CAUSAL;
+  m.Skv = nkeys;
+  const int ka = rank * TKW, kbnd = min(nkeys, ka + TKW);
+  const int kw = ka + wave * 32, kwe = min(nkeys, kw + 32);
   const int key = kw + l32;
 
   const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
@@ -1043,9 +1093,9 @@ dkdv_split_kernel(Params p) {
 
   // This half's sums dK^T / dV^T as float32 rows of the workspace (unscaled);
   // lane (key, hh) holds d = 32c + 8g + 4hh + u.
-  if (key < p.Skv) {
-    const int64_t n = (int64_t)p.B * p.Hkv * p.Skv * D;
-    const int64_t row = ((int64_t)bh * p.Skv + key) * D;
+  if (key < nkeys) {
+    const int64_t n = (int64_t)p.B * p.Hkv * nkeys * D;
+    const int64_t row = ((int64_t)bh * nkeys + key) * D;
     float* PK = p.dkv_part + (int64_t)half * 2 * n + row;
     float* PV = PK + n;
 #pragma unroll
@@ -1063,13 +1113,14 @@ dkdv_split_kernel(Params p) {
 // consecutive d of one key per thread.
 template <int D>
 __global__ void __launch_bounds__(256) dkdv_reduce_kernel(Params p) {
-  const int64_t n = (int64_t)p.B * p.Hkv * p.Skv * D;
+  const int nkeys = dkdv_tile_keys(p);
+  const int64_t n = (int64_t)p.B * p.Hkv * nkeys * D;
   const int64_t i8 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (i8 >= n) return;
   const int64_t row = i8 / D;
   const int d = (int)(i8 % D);
-  const int key = (int)(row % p.Skv);
-  const int bh = (int)(row / p.Skv);
+  const int key = (int)(row % nkeys);
+  const int bh = (int)(row / nkeys);
   const int b = bh / p.Hkv, hk = bh % p.Hkv;
   const float* P = p.dkv_part + i8;
   bf16* DK = static_cast<bf16*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh + (int64_t)key * p.dk.ss + d;
@@ -1085,6 +1136,62 @@ __global__ void __launch_bounds__(256) dkdv_reduce_kernel(Params p) {
                           to_bf16x4((a1[0] + b1[0]) * sc, (a1[1] + b1[1]) * sc, (a1[2] + b1[2]) * sc, (a1[3] + b1[3]) * sc));
     *reinterpret_cast<bf16x8*>(t == 0 ? DK : DV) = o;
   }
+}
+
+// dK/dV of the TTT keys past step 0.  Key j = s*L + r (s >= 1, L = Sq)
+// meets one query row, r, in each head of its group (when r < kv_valid):
+//   dV_j = sum_h P_h dO_hr,  dK_j = scale * sum_h dS_h Q_hr,
+//   P_h = exp2(scale log2(e) q_hr.k_j - LSE_hr log2(e)),  dS_h = P_h (dO_hr.v_j - Delta_hr),
+// the heads summed in order (bitwise reproducible).  D/8 lanes per key, eight
+// consecutive d each, the two dot products summed over the key's lanes by a
+// butterfly (every lane ends with the same sum).  Consecutive key groups take
+// the later steps of one row r, so its Q and dO rows are read together.
+// Keys whose row is not below kv_valid get exact zeros.
+template <int D>
+__global__ void __launch_bounds__(256) ttt_dkdv_kernel(Params p) {
+  constexpr int LPK = D / 8, KPB = 256 / LPK;
+  const int L = p.Sq, nlate = p.Skv - p.Sq, nst = p.Skv / p.Sq - 1;
+  const int64_t g = (int64_t)blockIdx.x * KPB + threadIdx.x / LPK;
+  if (g >= (int64_t)p.B * p.Hkv * nlate) return;   // whole key groups leave together
+  const int sub = threadIdx.x % LPK;
+  const int bh = (int)(g / nlate), idx = (int)(g % nlate);
+  const int r = idx / nst, j = (1 + idx % nst) * L + r;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const MaskB m = resolve_mask(p, b);
+  const bf16x8 k8 = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.k.ptr) + b * p.k.sb +
+                                                     hk * p.k.sh + (int64_t)j * p.k.ss + 8 * sub);
+  const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.v.ptr) + b * p.v.sb +
+                                                     hk * p.v.sh + (int64_t)j * p.v.ss + 8 * sub);
+  float dk[8] = {}, dv[8] = {};
+  if (r < m.kvv) {
+    for (int h = 0; h < p.G; ++h) {
+      const int hq = hk * p.G + h;
+      const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.q.ptr) + b * p.q.sb +
+                                                         hq * p.q.sh + (int64_t)r * p.q.ss + 8 * sub);
+      const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb +
+                                                         hq * p.dout.sh + (int64_t)r * p.dout.ss + 8 * sub);
+      const int64_t row = ((int64_t)b * p.Hq + hq) * p.Sq + r;
+      float sd = dot_bf16x8(q8, k8, 0.f), pd = dot_bf16x8(g8, v8, 0.f);
+#pragma unroll
+      for (int o = 1; o < LPK; o <<= 1) {
+        sd += __shfl_xor(sd, o, LPK);
+        pd += __shfl_xor(pd, o, LPK);
+      }
+      const float pr = exp2_fast(sd * p.scale_log2 - p.lse2[row]);
+      const float ds = pr * (pd - p.delta[row]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dv[e] += pr * (float)g8[e];
+        dk[e] += ds * (float)q8[e];
+      }
+    }
+  }
+  bf16* DK = static_cast<bf16*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh + (int64_t)j * p.dk.ss + 8 * sub;
+  bf16* DV = static_cast<bf16*>(const_cast<void*>(p.dv.ptr)) + b * p.dv.sb + hk * p.dv.sh + (int64_t)j * p.dv.ss + 8 * sub;
+  const float sc = p.scale;
+  *reinterpret_cast<bf16x8*>(DK) = cat8(to_bf16x4(dk[0] * sc, dk[1] * sc, dk[2] * sc, dk[3] * sc),
+                                        to_bf16x4(dk[4] * sc, dk[5] * sc, dk[6] * sc, dk[7] * sc));
+  *reinterpret_cast<bf16x8*>(DV) = cat8(to_bf16x4(dv[0], dv[1], dv[2], dv[3]), to_bf16x4(dv[4], dv[5], dv[6], dv[7]));
 }
 
 template <typename K>
@@ -1115,14 +1222,21 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
   if constexpr (D >= 32) {
     if (stage == STAGE_DKDV) {
       using LD = KvSplit<D>;
-      const int64_t nblk = (int64_t)p.B * p.Hkv * 2 * ((p.Skv + LD::TKW - 1) / LD::TKW);
+      const int nkeys = dkdv_tile_keys(p);
+      const int64_t nblk = (int64_t)p.B * p.Hkv * 2 * ((nkeys + LD::TKW - 1) / LD::TKW);
       if (nblk > 0) {
         auto k = dkdv_split_kernel<D>;
         if ((e = set_lds(k, LD::BYTES)) != hipSuccess) return e;
         hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(LD::NW * 64), LD::BYTES, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int64_t n8 = (int64_t)p.B * p.Hkv * p.Skv * D / 8;
+        const int64_t n8 = (int64_t)p.B * p.Hkv * nkeys * D / 8;
         hipLaunchKernelGGL(dkdv_reduce_kernel<D>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      const int64_t nlate = (int64_t)p.B * p.Hkv * (p.Skv - nkeys);
+      if (p.mask.kind == MASK_TTT && nlate > 0) {
+        constexpr int KPB = 256 / (D / 8);
+        hipLaunchKernelGGL(ttt_dkdv_kernel<D>, dim3((unsigned)((nlate + KPB - 1) / KPB)), dim3(256), 0, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
     }

@@ -59,6 +59,15 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// c + the dot product of two bf16x8 (four two-way dot products, fp32).
+__device__ __forceinline__ float dot_bf16x8(bf16x8 x, bf16x8 y, float c) {
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), __builtin_shufflevector(y, y, 0, 1), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), __builtin_shufflevector(y, y, 2, 3), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), __builtin_shufflevector(y, y, 4, 5), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), __builtin_shufflevector(y, y, 6, 7), c, false);
+  return c;
+}
+
 // c + the sum of the eight bf16 values of x (four two-way dot products with
 // ones, accumulated in fp32).
 __device__ __forceinline__ float sum_bf16x8(bf16x8 x, float c) {

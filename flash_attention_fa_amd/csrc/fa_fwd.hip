@@ -77,16 +77,20 @@ __host__ __device__ constexpr int vt_pos(int j) { return (j & ~12) | ((j & 4) <<
 // for real keys and 0 for every other position of the padded key range
 // (past Skv, or not valid under the mask), so the forward's copies need no
 // per-row selection and masked keys add 0 * 0.  A block converts one
-// (b, hk, tile) at a time, striding over all of them.
+// (b, hk, tile) at a time, striding over all of them; `ntile` tiles per
+// (b, hk), the ones the forward's tile walk reads.
 template <int D>
-__global__ void __launch_bounds__(256) vt_kernel(Params p, int64_t nblk) {
+__global__ void __launch_bounds__(256) vt_kernel(Params p, int ntile, int64_t nblk) {
   __shared__ bf16 tile[TK][D + 8];
-  const int ntile = (int)(p.vt_ss / TK);
   constexpr int CPR = D / 8;
   for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
     const int t = (int)(blk % ntile), bh = (int)(blk / ntile);
     const int b = bh / p.Hkv, hk = bh % p.Hkv;
-    const MaskB m = resolve_mask(p, b);
+    MaskB m = resolve_mask(p, b);
+    if (m.kind == MASK_TTT) {   // the tile walk's view: step-0 keys only
+      m.kind = MASK_CAUSAL;
+      m.Skv = min(m.Skv, m.L);
+    }
     const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
     __syncthreads();   // the previous tile's reads of `tile` are done
     for (int i = threadIdx.x; i < TK * CPR; i += 256) {
@@ -112,8 +116,13 @@ struct Buf {
   static constexpr int value = K;
 };
 
-// TTT: instantiated for the EAGLE3 mask; the other instance may assume
-// FULL or CAUSAL, which drops the TTT arms of the tile walk and the mask.
+// TTT: instantiated for the EAGLE3 mask.  Its step-0 part (keys below L =
+// Sq) is the causal mask with the same shift and kv_valid, so the tile loop
+// of both instances knows the kind is FULL or CAUSAL (which drops every TTT
+// arm from it).  The keys of steps 1 .. n-1 that row i sees are the single
+// keys s*L + i (when i < kv_valid): instead of a 64-key tile per step that
+// holds one key per row, each lane folds its row's keys into the running
+// max, normaliser and O before the tile loop (ttt_fold).
 template <int D, int NW, bool TTT>
 __global__ void __launch_bounds__(NW * 64, 2)
 fwd_kernel(Params p) {
@@ -139,8 +148,10 @@ fwd_kernel(Params p) {
   const int b = col / p.Hq, h = col % p.Hq, hk = h / p.G;
   const int qtile = p.mask.kind == MASK_FULL ? rank : nq - 1 - rank;
   MaskB m = resolve_mask(p, b);
-  // the instance's kind, visibly to the compiler (FULL or CAUSAL, or TTT)
-  m.kind = TTT ? MASK_TTT : (m.kind == MASK_FULL ? MASK_FULL : MASK_CAUSAL);
+  // the tile loop's kind, visibly to the compiler: FULL or CAUSAL (the TTT
+  // instance walks its step-0 keys, which the causal mask describes)
+  m.kind = !TTT && m.kind == MASK_FULL ? MASK_FULL : MASK_CAUSAL;
+  if (TTT) m.Skv = min(m.Skv, m.L);
 
   const int qa = qtile * TQ, qb = min(p.Sq, qa + TQ);
   const int wa = qa + wave * 32, wb = min(p.Sq, wa + 32);
@@ -162,6 +173,45 @@ fwd_kernel(Params p) {
 #pragma unroll
   for (int c = 0; c < NDB; ++c) acc[c] = f32x16{};
   float mrun = kMaxInit, lsum = 0.f;
+
+  if constexpr (TTT) {
+    // ttt_fold: key s*L + i of each later step s, one per row, with the exact
+    // running max (no lazy bound here), before the tile loop (the order of
+    // the keys does not change the result).  The score's two lane halves each
+    // hold half of q_i.k (the d of qreg), summed across the halves; O^T
+    // takes p * V row in the lane's own d positions.  Rows that are not real
+    // or not below kv_valid take score -inf, which leaves O, l and the max
+    // unchanged.
+    const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
+    const int nseg = p.Skv / p.Sq;
+    const bool rok = qi < p.Sq && qi < m.kvv;
+#pragma unroll 1
+    for (int s = 1; s < nseg; ++s) {
+      const int64_t j = (int64_t)s * p.Sq + (rok ? qi : 0);
+      const bf16* kr = Kg + j * p.k.ss + 8 * hh;
+      const bf16* vr = Vg + j * p.v.ss + 4 * hh;
+      float dot = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) dot = dot_bf16x8(qreg[jj], *reinterpret_cast<const bf16x8*>(kr + 16 * jj), dot);
+      dot = half_swap_sum(dot);
+      const float x = rok ? dot * p.scale_log2 : -INFINITY;
+      const float mn = fmaxf(mrun, x);
+      const float alpha = exp2_fast(mrun - mn);
+      const float pr = exp2_fast(x - mn);
+      mrun = mn;
+      lsum = lsum * alpha + (hh == 0 ? pr : 0.f);   // l's two halves are summed at the end
+#pragma unroll
+      for (int c = 0; c < NDB; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (32 * c + 8 * g >= D) continue;   // d = 32c + 8g + 4hh does not exist (D = 16)
+          const bf16x4 v4 = *reinterpret_cast<const bf16x4*>(vr + 32 * c + 8 * g);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[c][4 * g + u] = acc[c][4 * g + u] * alpha + pr * (float)v4[u];
+        }
+    }
+  }
+
 
   // Asynchronous copy of key tile t into ring buffer k: this wave's share of
   // the 2 * NINS instructions (K rows first, then V^T rows; which kind a
@@ -435,10 +485,13 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   const int nq = (p.Sq + TQ - 1) / TQ;
   const int64_t nblk = (int64_t)p.B * p.Hq * nq;
   if (nblk == 0) return hipSuccess;
-  const int64_t nvt = (int64_t)p.B * p.Hkv * (p.vt_ss / TK);
+  // V^T of the keys the tile walk reads (under TTT, the step-0 keys only)
+  const int walk_keys = p.mask.kind == MASK_TTT ? std::min(p.Skv, p.Sq) : p.Skv;
+  const int nvtile = (walk_keys + TK - 1) / TK;
+  const int64_t nvt = (int64_t)p.B * p.Hkv * nvtile;
   if (nvt > 0) {
     const unsigned grid = (unsigned)std::min<int64_t>(nvt, 1 << 20);
-    hipLaunchKernelGGL(vt_kernel<D>, dim3(grid), dim3(256), 0, stream, p, nvt);
+    hipLaunchKernelGGL(vt_kernel<D>, dim3(grid), dim3(256), 0, stream, p, nvtile, nvt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

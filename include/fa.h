@@ -134,8 +134,9 @@ fa_status fa_fwd(const fa_fwd_args* args, void* ws, size_t ws_bytes, hipStream_t
  * [B, Hq, Sq] arrays (Delta, and LSE in log2 units), each rounded up to 256
  * bytes, and for FA_BF16 with D >= 32 the dK/dV kernel's float32 partial
  * sums, four [B, Hkv, Skv, D] arrays (two halves of each key block's query
- * steps, dK and dV), rounded up to 256 bytes; linear in Sq and Skv, never
- * S x S.  Returns 0 when args is NULL. */
+ * steps, dK and dV; under FA_MASK_TTT only the Sq step-0 keys have them, so
+ * Sq replaces Skv), rounded up to 256 bytes; linear in Sq and Skv, never
+ * S x S.  Depends on args->mask.kind.  Returns 0 when args is NULL. */
 size_t fa_bwd_workspace_bytes(const fa_bwd_args* args);
 
 /* Backward: writes dQ, dK, dV; bitwise identical on every rerun (fixed

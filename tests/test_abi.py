@@ -216,6 +216,9 @@ def test_workspace_is_linear_in_sequence_length():
              for s in (16384, 32768)]
     # Delta and LSE*log2(e) [B, Hq, Sq], then the dK/dV halves' float32 sums 4 x [B, Hkv, Skv, D]
     assert sizes[1] == 2 * sizes[0] == 2 * (2 * 32 * 16384 * 4 + 4 * 4 * 16384 * 128 * 4)
+    # under TTT only the Sq step-0 keys have partial sums
+    ttt = bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=768, D=128, kind=_lib.FA_MASK_TTT)
+    assert _lib.lib().fa_bwd_workspace_bytes(ttt) == 2 * 32 * 256 * 4 + 4 * 4 * 256 * 128 * 4
     # bf16 at D = 32 and 64 holds the partial sums too; D = 16 and fp32 need none
     assert _lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=64)) == \
         2 * 32 * 256 * 4 + 4 * 4 * 256 * 64 * 4

@@ -98,7 +98,7 @@ def test_bf16_ttt(L, t, shift, kvv):
                label=f"bf16 ttt L={L} t={t} shift={shift}")
 
 
-@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("D", [16, 32, 64])
 def test_bf16_ttt_small_head_dim(D):
     q, k, v, do = inputs(1, 4, 2, 130, 390, D, torch.bfloat16, seed=D + 5)
     check_case(q, k, v, do, TTT, "bf16", kv_valid=(100,), label=f"bf16 ttt D={D}")
