@@ -835,12 +835,6 @@ dkdv_kernel(Params p) {
 // Each half writes its float32 sums to the workspace and dkdv_reduce_kernel
 // adds the two halves, always half 0 + half 1, so reruns are bitwise
 // identical.
-// Keys the tile kernels of the dK/dV stage own: all of them, or under TTT
-// the step-0 keys (the later steps' keys each meet one query row).
-__device__ __host__ __forceinline__ int dkdv_tile_keys(const Params& p) {
-  return p.mask.kind == MASK_TTT && p.Sq < p.Skv ? p.Sq : p.Skv;
-}
-
 template <int D>
 struct KvSplit {
   static constexpr int NW = 8;
@@ -877,7 +871,7 @@ dkdv_split_kernel(Params p) {
   // Under TTT this kernel takes the step-0 keys (below L = Sq), which the
   // causal mask with the same shift and kv_valid describes; ttt_dkdv_kernel
   // takes the keys of the later steps.
-  const int nkeys = dkdv_tile_keys(p);
+  const int nkeys = walk_keys(p);
   const int nkt = (nkeys + TKW - 1) / TKW;
   int col, rank;
   map_block(blockIdx.x, p.B * p.Hkv * 2, nkt, col, rank);
@@ -1113,7 +1107,7 @@ dkdv_split_kernel(Params p) {
 // consecutive d of one key per thread.
 template <int D>
 __global__ void __launch_bounds__(256) dkdv_reduce_kernel(Params p) {
-  const int nkeys = dkdv_tile_keys(p);
+  const int nkeys = walk_keys(p);
   const int64_t n = (int64_t)p.B * p.Hkv * nkeys * D;
   const int64_t i8 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (i8 >= n) return;
@@ -1222,7 +1216,7 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
   if constexpr (D >= 32) {
     if (stage == STAGE_DKDV) {
       using LD = KvSplit<D>;
-      const int nkeys = dkdv_tile_keys(p);
+      const int nkeys = walk_keys(p);
       const int64_t nblk = (int64_t)p.B * p.Hkv * 2 * ((nkeys + LD::TKW - 1) / LD::TKW);
       if (nblk > 0) {
         auto k = dkdv_split_kernel<D>;

@@ -384,6 +384,84 @@ struct TileWalk {
 };
 
 // --------------------------------------------------------------------------
+// Transposed key tiles.  The forward's PV product reads V^T as MFMA A
+// operands whose k index runs over keys; a small pre-pass writes such a
+// transposed copy, X^T[b, hk, d, keys] of a [b, hk, keys, d] tensor X, into
+// the caller's workspace, in tiles of kVtTile keys.
+//
+// Row d of a tile is 64 keys (128 bytes, eight 16-byte chunks); in LDS chunk
+// c of row d sits at slot c ^ vt_swz(d), so the 16 rows one 16-lane group of
+// a 16-byte read touches cover all 64 banks.
+__device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 7; }
+
+// Stored position of key tile offset j in a transposed row: within each
+// group of 16 keys, bits 2 and 3 of the offset swap places.  The B operand
+// that meets these rows comes straight from transposed score registers,
+// where lane half hh holds keys 4hh..4hh+3 and 8+4hh..8+4hh+3 of each 16-key
+// step in its eight k slots; with this order those eight keys are one
+// 16-byte run of the row.
+__host__ __device__ constexpr int vt_pos(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
+
+// The pre-pass: dst[b, hk, d, tile*64 + vt_pos(j)] = src[b, hk, tile*64 + j, d]
+// for real keys and 0 for every other position of the padded key range
+// (past Skv, or not valid under the mask), so copies of these tiles need no
+// per-row selection and masked keys meet zeros.  Under TTT only the step-0
+// keys are real here (the tile loops walk those; the later steps' keys are
+// taken one per row).  A block converts one (b, hk, tile) at a time,
+// striding over all of them, `ntile` tiles per (b, hk); rows of dst hold
+// dst_ss keys.
+template <int D>
+__global__ void __launch_bounds__(256) transpose_keys_kernel(Params p, Tensor src, bf16* dst, int64_t dst_ss,
+                                                             int ntile, int64_t nblk) {
+  constexpr int TK = kVtTile;
+  constexpr int CPR = D / 8;
+  __shared__ bf16 tile[TK][D + 8];
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int t = (int)(blk % ntile), bh = (int)(blk / ntile);
+    const int b = bh / p.Hkv, hk = bh % p.Hkv;
+    MaskB m = resolve_mask(p, b);
+    if (m.kind == MASK_TTT) {
+      m.kind = MASK_CAUSAL;
+      m.Skv = min(m.Skv, m.L);
+    }
+    const bf16* Xg = static_cast<const bf16*>(src.ptr) + b * src.sb + hk * src.sh;
+    __syncthreads();   // the previous tile's reads of `tile` are done
+    for (int i = threadIdx.x; i < TK * CPR; i += 256) {
+      const int r = i / CPR, c = i % CPR, j = t * TK + r;
+      bf16x8 x = {};
+      if (key_valid(m, j)) x = *reinterpret_cast<const bf16x8*>(Xg + (int64_t)j * src.ss + 8 * c);
+      *reinterpret_cast<bf16x8*>(&tile[r][8 * c]) = x;
+    }
+    __syncthreads();
+    bf16* Xt = dst + (int64_t)bh * D * dst_ss + (int64_t)t * TK;
+    for (int i = threadIdx.x; i < D * (TK / 8); i += 256) {
+      const int d = i / (TK / 8), c = i % (TK / 8);
+      bf16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = tile[vt_pos(8 * c + e)][d];
+      *reinterpret_cast<bf16x8*>(Xt + (int64_t)d * dst_ss + 8 * c) = y;
+    }
+  }
+}
+
+// Keys the tile loops walk: all of them, or under TTT the Sq step-0 keys.
+__device__ __host__ __forceinline__ int walk_keys(const Params& p) {
+  return p.mask.kind == MASK_TTT && p.Sq < p.Skv ? p.Sq : p.Skv;
+}
+
+// Launches the pre-pass for the tiles the tile loops read.
+template <int D>
+hipError_t launch_transpose_keys(const Params& p, const Tensor& src, void* dst, int64_t dst_ss, hipStream_t s) {
+  const int ntile = (walk_keys(p) + kVtTile - 1) / kVtTile;
+  const int64_t nblk = (int64_t)p.B * p.Hkv * ntile;
+  if (nblk == 0) return hipSuccess;
+  const unsigned grid = (unsigned)(nblk < (1 << 20) ? nblk : (1 << 20));
+  hipLaunchKernelGGL(transpose_keys_kernel<D>, dim3(grid), dim3(256), 0, s, p, src, static_cast<bf16*>(dst),
+                     dst_ss, ntile, nblk);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
 // Block -> (column, rank).  Workgroup i runs on XCD i % 8; when the number of
 // (batch, head) columns is a multiple of 8, each XCD gets a contiguous run of
 // columns (neighbouring heads share a K/V head, so its L2 serves them all) and

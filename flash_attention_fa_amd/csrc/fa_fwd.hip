@@ -15,9 +15,10 @@
 // lane owns one query column and 32 keys of it: the softmax scale, running
 // max and normaliser are one scalar per lane.  O^T = V^T P^T takes P straight
 // from the score registers and V^T from a transposed copy of V that a small
-// pre-pass writes into the caller's workspace (vt_kernel): 16-byte LDS reads
-// serve it, where the row-major V tile would need transposing reads that
-// move half as many bytes per instruction at about half the rate.
+// pre-pass (transpose_keys_kernel) writes into the caller's workspace:
+// 16-byte LDS reads serve it, where the row-major V tile would need
+// transposing reads that move half as many bytes per instruction at about
+// half the rate.
 //
 // Vector-ALU budget.  At D = 128 a wave's 32 MFMAs per tile take about as long
 // as a few hundred vector instructions, so the exponentials and their
@@ -60,56 +61,6 @@ struct FwdLds {
   static constexpr int VT_BASE = NBUF * TILE_BYTES;
   static constexpr int BYTES = 2 * NBUF * TILE_BYTES;
 };
-
-// V^T row d of a key tile is 64 keys (128 bytes, eight 16-byte chunks);
-// chunk c of row d sits at slot c ^ vt_swz(d), so the 16 rows one 16-lane
-// group of a 16-byte read touches cover all 64 banks.
-__device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 7; }
-
-// Stored position of key tile offset j in a V^T row: within each group of 16
-// keys, bits 2 and 3 of the offset swap places.  The PV product's B operand
-// is P^T straight from the transposed score registers, where lane half hh
-// holds keys 4hh..4hh+3 and 8+4hh..8+4hh+3 of each 16-key step in its eight
-// k slots; with this order those eight keys are one 16-byte run of V^T.
-__host__ __device__ constexpr int vt_pos(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
-
-// V^T pre-pass: vt[b, hk, d, tile*64 + vt_pos(j)] = V[b, hk, tile*64 + j, d]
-// for real keys and 0 for every other position of the padded key range
-// (past Skv, or not valid under the mask), so the forward's copies need no
-// per-row selection and masked keys add 0 * 0.  A block converts one
-// (b, hk, tile) at a time, striding over all of them; `ntile` tiles per
-// (b, hk), the ones the forward's tile walk reads.
-template <int D>
-__global__ void __launch_bounds__(256) vt_kernel(Params p, int ntile, int64_t nblk) {
-  __shared__ bf16 tile[TK][D + 8];
-  constexpr int CPR = D / 8;
-  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-    const int t = (int)(blk % ntile), bh = (int)(blk / ntile);
-    const int b = bh / p.Hkv, hk = bh % p.Hkv;
-    MaskB m = resolve_mask(p, b);
-    if (m.kind == MASK_TTT) {   // the tile walk's view: step-0 keys only
-      m.kind = MASK_CAUSAL;
-      m.Skv = min(m.Skv, m.L);
-    }
-    const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
-    __syncthreads();   // the previous tile's reads of `tile` are done
-    for (int i = threadIdx.x; i < TK * CPR; i += 256) {
-      const int r = i / CPR, c = i % CPR, j = t * TK + r;
-      bf16x8 x = {};
-      if (key_valid(m, j)) x = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)j * p.v.ss + 8 * c);
-      *reinterpret_cast<bf16x8*>(&tile[r][8 * c]) = x;
-    }
-    __syncthreads();
-    bf16* Vt = static_cast<bf16*>(p.vt) + (int64_t)bh * D * p.vt_ss + (int64_t)t * TK;
-    for (int i = threadIdx.x; i < D * (TK / 8); i += 256) {
-      const int d = i / (TK / 8), c = i % (TK / 8);
-      bf16x8 y;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = tile[vt_pos(8 * c + e)][d];
-      *reinterpret_cast<bf16x8*>(Vt + (int64_t)d * p.vt_ss + 8 * c) = y;
-    }
-  }
-}
 
 template <int K>
 struct Buf {
@@ -485,20 +436,12 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   const int nq = (p.Sq + TQ - 1) / TQ;
   const int64_t nblk = (int64_t)p.B * p.Hq * nq;
   if (nblk == 0) return hipSuccess;
-  // V^T of the keys the tile walk reads (under TTT, the step-0 keys only)
-  const int walk_keys = p.mask.kind == MASK_TTT ? std::min(p.Skv, p.Sq) : p.Skv;
-  const int nvtile = (walk_keys + TK - 1) / TK;
-  const int64_t nvt = (int64_t)p.B * p.Hkv * nvtile;
-  if (nvt > 0) {
-    const unsigned grid = (unsigned)std::min<int64_t>(nvt, 1 << 20);
-    hipLaunchKernelGGL(vt_kernel<D>, dim3(grid), dim3(256), 0, stream, p, nvtile, nvt);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  // V^T of the keys the tile walk reads
+  hipError_t e = launch_transpose_keys<D>(p, p.v, p.vt, p.vt_ss, stream);
+  if (e != hipSuccess) return e;
   const int lds = FwdLds<D>::BYTES;
   auto k = p.mask.kind == MASK_TTT ? fwd_kernel<D, NW, true> : fwd_kernel<D, NW, false>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NW * 64), lds, stream, p);
   return hipGetLastError();
