@@ -16,7 +16,7 @@ tests/golden/, invariants, the step-by-step EAGLE3 TTT formulation
 in this package is "parity unpinned".
 """
 from .attention import (  # noqa: F401
-    FULL, CAUSAL, TTT,
+    FULL, CAUSAL, TTT, WINDOW,
     allowed, attention_forward, attention_backward, attention_ref,
     allowed_pair_count,
 )

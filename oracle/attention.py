@@ -21,13 +21,22 @@ Sources, by page and section:
 * "CS336 - LLM Systems", *Flash Attention (Triton)* / *How it works*: the
   fused kernel returns the same result as the explicit
   Q K^T -> softmax -> P V chain; only memory traffic changes.
+* The playbook, section *4. Measurement discipline*: the diffusion trainer's
+  attention geometries include windowed self-attention besides full
+  self-attention and cross-attention.  The page does not define the window;
+  WINDOW here is a band of key positions around the query position (see
+  ``allowed``).
 
 Readings taken where the pages are silent:
   * scale defaults to 1/sqrt(D);
   * LSE is the natural-log logsumexp of the *scaled* scores;
   * CAUSAL with Sq != Skv is top-left aligned: key j allowed iff j <= i - shift;
   * kv_valid[b] masks keys only, every query row is computed;
-  * GQA maps query head h to key/value head h // (Hq / Hkv).
+  * GQA maps query head h to key/value head h // (Hq / Hkv);
+  * WINDOW (left, right): key j allowed iff
+    i - shift - left <= j <= i - shift + right (and j below kv_valid), so
+    (left, 0) is a causal sliding window of left + 1 keys and (w, w) a
+    symmetric band.
 
 The backward is the gradient of  L = sum(O * dO)  (dO is the upstream
 gradient), derived from the softmax Jacobian:
@@ -36,19 +45,21 @@ gradient), derived from the softmax Jacobian:
 """
 import numpy as np
 
-FULL, CAUSAL, TTT = 0, 1, 2
+FULL, CAUSAL, TTT, WINDOW = 0, 1, 2, 3
 
 # Rows of S materialised at a time; only bounds RAM, never splits a row.
 _ROW_BLOCK = 1024
 
 
-def allowed(kind, Sq, Skv, shift=0, kv_valid=None, rows=None):
+def allowed(kind, Sq, Skv, shift=0, kv_valid=None, rows=None, window=None):
     """Boolean [len(rows), Skv] matrix: may query i attend key j?
 
     A literal transcription of the masks on the SpecForge page (*Flex
     Attention* section): FULL is the padding mask alone, CAUSAL is the
     ``causal_mask`` function, TTT is ``or_masks(causal_mask, suffix_mask)``
     with Q_LEN = Sq.  ``kv_valid`` plays the role of ``seq_lengths[b]``.
+    WINDOW (``window`` = (left, right)) is the band
+    i - shift - left <= j <= i - shift + right with the padding mask.
     """
     i = (np.arange(Sq) if rows is None else np.asarray(rows))[:, None]
     j = np.arange(Skv)[None, :]
@@ -63,16 +74,19 @@ def allowed(kind, Sq, Skv, shift=0, kv_valid=None, rows=None):
         q_len = Sq
         suffix = (j >= q_len) & ((j % q_len) < n_valid) & (((j - i) % q_len) == 0)
         return causal | suffix
+    if kind == WINDOW:
+        left, right = window
+        return (j >= i - shift - left) & (j <= i - shift + right) & padding
     raise ValueError(f"unknown mask kind {kind}")
 
 
-def allowed_pair_count(kind, Sq, Skv, shift=0, kv_valid=None):
+def allowed_pair_count(kind, Sq, Skv, shift=0, kv_valid=None, window=None):
     """Number of allowed (i, j) pairs for one (batch, head): the unit in which
     attention work is counted (4 D flop per pair forward, 10 D backward)."""
     total = 0
     for r0 in range(0, Sq, 4096):
         rows = np.arange(r0, min(Sq, r0 + 4096))
-        total += int(allowed(kind, Sq, Skv, shift, kv_valid, rows).sum())
+        total += int(allowed(kind, Sq, Skv, shift, kv_valid, rows, window).sum())
     return total
 
 
@@ -113,7 +127,7 @@ def _row_blocks(Sq, rows):
 
 
 def attention_forward(q, k, v, kind=FULL, shift=0, kv_valid=None, scale=None,
-                      heads=None, rows=None):
+                      heads=None, rows=None, window=None):
     """O [B,Hq,Sq,D] and LSE [B,Hq,Sq] in float64.
 
     ``heads`` (a list of query heads) and ``rows`` (a half-open range
@@ -131,7 +145,7 @@ def attention_forward(q, k, v, kind=FULL, shift=0, kv_valid=None, scale=None,
     LSE = np.full((B, Hq, Sq), np.nan)
     for b in range(B):
         for rb in _row_blocks(Sq, rows):
-            A = allowed(kind, Sq, Skv, shift, kvv[b], rb)
+            A = allowed(kind, Sq, Skv, shift, kvv[b], rb, window)
             for h in hs:
                 g = h // G
                 S = s * (q[b, h, rb] @ k[b, g].T)
@@ -142,7 +156,7 @@ def attention_forward(q, k, v, kind=FULL, shift=0, kv_valid=None, scale=None,
 
 
 def attention_backward(q, k, v, do, kind=FULL, shift=0, kv_valid=None,
-                       scale=None, heads=None, rows=None):
+                       scale=None, heads=None, rows=None, window=None):
     """dQ, dK, dV (float64) of L = sum(O * dO), plus Delta [B,Hq,Sq].
 
     P is rebuilt from the scores, exactly as the definition states; dK and dV
@@ -162,7 +176,7 @@ def attention_backward(q, k, v, do, kind=FULL, shift=0, kv_valid=None,
     Delta = np.full((B, Hq, Sq), np.nan)
     for b in range(B):
         for rb in _row_blocks(Sq, rows):
-            A = allowed(kind, Sq, Skv, shift, kvv[b], rb)
+            A = allowed(kind, Sq, Skv, shift, kvv[b], rb, window)
             for h in hs:
                 g = h // G
                 S = s * (q[b, h, rb] @ k[b, g].T)
@@ -179,9 +193,9 @@ def attention_backward(q, k, v, do, kind=FULL, shift=0, kv_valid=None,
 
 
 def attention_ref(q, k, v, do, kind=FULL, shift=0, kv_valid=None, scale=None,
-                  heads=None, rows=None):
+                  heads=None, rows=None, window=None):
     """Forward and backward together: dict with O, LSE, dQ, dK, dV, Delta."""
-    O, LSE = attention_forward(q, k, v, kind, shift, kv_valid, scale, heads, rows)
+    O, LSE = attention_forward(q, k, v, kind, shift, kv_valid, scale, heads, rows, window)
     dQ, dK, dV, Delta = attention_backward(q, k, v, do, kind, shift, kv_valid,
-                                           scale, heads, rows)
+                                           scale, heads, rows, window)
     return dict(O=O, LSE=LSE, dQ=dQ, dK=dK, dV=dV, Delta=Delta)

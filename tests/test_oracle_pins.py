@@ -13,7 +13,10 @@ or index, a transposed operand, a wrong mask index) fails at least one:
   sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, Delta = rowsum(dO * O));
 * the step-by-step EAGLE3 TTT formulation (oracle/ttt_steps.py);
 * brute force of the SpecForge mask functions, pair by pair;
-* padding equals truncation; padded keys get exactly-zero gradients.
+* padding equals truncation; padded keys get exactly-zero gradients;
+* WINDOW: torch fp64 SDPA and autograd with a band mask built by
+  torch.tril / torch.triu, the limits that reduce it to CAUSAL and FULL,
+  finite differences, the gradient invariants, and pair counts in closed form.
 """
 import json
 import math
@@ -23,7 +26,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (FULL, CAUSAL, TTT, allowed, attention_forward,
+from oracle import (FULL, CAUSAL, TTT, WINDOW, allowed, attention_forward,
                     attention_backward, attention_ref, allowed_pair_count,
                     ttt_stepwise_forward)
 
@@ -131,20 +134,24 @@ FD_CASES = [
     (TTT, 1, 2, 1, 5, 15, 4, 0, None),
     (TTT, 1, 2, 2, 6, 12, 4, 1, (4,)),
     (TTT, 2, 4, 2, 4, 8, 8, 0, (4, 3)),
+    # WINDOW (left, right)
+    (WINDOW, 1, 2, 1, 9, 9, 4, 0, None, (2, 0)),
+    (WINDOW, 2, 4, 2, 8, 11, 4, 1, (11, 6), (1, 3)),
 ]
 
 
 @pytest.mark.parametrize("case", FD_CASES, ids=lambda c: f"k{c[0]}_{c[4]}x{c[5]}")
 def test_backward_matches_finite_differences(case):
-    kind, B, Hq, Hkv, Sq, Skv, D, shift, kvv = case
+    kind, B, Hq, Hkv, Sq, Skv, D, shift, kvv = case[:9]
+    win = case[9] if len(case) > 9 else None
     q = _rand((B, Hq, Sq, D), 11)
     k = _rand((B, Hkv, Skv, D), 12)
     v = _rand((B, Hkv, Skv, D), 13)
     do = _rand((B, Hq, Sq, D), 14)
-    dQ, dK, dV, _ = attention_backward(q, k, v, do, kind, shift, kvv)
+    dQ, dK, dV, _ = attention_backward(q, k, v, do, kind, shift, kvv, window=win)
 
     def loss(q_, k_, v_):
-        O, _ = attention_forward(q_, k_, v_, kind, shift, kvv)
+        O, _ = attention_forward(q_, k_, v_, kind, shift, kvv, window=win)
         return float((O * do).sum())
 
     h = 1e-6
@@ -201,20 +208,21 @@ def test_causal_row_zero_and_key_shift():
     np.testing.assert_allclose(LSE2, LSE + (q @ c) / 4.0, atol=1e-12)
 
 
-@pytest.mark.parametrize("kind,shift,kvv", [(FULL, 0, (7,)), (CAUSAL, 3, None),
-                                            (TTT, 0, (5,)), (TTT, 2, None)])
-def test_gradient_sum_invariants(kind, shift, kvv):
+@pytest.mark.parametrize("kind,shift,kvv,win", [(FULL, 0, (7,), None), (CAUSAL, 3, None, None),
+                                                (TTT, 0, (5,), None), (TTT, 2, None, None),
+                                                (WINDOW, 2, (9,), (2, 1))])
+def test_gradient_sum_invariants(kind, shift, kvv, win):
     B, Hq, Hkv, Sq, D = 1, 4, 2, 8, 8
     Skv = 3 * Sq if kind == TTT else 11
     q = _rand((B, Hq, Sq, D), 40)
     k, v = _rand((B, Hkv, Skv, D), 41), _rand((B, Hkv, Skv, D), 42)
     do = _rand((B, Hq, Sq, D), 43)
-    r = attention_ref(q, k, v, do, kind, shift, kvv)
+    r = attention_ref(q, k, v, do, kind, shift, kvv, window=win)
     # sum_j dS_ij = 0  =>  sum_j dK_j = 0 per (b, kv head)
     np.testing.assert_allclose(r["dK"].sum(axis=2), 0.0, atol=1e-12)
     # sum_j P_ij = 1  =>  sum_j dV_j = sum over non-empty rows of dO_i (per group)
     G = Hq // Hkv
-    nonempty = allowed(kind, Sq, Skv, shift, None if kvv is None else kvv[0]).any(1)
+    nonempty = allowed(kind, Sq, Skv, shift, None if kvv is None else kvv[0], window=win).any(1)
     expect = do[:, :, nonempty].sum(axis=2).reshape(B, Hkv, G, D).sum(axis=2)
     np.testing.assert_allclose(r["dV"].sum(axis=2), expect, atol=1e-12)
     # Delta (defined as sum_j P dP) equals rowsum(dO * O)
@@ -326,3 +334,65 @@ def test_pair_counts_closed_form():
     assert allowed_pair_count(FULL, S, 20, 0, 13) == S * 13
     t = 2
     assert allowed_pair_count(TTT, S, (t + 1) * S) == S * (S + 1) // 2 + t * S
+    # causal window of w + 1 keys: rows i < w see i + 1 keys, the rest w + 1
+    w = 9
+    assert allowed_pair_count(WINDOW, S, S, window=(w, 0)) == w * (w + 1) // 2 + (S - w) * (w + 1)
+    # symmetric band of half-width w: (2w + 1) S minus the two clipped corners
+    assert allowed_pair_count(WINDOW, S, S, window=(w, w)) == (2 * w + 1) * S - w * (w + 1)
+
+
+# --------------------------------------------------------------------------
+# WINDOW
+
+def _band(Sq, Skv, shift, left, right):
+    """Boolean band mask from torch.tril / torch.triu: j - i within
+    [-shift - left, -shift + right]."""
+    ones = torch.ones(Sq, Skv, dtype=torch.bool)
+    return ones.tril(right - shift) & ones.triu(-shift - left)
+
+
+@pytest.mark.parametrize("Hq,Hkv,Sq,Skv,shift,left,right", [
+    (2, 2, 16, 16, 0, 3, 0), (4, 2, 13, 13, 0, 2, 2), (8, 1, 20, 20, 2, 5, 1),
+    (2, 1, 12, 17, 0, 4, 6)])
+def test_window_matches_torch_sdpa_band_mask(Hq, Hkv, Sq, Skv, shift, left, right):
+    B, D = 2, 8
+    q, k, v = _rand((B, Hq, Sq, D), 70), _rand((B, Hkv, Skv, D), 71), _rand((B, Hkv, Skv, D), 72)
+    do = _rand((B, Hq, Sq, D), 73)
+    band = _band(Sq, Skv, shift, left, right)
+    rows = band.any(1).numpy()                    # SDPA gives NaN on empty rows
+    assert rows.sum() >= Sq - shift
+    r = attention_ref(q, k, v, do, WINDOW, shift, window=(left, right))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq[:, :, rows], tk, tv, attn_mask=band[rows], enable_gqa=Hq != Hkv)
+    out.backward(torch.tensor(do[:, :, rows]))
+    np.testing.assert_allclose(r["O"][:, :, rows], out.detach().numpy(), atol=1e-12)
+    assert np.all(r["O"][:, :, ~rows] == 0.0)
+    np.testing.assert_allclose(r["dQ"][:, :, rows], tq.grad.numpy()[:, :, rows], atol=1e-11)
+    for name, t in (("dK", tk), ("dV", tv)):
+        assert np.abs(t.grad.numpy()).max() > 1e-3
+        np.testing.assert_allclose(r[name], t.grad.numpy(), atol=1e-11, err_msg=name)
+
+
+def test_window_limits_are_causal_and_full():
+    B, Hq, Hkv, S, D = 1, 4, 2, 19, 8
+    q, k, v = _rand((B, Hq, S, D), 80), _rand((B, Hkv, S, D), 81), _rand((B, Hkv, S, D), 82)
+    do = _rand((B, Hq, S, D), 83)
+    for shift in (0, 2):
+        a = attention_ref(q, k, v, do, WINDOW, shift, (15,), window=(S, 0))
+        c = attention_ref(q, k, v, do, CAUSAL, shift, (15,))
+        for name in a:
+            np.testing.assert_array_equal(a[name], c[name], err_msg=name)
+    a = attention_ref(q, k, v, do, WINDOW, 0, (11,), window=(S, S))
+    f = attention_ref(q, k, v, do, FULL, 0, (11,))
+    for name in a:
+        np.testing.assert_array_equal(a[name], f[name], err_msg=name)
+
+
+def test_window_predicate_brute_force():
+    Sq, Skv, shift, left, right, seq = 9, 13, 1, 2, 3, 11
+    A = allowed(WINDOW, Sq, Skv, shift, seq, window=(left, right))
+    for i in range(Sq):
+        for j in range(Skv):
+            expect = (i - shift - left <= j <= i - shift + right) and j < seq
+            assert A[i, j] == expect, (i, j)
