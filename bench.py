@@ -71,6 +71,12 @@ def pair_count(w):
         if w.kind == W.FULL:
             out.append(w.Sq * kvv)
             continue
+        if w.kind == W.WINDOW:
+            left, right = w.window
+            lo = np.clip(i - w.shift - left, 0, kvv)
+            hi = np.clip(i - w.shift + right + 1, 0, kvv)
+            out.append(int(np.maximum(hi - lo, 0).sum()))
+            continue
         causal = int(np.clip(i - w.shift + 1, 0, kvv).sum())
         if w.kind == W.CAUSAL:
             out.append(causal)
@@ -165,7 +171,7 @@ def cpu_baseline(w, q, k, v, do, nheads):
     args = [x[:1].double().numpy() for x in (q, k, v, do)]
     t0 = time.perf_counter()
     attention_ref(*args, w.kind, w.shift, None if kvv is None else kvv[:1], w.scale,
-                  heads=list(range(nheads)))
+                  heads=list(range(nheads)), window=w.window)
     sec = time.perf_counter() - t0
     pairs = pair_count(w)[0] * nheads
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -197,7 +203,8 @@ def measure(fa, w, dev, steps, warmup, inputs):
     ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(qg, kg)), dtype=torch.uint8, device=dev)
     fws = torch.empty(max(1, fa.fa_fwd_workspace_bytes(qg, kg)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    kw = dict(mask_kind=w.kind, causal_shift=w.shift, kv_valid=kvv, scale=w.scale, stream=stream)
+    kw = dict(mask_kind=w.kind, causal_shift=w.shift, kv_valid=kvv, scale=w.scale, window=w.window,
+              stream=stream)
 
     def fwd():
         fa.fa_fwd(qg, kg, vg, out=o, lse=lse, workspace=fws, **kw)

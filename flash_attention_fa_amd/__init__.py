@@ -16,10 +16,12 @@ that saves (O, LSE) for the backward.
 
 Tensors are logical [B, H, S, D] (any strides with unit stride in D): q is
 [B, Hq, Sq, D], k and v are [B, Hkv, Skv, D] with Hq a multiple of Hkv.
-Mask kinds: ``FULL``, ``CAUSAL`` (key j <= query i - causal_shift) and
+Mask kinds: ``FULL``, ``CAUSAL`` (key j <= query i - causal_shift),
 ``TTT`` (EAGLE3 training-time test: Skv = n * Sq, causal over the step-0 keys
-plus the key at the query's own position in each later step).  ``kv_valid``
-is an optional int32 device tensor [B] of valid key counts.
+plus the key at the query's own position in each later step) and ``WINDOW``
+(``window=(left, right)``: i - causal_shift - left <= j <= i - causal_shift +
+right).  ``kv_valid`` is an optional int32 device tensor [B] of valid key
+counts.
 """
 import math
 
@@ -27,13 +29,13 @@ import torch
 
 from . import _lib
 from ._lib import (FAError, FA_BF16, FA_F32, FA_MASK_FULL, FA_MASK_CAUSAL,  # noqa: F401
-                   FA_MASK_TTT, FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ)
+                   FA_MASK_TTT, FA_MASK_WINDOW, FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ)
 
-FULL, CAUSAL, TTT = FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_TTT
+FULL, CAUSAL, TTT, WINDOW = FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_TTT, FA_MASK_WINDOW
 
 __all__ = ["fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes",
            "fa_last_error", "FA_BWD_DELTA", "FA_BWD_DKDV", "FA_BWD_DQ",
-           "attention", "FAError", "FULL", "CAUSAL", "TTT"]
+           "attention", "FAError", "FULL", "CAUSAL", "TTT", "WINDOW"]
 
 
 def _dtype_code(t):
@@ -52,13 +54,16 @@ def _tensor(t):
     return _lib.fa_tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
-def _mask(kind, causal_shift, kv_valid):
+def _mask(kind, causal_shift, kv_valid, window=None):
     ptr = None
     if kv_valid is not None:
         if kv_valid.dtype != torch.int32 or not kv_valid.is_contiguous():
             raise FAError(_lib.FA_ERR_INVALID_ARG, "kv_valid must be a contiguous int32 tensor")
         ptr = kv_valid.data_ptr()
-    return _lib.fa_mask_desc(int(kind), int(causal_shift), ptr)
+    if int(kind) == WINDOW and window is None:
+        raise FAError(_lib.FA_ERR_INVALID_ARG, "mask_kind WINDOW needs window=(left, right)")
+    left, right = (0, 0) if window is None else (int(window[0]), int(window[1]))
+    return _lib.fa_mask_desc(int(kind), int(causal_shift), ptr, left, right)
 
 
 def _stream(t, stream):
@@ -88,7 +93,7 @@ def fa_fwd_workspace_bytes(q, k):
     return int(_lib.lib().fa_fwd_workspace_bytes(_fwd_shape_args(q, k)))
 
 
-def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None,
+def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=None, scale=None,
            out=None, lse=None, workspace=None, stream=None):
     """Forward attention.  Returns (O [B,Hq,Sq,D] in q's dtype, LSE [B,Hq,Sq] fp32).
 
@@ -103,7 +108,7 @@ def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None
     a.scale = 0.0 if scale is None else float(scale)
     a.q, a.k, a.v, a.o = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
     a.lse = lse.data_ptr()
-    a.mask = _mask(mask_kind, causal_shift, kv_valid)
+    a.mask = _mask(mask_kind, causal_shift, kv_valid, window)
     for t in (k, v, out):
         if t.dtype != q.dtype:
             raise FAError(_lib.FA_ERR_INVALID_ARG, "q, k, v and out must share one dtype")
@@ -115,7 +120,7 @@ def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None
     return out, lse
 
 
-def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale):
+def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window=None):
     B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
     a = _lib.fa_bwd_args()
     a.dtype = _dtype_code(q)
@@ -125,7 +130,7 @@ def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_val
     a.lse = None if lse is None else lse.data_ptr()
     if dq is not None:
         a.dq, a.dk, a.dv = _tensor(dq), _tensor(dk), _tensor(dv)
-    a.mask = _mask(mask_kind, causal_shift, kv_valid)
+    a.mask = _mask(mask_kind, causal_shift, kv_valid, window)
     return a
 
 
@@ -135,11 +140,11 @@ def fa_bwd_workspace_bytes(q, k, *, mask_kind=FULL):
     B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
     a.dtype = _dtype_code(q)
     a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
-    a.mask = _lib.fa_mask_desc(int(mask_kind), 0, None)
+    a.mask = _lib.fa_mask_desc(int(mask_kind), 0, None, 0, 0)
     return int(_lib.lib().fa_bwd_workspace_bytes(a))
 
 
-def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=None,
+def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=None,
            scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Backward attention.  Returns (dQ, dK, dV) in q's dtype."""
     if dq is None:
@@ -148,7 +153,7 @@ def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=No
         dk = torch.empty_like(k, memory_format=torch.contiguous_format)
     if dv is None:
         dv = torch.empty_like(v, memory_format=torch.contiguous_format)
-    a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale)
+    a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window)
     need = int(_lib.lib().fa_bwd_workspace_bytes(a))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -159,13 +164,13 @@ def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=No
 
 
 def fa_bwd_stage(stage, q, k, v, o, lse, dout, dq, dk, dv, workspace, *, mask_kind=FULL,
-                 causal_shift=0, kv_valid=None, scale=None, stream=None):
+                 causal_shift=0, kv_valid=None, window=None, scale=None, stream=None):
     """One stage (FA_BWD_DELTA, FA_BWD_DKDV or FA_BWD_DQ) of ``fa_bwd``.
 
     The caller provides the outputs and the workspace; DKDV and DQ read the
     Delta that a DELTA stage left in ``workspace``.
     """
-    a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale)
+    a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window)
     _lib.check(_lib.lib().fa_bwd_stage(a, int(stage), workspace.data_ptr(),
                                        workspace.numel() * workspace.element_size(),
                                        _stream(q, stream)))
@@ -177,30 +182,31 @@ def fa_last_error():
 
 class _Attention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, mask_kind, causal_shift, kv_valid, scale):
+    def forward(ctx, q, k, v, mask_kind, causal_shift, kv_valid, scale, window):
         o, lse = fa_fwd(q, k, v, mask_kind=mask_kind, causal_shift=causal_shift,
-                        kv_valid=kv_valid, scale=scale)
+                        kv_valid=kv_valid, window=window, scale=scale)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.cfg = (mask_kind, causal_shift, kv_valid, scale)
+        ctx.cfg = (mask_kind, causal_shift, kv_valid, scale, window)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        mask_kind, causal_shift, kv_valid, scale = ctx.cfg
+        mask_kind, causal_shift, kv_valid, scale, window = ctx.cfg
         if do.stride(-1) != 1:
             do = do.contiguous()
-        dq, dk, dv = fa_bwd(q, k, v, o, lse, do, mask_kind=mask_kind,
-                            causal_shift=causal_shift, kv_valid=kv_valid, scale=scale)
-        return dq, dk, dv, None, None, None, None
+        dq, dk, dv = fa_bwd(q, k, v, o, lse, do, mask_kind=mask_kind, causal_shift=causal_shift,
+                            kv_valid=kv_valid, window=window, scale=scale)
+        return dq, dk, dv, None, None, None, None, None
 
 
-def attention(q, k, v, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None):
+def attention(q, k, v, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None, window=None):
     """Fused attention O = softmax(scale q k^T + mask) v, differentiable.
 
-    ``scale`` defaults to 1/sqrt(D).  Saves only O and LSE for the backward.
+    ``scale`` defaults to 1/sqrt(D); ``window`` = (left, right) for WINDOW.
+    Saves only O and LSE for the backward.
     """
-    return _Attention.apply(q, k, v, mask_kind, causal_shift, kv_valid, scale)
+    return _Attention.apply(q, k, v, mask_kind, causal_shift, kv_valid, scale, window)
 
 
 def default_scale(D):

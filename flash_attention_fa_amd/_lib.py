@@ -23,6 +23,7 @@ FA_F32 = 1
 FA_MASK_FULL = 0
 FA_MASK_CAUSAL = 1
 FA_MASK_TTT = 2
+FA_MASK_WINDOW = 3
 
 EXPORTED = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes",
             "fa_last_error")
@@ -38,7 +39,8 @@ class fa_tensor(ctypes.Structure):
 
 class fa_mask_desc(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("causal_shift", ctypes.c_int32),
-                ("kv_valid", ctypes.c_void_p)]
+                ("kv_valid", ctypes.c_void_p), ("window_left", ctypes.c_int32),
+                ("window_right", ctypes.c_int32)]
 
 
 _SHAPE = [("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("Hq", ctypes.c_int32),

@@ -71,8 +71,11 @@ fa_status check_shape(const Shape& s, const fa_mask_desc& m) {
     return fail(FA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", s.Hq, s.Hkv);
   if (s.D != 16 && s.D != 32 && s.D != 64 && s.D != 128)
     return fail(FA_ERR_UNSUPPORTED, "head dim D=%d not in {16, 32, 64, 128}", s.D);
-  if (m.kind != FA_MASK_FULL && m.kind != FA_MASK_CAUSAL && m.kind != FA_MASK_TTT)
+  if (m.kind != FA_MASK_FULL && m.kind != FA_MASK_CAUSAL && m.kind != FA_MASK_TTT &&
+      m.kind != FA_MASK_WINDOW)
     return fail(FA_ERR_UNSUPPORTED, "unknown mask kind %d", m.kind);
+  if (m.kind == FA_MASK_WINDOW && (m.window_left < 0 || m.window_right < 0))
+    return fail(FA_ERR_INVALID_ARG, "negative window (left %d, right %d)", m.window_left, m.window_right);
   if (m.causal_shift < 0)
     return fail(FA_ERR_INVALID_ARG, "negative causal_shift %d", m.causal_shift);
   if (m.kind == FA_MASK_TTT) {
@@ -143,6 +146,8 @@ void fill_common(fa::Params& p, const Shape& s, float scale, const fa_mask_desc&
   p.mask.kind = m.kind;
   p.mask.shift = m.causal_shift;
   p.mask.kv_valid = m.kv_valid;
+  p.mask.wl = m.kind == FA_MASK_WINDOW ? m.window_left : 0;
+  p.mask.wr = m.kind == FA_MASK_WINDOW ? m.window_right : 0;
 }
 
 // One float32 [B, Hq, Sq] array, rounded up to 256 bytes.
@@ -151,12 +156,14 @@ size_t row_array_bytes(const Shape& s) {
   return (n + 255) / 256 * 256;
 }
 
-// The dK/dV kernel's partial sums (bf16, D >= 32): two halves of float32
-// dK^T and dV^T, [2][2][B, Hkv, keys, D], rounded up to 256 bytes, over the
-// keys the tile kernel owns (all Skv, or under TTT the Sq step-0 keys).
+// The dK/dV kernel's partial sums (bf16, D >= 32, when it splits its key
+// blocks, fa::dkdv_split): two halves of float32 dK^T and dV^T,
+// [2][2][B, Hkv, keys, D], rounded up to 256 bytes, over the keys the tile
+// kernel owns (all Skv, or under TTT the Sq step-0 keys).
 size_t part_bytes(const Shape& s, int kind) {
   if (s.dtype != FA_BF16 || s.D < 32) return 0;
   const int keys = kind == FA_MASK_TTT && s.Sq < s.Skv ? s.Sq : s.Skv;
+  if (!fa::dkdv_split(std::max(s.B, 0), std::max(s.Hkv, 0), std::max(keys, 0))) return 0;
   size_t n = (size_t)4 * std::max(s.B, 0) * (size_t)std::max(s.Hkv, 0) * (size_t)std::max(keys, 0) *
              (size_t)s.D * 4;
   return (n + 255) / 256 * 256;

@@ -297,13 +297,14 @@ struct DqDma {
   static constexpr int BYTES = DQ_NBUF * BUF;
 };
 
-// TTT: instantiated for the EAGLE3 mask.  As in the forward, both instances
-// walk FULL or CAUSAL tiles only (the TTT instance its step-0 keys, which the
-// causal mask describes), and the TTT instance adds the single key s*L + i of
-// each later step s to row i's dQ with vector arithmetic (ttt_fold).
-template <int D, int NW, bool TTT>
+// MK: the mask-kind instance.  As in the forward, the MK_TTT tile loop walks
+// the step-0 keys, which the causal mask describes, and adds the single key
+// s*L + i of each later step s to row i's dQ with vector arithmetic
+// (ttt_fold).
+template <int D, int NW, int MK>
 __global__ void __launch_bounds__(NW * 64, 2)
 dq_dma_kernel(Params p) {
+  constexpr bool TTT = MK == MK_TTT;
   using L = DqDma<D>;
   constexpr int TQ = NW * 32;
   constexpr int TK = DQ_TK;
@@ -328,8 +329,7 @@ dq_dma_kernel(Params p) {
   const int b = col / p.Hq, h = col % p.Hq, hk = h / p.G;
   const int qtile = p.mask.kind == MASK_FULL ? rank : nq - 1 - rank;
   MaskB m = resolve_mask(p, b);
-  m.kind = !TTT && m.kind == MASK_FULL ? MASK_FULL : MASK_CAUSAL;
-  if (TTT) m.Skv = min(m.Skv, m.L);
+  set_instance_kind<MK>(m);
   const int qa = qtile * TQ, qb = min(p.Sq, qa + TQ);
   const int wa = qa + wave * 32, wb = min(p.Sq, wa + 32);
   const int qi = wa + l32;
@@ -550,11 +550,12 @@ dq_dma_kernel(Params p) {
 // Two waves share each 32-key block: wave w takes key block w % NKB and the
 // (w / NKB)-th 32-row half of every 64-row query tile, so a SIMD runs two
 // waves and one hides the other's latency.  K^T stays in registers and V^T
-// is read from an LDS copy of the workgroup's V rows (this kernel serves
-// D = 16; wider heads take dkdv_split_kernel).  Each query tile is staged row-major and transposed, so
-// every MFMA operand is one 16-byte LDS read.  At the end the second
-// wave of each pair hands its partial dK/dV to the first through LDS, which
-// adds it to its own (always in that order) and writes the result.
+// is read from an LDS copy of the workgroup's V rows.  Each query tile is
+// staged row-major and transposed, so every MFMA operand is one 16-byte LDS
+// read.  At the end the second wave of each pair hands its partial dK/dV to
+// the first through LDS, which adds it to its own (always in that order) and
+// writes the result.  This kernel serves D = 16; wider heads take
+// dkdv_split_kernel.
 constexpr int KV_TQ = 64;
 
 template <int D, int NKB>
@@ -829,12 +830,14 @@ dkdv_kernel(Params p) {
 //
 // 256 keys per workgroup let each staged query row serve twice the matrix
 // work of a 128-key block (the copies into LDS are the kernel's costliest
-// non-matrix work); splitting each key block's steps between two workgroups
-// keeps enough workgroups to balance the causal triangle (the halves are the
-// two halves of the group's heads, or of the steps when the group is odd).
-// Each half writes its float32 sums to the workspace and dkdv_reduce_kernel
-// adds the two halves, always half 0 + half 1, so reruns are bitwise
-// identical.
+// non-matrix work).  With fewer than 1024 such blocks (dkdv_split), each
+// block's steps are split between two workgroups, which keeps enough
+// workgroups to balance the causal triangle (the halves are the two halves
+// of the group's heads, or of the steps when the group is odd); each half
+// writes its float32 sums to the workspace and dkdv_reduce_kernel adds the
+// two halves, always half 0 + half 1, so reruns are bitwise identical.
+// With more blocks one workgroup takes every step of its block and writes
+// dK and dV directly.
 template <int D>
 struct KvSplit {
   static constexpr int NW = 8;
@@ -846,7 +849,11 @@ struct KvSplit {
   static constexpr int BYTES = 2 * STAGE + VB;
 };
 
-template <int D>
+// MK: MK_FC (FULL, CAUSAL and TTT's step-0 keys) or MK_WIN.  SPLIT: two
+// workgroups per key block, each writing float32 partial sums (see
+// dkdv_split); without it one workgroup takes every step of its block and
+// writes dK, dV.
+template <int D, int MK, bool SPLIT>
 __global__ void __launch_bounds__(512)
 dkdv_split_kernel(Params p) {
   using L = KvSplit<D>;
@@ -859,8 +866,8 @@ dkdv_split_kernel(Params p) {
   constexpr int VINS = TKW / RPI;       // copy instructions for the V rows
   constexpr int VLPW = VINS / NW;
   constexpr int ROW16 = 16 * 2 * D;     // bytes of 16 rows
-  static_assert(D >= 32 && QLPW * NW == 2 * QINS && QINS % QLPW == 0 && VLPW * NW == VINS,
-                "copy split");
+  static_assert(D >= 32 && QLPW * NW == 2 * QINS && QINS % QLPW == 0 && VLPW * NW == VINS &&
+                TKW == kDkdvKeys, "copy split");
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* const Vs = smem + 2 * L::STAGE;
 
@@ -874,11 +881,11 @@ dkdv_split_kernel(Params p) {
   const int nkeys = walk_keys(p);
   const int nkt = (nkeys + TKW - 1) / TKW;
   int col, rank;
-  map_block(blockIdx.x, p.B * p.Hkv * 2, nkt, col, rank);
-  const int half = col & 1, bh = col >> 1;
+  map_block(blockIdx.x, p.B * p.Hkv * (SPLIT ? 2 : 1), nkt, col, rank);
+  const int half = SPLIT ? col & 1 : 0, bh = SPLIT ? col >> 1 : col;
   const int b = bh / p.Hkv, hk = bh % p.Hkv;
   MaskB m = resolve_mask(p, b);
-  m.kind = m.kind == MASK_FULL ? MASK_FULL : MASK_CAUSAL;
+  set_instance_kind<MK>(m);
   m.Skv = nkeys;
   const int ka = rank * TKW, kbnd = min(nkeys, ka + TKW);
   const int kw = ka + wave * 32, kwe = min(nkeys, kw + 32);
@@ -917,13 +924,15 @@ dkdv_split_kernel(Params p) {
   // tiles at about the same time).  With an even group each half takes half
   // of the heads over every tile (each Q/dO tile is then read by one half
   // only, on one XCD); with an odd one, half of the steps in that order.
+  // Without SPLIT the one workgroup takes them all.
   const int ntile = t_last - t_first;
-  const bool by_head = (p.G & 1) == 0;
+  const bool by_head = SPLIT && (p.G & 1) == 0;
   const int hbeg = by_head ? half * (p.G / 2) : 0;
   const int hend = by_head ? hbeg + p.G / 2 : p.G;
   const int nall = ntile * p.G;
   const int s0 = by_head || half == 0 ? 0 : (nall + 1) / 2;
-  const int nsteps = by_head ? ntile * (p.G / 2) : (half == 0 ? (nall + 1) / 2 : nall - (nall + 1) / 2);
+  const int nsteps = !SPLIT ? nall
+                   : by_head ? ntile * (p.G / 2) : (half == 0 ? (nall + 1) / 2 : nall - (nall + 1) / 2);
 
   // Waves 0..NW/2-1 copy the Q rows, the others the dO rows (a run of QLPW
   // 1 KB copies each); LSE*log2(e) and Delta come through wave 0's registers.
@@ -1085,6 +1094,27 @@ dkdv_split_kernel(Params p) {
     advance(nxt);
   }
 
+  // Without SPLIT: dK = scale * dK^T sums, dV = dV^T sums, rounded to bf16;
+  // lane (key, hh) holds d = 32c + 8g + 4hh + u.  Keys no query attends
+  // hold exact zeros (every product added 0).
+  if (!SPLIT) {
+    if (key < nkeys) {
+      bf16* DK = static_cast<bf16*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh + (int64_t)key * p.dk.ss;
+      bf16* DV = static_cast<bf16*>(const_cast<void*>(p.dv.ptr)) + b * p.dv.sb + hk * p.dv.sh + (int64_t)key * p.dv.ss;
+      const float sc = p.scale;
+#pragma unroll
+      for (int c = 0; c < NDB; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * c + 8 * g + 4 * hh;
+          *reinterpret_cast<bf16x4*>(DK + d) = to_bf16x4(dka[c][4 * g] * sc, dka[c][4 * g + 1] * sc,
+                                                         dka[c][4 * g + 2] * sc, dka[c][4 * g + 3] * sc);
+          *reinterpret_cast<bf16x4*>(DV + d) = to_bf16x4(dva[c][4 * g], dva[c][4 * g + 1], dva[c][4 * g + 2],
+                                                         dva[c][4 * g + 3]);
+        }
+    }
+    return;
+  }
   // This half's sums dK^T / dV^T as float32 rows of the workspace (unscaled);
   // lane (key, hh) holds d = 32c + 8g + 4hh + u.
   if (key < nkeys) {
@@ -1217,15 +1247,20 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     if (stage == STAGE_DKDV) {
       using LD = KvSplit<D>;
       const int nkeys = walk_keys(p);
-      const int64_t nblk = (int64_t)p.B * p.Hkv * 2 * ((nkeys + LD::TKW - 1) / LD::TKW);
+      const bool split = dkdv_split(p.B, p.Hkv, nkeys);
+      const int64_t nblk = (int64_t)p.B * p.Hkv * (split ? 2 : 1) * ((nkeys + LD::TKW - 1) / LD::TKW);
       if (nblk > 0) {
-        auto k = dkdv_split_kernel<D>;
+        const bool win = p.mask.kind == MASK_WINDOW;
+        auto k = split ? (win ? dkdv_split_kernel<D, MK_WIN, true> : dkdv_split_kernel<D, MK_FC, true>)
+                       : (win ? dkdv_split_kernel<D, MK_WIN, false> : dkdv_split_kernel<D, MK_FC, false>);
         if ((e = set_lds(k, LD::BYTES)) != hipSuccess) return e;
         hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(LD::NW * 64), LD::BYTES, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int64_t n8 = (int64_t)p.B * p.Hkv * nkeys * D / 8;
-        hipLaunchKernelGGL(dkdv_reduce_kernel<D>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (split) {
+          const int64_t n8 = (int64_t)p.B * p.Hkv * nkeys * D / 8;
+          hipLaunchKernelGGL(dkdv_reduce_kernel<D>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p);
+          if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
       }
       const int64_t nlate = (int64_t)p.B * p.Hkv * (p.Skv - nkeys);
       if (p.mask.kind == MASK_TTT && nlate > 0) {
@@ -1249,9 +1284,11 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     // 8-wave workgroups when there are enough to fill the chip twice over
     const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
     if constexpr (D >= 32) {
-      const bool ttt = p.mask.kind == MASK_TTT;
-      auto k = wg8 >= 512 ? (ttt ? dq_dma_kernel<D, 8, true> : dq_dma_kernel<D, 8, false>)
-                          : (ttt ? dq_dma_kernel<D, 4, true> : dq_dma_kernel<D, 4, false>);
+      const int mk = mask_instance(p.mask.kind);
+      auto k = wg8 >= 512 ? (mk == MK_TTT ? dq_dma_kernel<D, 8, MK_TTT>
+                                          : (mk == MK_WIN ? dq_dma_kernel<D, 8, MK_WIN> : dq_dma_kernel<D, 8, MK_FC>))
+                          : (mk == MK_TTT ? dq_dma_kernel<D, 4, MK_TTT>
+                                          : (mk == MK_WIN ? dq_dma_kernel<D, 4, MK_WIN> : dq_dma_kernel<D, 4, MK_FC>));
       const int nw = wg8 >= 512 ? 8 : 4;
       const int64_t nblk = (int64_t)p.B * p.Hq * ((p.Sq + nw * 32 - 1) / (nw * 32));
       if ((e = set_lds(k, DqDma<D>::BYTES)) != hipSuccess) return e;

@@ -31,7 +31,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define FA_LDS(T, p) ((T __attribute__((address_space(3)))*)(p))
 
-enum { MASK_FULL = 0, MASK_CAUSAL = 1, MASK_TTT = 2 };
+enum { MASK_FULL = 0, MASK_CAUSAL = 1, MASK_TTT = 2, MASK_WINDOW = 3 };
 enum { TILE_SKIP = 0, TILE_FULL = 1, TILE_PART = 2 };
 
 constexpr float kLn2 = 0.6931471805599453f;
@@ -237,15 +237,23 @@ __device__ __forceinline__ void barrier_lds() {
 
 struct MaskB {
   int kind, shift, Sq, Skv, L, kvv;  // L = Sq (TTT step length); kvv clamped
+  int wl, wr;                        // WINDOW band: keys before / after the diagonal
 };
 
+// Shift and window are clamped to 2 (Sq + Skv): past that the predicate no
+// longer changes (a larger shift already leaves every row empty, a wider
+// window already covers every key), and the band arithmetic stays far from
+// int overflow.
 __device__ __forceinline__ MaskB resolve_mask(const Params& p, int b) {
   MaskB m;
+  const int lim = 2 * (p.Sq + p.Skv);
   m.kind = p.mask.kind;
-  m.shift = p.mask.shift;
+  m.shift = min(p.mask.shift, lim);
   m.Sq = p.Sq;
   m.Skv = p.Skv;
   m.L = p.Sq;
+  m.wl = min(p.mask.wl, lim);
+  m.wr = min(p.mask.wr, lim);
   const int cap = p.mask.kind == MASK_TTT ? p.Sq : p.Skv;
   int v = p.mask.kv_valid ? p.mask.kv_valid[b] : cap;
   m.kvv = v < 0 ? 0 : (v > cap ? cap : v);
@@ -258,6 +266,10 @@ __device__ __forceinline__ MaskB resolve_mask(const Params& p, int b) {
 __device__ __forceinline__ bool allowed(const MaskB& m, int i, int j) {
   const bool valid = j < m.kvv;
   if (m.kind == MASK_FULL) return valid;
+  if (m.kind == MASK_WINDOW) {
+    const int d = j - (i - m.shift);   // offset from the shifted diagonal
+    return (d >= -m.wl) & (d <= m.wr) & valid;
+  }
   const bool causal = (j <= i - m.shift) & valid;
   if (m.kind == MASK_CAUSAL) return causal;
   // TTT suffix: key of a later step at the query's own position (keys past
@@ -297,8 +309,8 @@ __device__ __forceinline__ void segment_tiles(const MaskB& m, int s, int qa, int
                                               int& t0, int& t1) {
   int lo, hi;
   if (s == 0) {
-    lo = 0;
-    hi = m.kind == MASK_FULL ? m.kvv : min(m.kvv, qb - m.shift);
+    lo = m.kind == MASK_WINDOW ? max(0, qa - m.shift - m.wl) : 0;
+    hi = m.kind == MASK_FULL ? m.kvv : min(m.kvv, qb - m.shift + (m.kind == MASK_WINDOW ? m.wr : 0));
   } else {
     lo = s * m.L + qa;
     hi = s * m.L + min(qb, m.kvv);
@@ -313,6 +325,13 @@ __device__ __forceinline__ void segment_tiles(const MaskB& m, int s, int qa, int
 __device__ __forceinline__ int rect_state(const MaskB& m, int k0, int k1, int qa, int qb) {
   if (qb <= qa || k1 <= k0) return TILE_SKIP;
   if (m.kind == MASK_FULL) return k1 <= m.kvv ? TILE_FULL : (k0 < m.kvv ? TILE_PART : TILE_SKIP);
+  if (m.kind == MASK_WINDOW) {
+    // the rows' bands [i - shift - wl, i - shift + wr] move by one key per
+    // row, so together they cover [qa - shift - wl, qb - 1 - shift + wr]
+    const bool w_any = (k0 <= qb - 1 - m.shift + m.wr) && (k1 - 1 >= qa - m.shift - m.wl) && (k0 < m.kvv);
+    const bool w_all = (k0 >= qb - 1 - m.shift - m.wl) && (k1 - 1 <= qa - m.shift + m.wr) && (k1 <= m.kvv);
+    return w_all ? TILE_FULL : (w_any ? TILE_PART : TILE_SKIP);
+  }
   const bool c_any = (k0 <= qb - 1 - m.shift) && (k0 < m.kvv);
   const bool c_all = (k1 - 1 <= qa - m.shift) && (k1 <= m.kvv);
   if (m.kind == MASK_CAUSAL) return c_all ? TILE_FULL : (c_any ? TILE_PART : TILE_SKIP);
@@ -333,6 +352,7 @@ __device__ __forceinline__ int rect_state(const MaskB& m, int k0, int k1, int qa
 // full (keys below kv_valid and, unless FULL, at most qa - shift): tiles
 // [0, result) need neither classification nor a mask for rows >= qa.
 __device__ __forceinline__ int full_tiles_below(const MaskB& m, int qa, int TK) {
+  if (m.kind == MASK_WINDOW) return 0;   // a band has no fully visible prefix in general
   int lim = m.kvv;
   if (m.kind != MASK_FULL) lim = min(lim, qa - m.shift + 1);
   return lim > 0 ? lim / TK : 0;
@@ -348,6 +368,15 @@ __device__ __forceinline__ void query_hull(const MaskB& m, int k0, int k1, int& 
   lo = m.Sq; hi = 0;
   if (m.kind == MASK_FULL) {
     if (k0 < m.kvv) { lo = 0; hi = m.Sq; }
+    return;
+  }
+  if (m.kind == MASK_WINDOW) {
+    // rows i whose band meets [k0, k1): k0 + shift - wr <= i <= k1 - 1 + shift + wl
+    if (k0 < m.kvv && k0 < k1) {
+      lo = max(0, k0 + m.shift - m.wr);
+      hi = min(m.Sq, k1 + m.shift + m.wl);
+      if (hi < lo) { lo = m.Sq; hi = 0; }
+    }
     return;
   }
   if (k0 < m.kvv) { lo = min(m.Sq, max(0, k0 + m.shift)); hi = m.Sq; }
@@ -441,6 +470,26 @@ __global__ void __launch_bounds__(256) transpose_keys_kernel(Params p, Tensor sr
       for (int e = 0; e < 8; ++e) y[e] = tile[vt_pos(8 * c + e)][d];
       *reinterpret_cast<bf16x8*>(Xt + (int64_t)d * dst_ss + 8 * c) = y;
     }
+  }
+}
+
+// Mask-kind instances of the tile kernels.  Each instance fixes, visibly to
+// the compiler, which arms of the mask helpers its tile loop can reach:
+// MK_FC FULL or CAUSAL, MK_TTT the causal view of TTT's step-0 keys (the
+// later steps' keys are taken one per row outside the loop), MK_WIN WINDOW.
+enum { MK_FC = 0, MK_TTT = 1, MK_WIN = 2 };
+
+__host__ __device__ __forceinline__ int mask_instance(int kind) {
+  return kind == MASK_TTT ? MK_TTT : (kind == MASK_WINDOW ? MK_WIN : MK_FC);
+}
+
+template <int MK>
+__device__ __forceinline__ void set_instance_kind(MaskB& m) {
+  if constexpr (MK == MK_WIN) {
+    m.kind = MASK_WINDOW;
+  } else {
+    m.kind = MK == MK_FC && m.kind == MASK_FULL ? MASK_FULL : MASK_CAUSAL;
+    if constexpr (MK == MK_TTT) m.Skv = min(m.Skv, m.L);
   }
 }
 

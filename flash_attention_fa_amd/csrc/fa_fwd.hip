@@ -67,16 +67,17 @@ struct Buf {
   static constexpr int value = K;
 };
 
-// TTT: instantiated for the EAGLE3 mask.  Its step-0 part (keys below L =
-// Sq) is the causal mask with the same shift and kv_valid, so the tile loop
-// of both instances knows the kind is FULL or CAUSAL (which drops every TTT
-// arm from it).  The keys of steps 1 .. n-1 that row i sees are the single
-// keys s*L + i (when i < kv_valid): instead of a 64-key tile per step that
-// holds one key per row, each lane folds its row's keys into the running
-// max, normaliser and O before the tile loop (ttt_fold).
-template <int D, int NW, bool TTT>
+// MK: the mask-kind instance (MK_FC, MK_TTT, MK_WIN).  TTT's step-0 part
+// (keys below L = Sq) is the causal mask with the same shift and kv_valid,
+// so the MK_TTT tile loop is the causal one.  The keys of steps 1 .. n-1
+// that row i sees are the single keys s*L + i (when i < kv_valid): instead
+// of a 64-key tile per step that holds one key per row, each lane folds its
+// row's keys into the running max, normaliser and O before the tile loop
+// (ttt_fold).
+template <int D, int NW, int MK>
 __global__ void __launch_bounds__(NW * 64, 2)
 fwd_kernel(Params p) {
+  constexpr bool TTT = MK == MK_TTT;
   constexpr int TQ = NW * 32;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;              // rows per 1 KB copy instruction
@@ -99,10 +100,7 @@ fwd_kernel(Params p) {
   const int b = col / p.Hq, h = col % p.Hq, hk = h / p.G;
   const int qtile = p.mask.kind == MASK_FULL ? rank : nq - 1 - rank;
   MaskB m = resolve_mask(p, b);
-  // the tile loop's kind, visibly to the compiler: FULL or CAUSAL (the TTT
-  // instance walks its step-0 keys, which the causal mask describes)
-  m.kind = !TTT && m.kind == MASK_FULL ? MASK_FULL : MASK_CAUSAL;
-  if (TTT) m.Skv = min(m.Skv, m.L);
+  set_instance_kind<MK>(m);
 
   const int qa = qtile * TQ, qb = min(p.Sq, qa + TQ);
   const int wa = qa + wave * 32, wb = min(p.Sq, wa + 32);
@@ -188,18 +186,17 @@ fwd_kernel(Params p) {
       zoff[x] = roff[x];
     }
   }
-  const bool ttt = m.kind == MASK_TTT;
-  const int whole_lim = ttt ? 0 : m.kvv;      // tiles ending at or below it hold only real keys
+  // Keys below kv_valid are real (kv_valid <= the walked key count).
   auto copy_tile = [&](int t, int k) __attribute__((always_inline)) {
     const int tb = t * TK;
-    const int lim = t >= 0 ? (tb + TK <= whole_lim ? TK : m.kvv - tb) : 0;   // rows below lim are real keys
+    const int lim = t >= 0 ? (tb + TK <= m.kvv ? TK : m.kvv - tb) : 0;   // rows below lim are real keys
 #pragma unroll
     for (int x = 0; x < LPW; ++x) {
       const int idx = wave * LPW + x;
       if (ALL_COPY || idx < 2 * NINS) {
         if (idx < NINS) {
           const int row = idx * RPI + crow;
-          const bool ok = ttt ? (t >= 0 && key_valid(m, tb + row)) : row < lim;
+          const bool ok = row < lim;
           const bf16* g = ok ? Kg + (int64_t)tb * p.k.ss + roff[x] : Kg + zoff[x];
           lds_dma16(g, smem + k * L::TILE_BYTES + idx * 1024);
         } else {
@@ -440,7 +437,8 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   hipError_t e = launch_transpose_keys<D>(p, p.v, p.vt, p.vt_ss, stream);
   if (e != hipSuccess) return e;
   const int lds = FwdLds<D>::BYTES;
-  auto k = p.mask.kind == MASK_TTT ? fwd_kernel<D, NW, true> : fwd_kernel<D, NW, false>;
+  const int mk = mask_instance(p.mask.kind);
+  auto k = mk == MK_TTT ? fwd_kernel<D, NW, MK_TTT> : (mk == MK_WIN ? fwd_kernel<D, NW, MK_WIN> : fwd_kernel<D, NW, MK_FC>);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NW * 64), lds, stream, p);

@@ -12,9 +12,10 @@ struct Tensor {
 };
 
 struct Mask {
-  int kind;            // 0 FULL, 1 CAUSAL, 2 TTT
+  int kind;            // 0 FULL, 1 CAUSAL, 2 TTT, 3 WINDOW
   int shift;           // causal shift (>= 0)
   const int* kv_valid; // device [B] or nullptr
+  int wl, wr;          // WINDOW: keys allowed before / after the (shifted) diagonal
 };
 
 // Keys per V^T tile of the forward workspace (the forward's key tile).
@@ -38,6 +39,17 @@ struct Params {
   float* dkv_part;     // backward workspace (bf16, D >= 32): two halves' float32
                        // sums [2][dK^T, dV^T][B, Hkv, Skv, D]
 };
+
+// The bf16 dK/dV kernel (D >= 32) owns 256-key blocks.  With fewer than
+// 1024 blocks it splits each block's query steps between two workgroups
+// (so the causal triangle still balances over the chip), which then need
+// float32 partial sums in the workspace and a reduction; with more, every
+// workgroup takes all steps of its block and writes dK, dV itself.
+constexpr int kDkdvKeys = 256;
+inline bool dkdv_split(int B, int Hkv, int keys) {
+  const int64_t nkt = ((int64_t)keys + kDkdvKeys - 1) / kDkdvKeys;
+  return (int64_t)B * Hkv * nkt < 1024;
+}
 
 // Launchers (one translation unit per kernel family).  Each returns the
 // hipError_t of its launches; shapes were validated by the dispatcher.

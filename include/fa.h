@@ -26,6 +26,14 @@
  *                     (j >= L and (j - i) mod L == 0 and (j mod L) < kv_valid[b])
  *                   i.e. causal over the step-0 keys plus, for every later
  *                   step s, the key of step s at the query's own position.
+ *   FA_MASK_WINDOW  a band of keys around the query position: key j allowed
+ *                   iff i - causal_shift - window_left <= j
+ *                       <= i - causal_shift + window_right  and j < kv_valid[b]
+ *                   ((w - 1, 0) is a causal sliding window of w keys, (w, w)
+ *                   a symmetric band; the ggml playbook, section "4.
+ *                   Measurement discipline", names windowed self-attention
+ *                   among the diffusion trainer's geometries without fixing
+ *                   the window's form).
  *   A query row with no allowed key gets O = 0 and LSE = 0, and contributes
  *   no gradient; a key no query may attend gets dK = dV = 0 exactly (ggml
  *   playbook, "6. Trap list", items 8 and 9).
@@ -72,7 +80,7 @@ typedef enum {
 
 typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
 
-typedef enum { FA_MASK_FULL = 0, FA_MASK_CAUSAL = 1, FA_MASK_TTT = 2 } fa_mask_kind;
+typedef enum { FA_MASK_FULL = 0, FA_MASK_CAUSAL = 1, FA_MASK_TTT = 2, FA_MASK_WINDOW = 3 } fa_mask_kind;
 
 /* One [B, H, S, D] tensor: base pointer and element strides (D stride = 1). */
 typedef struct {
@@ -84,10 +92,12 @@ typedef struct {
 
 typedef struct {
   int32_t kind;              /* fa_mask_kind */
-  int32_t causal_shift;      /* >= 0; used by CAUSAL and by TTT's step-0 part */
+  int32_t causal_shift;      /* >= 0; used by CAUSAL, WINDOW and TTT's step-0 part */
   const int32_t* kv_valid;   /* device int32 [B] valid key count per batch
-                                (clamped to [0, Skv] for FULL/CAUSAL and to
-                                [0, Sq] for TTT), or NULL = all keys valid */
+                                (clamped to [0, Skv] for FULL/CAUSAL/WINDOW and
+                                to [0, Sq] for TTT), or NULL = all keys valid */
+  int32_t window_left;       /* WINDOW only: >= 0 keys before the diagonal */
+  int32_t window_right;      /* WINDOW only: >= 0 keys after the diagonal */
 } fa_mask_desc;
 
 typedef struct {

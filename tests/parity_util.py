@@ -30,29 +30,30 @@ def to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(q, k, v, do, kind, shift=0, kv_valid=None, scale=None, device="cuda"):
+def run_gpu(q, k, v, do, kind, shift=0, kv_valid=None, scale=None, device="cuda", window=None):
     """Forward + backward through the library; returns numpy float64 arrays."""
     qg, kg, vg, dog = (x.to(device) for x in (q, k, v, do))
     kvv = None if kv_valid is None else torch.tensor(list(kv_valid), dtype=torch.int32, device=device)
-    o, lse = fa.fa_fwd(qg, kg, vg, mask_kind=kind, causal_shift=shift, kv_valid=kvv, scale=scale)
+    o, lse = fa.fa_fwd(qg, kg, vg, mask_kind=kind, causal_shift=shift, kv_valid=kvv, scale=scale,
+                       window=window)
     dq, dk, dv = fa.fa_bwd(qg, kg, vg, o, lse, dog, mask_kind=kind, causal_shift=shift,
-                           kv_valid=kvv, scale=scale)
+                           kv_valid=kvv, scale=scale, window=window)
     torch.cuda.synchronize()
     return dict(O=to_np(o), LSE=to_np(lse), dQ=to_np(dq), dK=to_np(dk), dV=to_np(dv))
 
 
-def structure(kind, B, Sq, Skv, shift, kv_valid):
+def structure(kind, B, Sq, Skv, shift, kv_valid, window=None):
     """(nonempty rows [B, Sq], attended keys [B, Skv]) from the oracle's predicate."""
     rows = np.zeros((B, Sq), bool)
     keys = np.zeros((B, Skv), bool)
     for b in range(B):
-        A = allowed(kind, Sq, Skv, shift, None if kv_valid is None else kv_valid[b])
+        A = allowed(kind, Sq, Skv, shift, None if kv_valid is None else kv_valid[b], window=window)
         rows[b] = A.any(1)
         keys[b] = A.any(0)
     return rows, keys
 
 
-def compare(got, ref, dtype, kind, shift=0, kv_valid=None, label="", zero_ref=()):
+def compare(got, ref, dtype, kind, shift=0, kv_valid=None, label="", zero_ref=(), window=None):
     """Assert the tolerance bar; returns the error summary dict.
 
     ``zero_ref`` names tensors whose exact value is identically zero (e.g.
@@ -61,7 +62,7 @@ def compare(got, ref, dtype, kind, shift=0, kv_valid=None, label="", zero_ref=()
     """
     B, Hq, Sq, D = ref["O"].shape
     Skv = ref["dK"].shape[2]
-    rows, keys = structure(kind, B, Sq, Skv, shift, kv_valid)
+    rows, keys = structure(kind, B, Sq, Skv, shift, kv_valid, window)
     errs = {}
     for name in ("O", "LSE", "dQ", "dK", "dV"):
         g, r = got[name], ref[name]
@@ -99,12 +100,13 @@ def compare(got, ref, dtype, kind, shift=0, kv_valid=None, label="", zero_ref=()
 
 
 def check_case(q, k, v, do, kind, dtype, shift=0, kv_valid=None, scale=None, label="",
-               zero_ref=(), ref_inputs=None):
+               zero_ref=(), ref_inputs=None, window=None):
     say(f"[parity] {label} q{tuple(q.shape)} k{tuple(k.shape)} kind={kind} shift={shift} "
-        f"kv_valid={kv_valid} dtype={dtype}")
-    got = run_gpu(q, k, v, do, kind, shift, kv_valid, scale)
+        f"kv_valid={kv_valid} window={window} dtype={dtype}")
+    got = run_gpu(q, k, v, do, kind, shift, kv_valid, scale, window=window)
     ref_in = (q, k, v, do) if ref_inputs is None else ref_inputs
-    ref = attention_ref(*(x.double().numpy() for x in ref_in), kind, shift, kv_valid, scale)
-    errs = compare(got, ref, dtype, kind, shift, kv_valid, label, zero_ref)
+    ref = attention_ref(*(x.double().numpy() for x in ref_in), kind, shift, kv_valid, scale,
+                        window=window)
+    errs = compare(got, ref, dtype, kind, shift, kv_valid, label, zero_ref, window)
     say(f"[parity] {label} ok {errs}")
     return errs

@@ -34,7 +34,8 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layout_matches_header():
     # offsets a C compiler gives the structs of fa.h on x86-64
     assert ctypes.sizeof(_lib.fa_tensor) == 32
-    assert ctypes.sizeof(_lib.fa_mask_desc) == 16
+    assert ctypes.sizeof(_lib.fa_mask_desc) == 24
+    assert _lib.fa_mask_desc.kv_valid.offset == 8 and _lib.fa_mask_desc.window_right.offset == 20
     assert _lib.fa_fwd_args.q.offset == 32
     assert _lib.fa_fwd_args.lse.offset == 32 + 4 * 32
     assert _lib.fa_fwd_args.mask.offset == 32 + 4 * 32 + 8
@@ -47,13 +48,13 @@ def _t(slot, B, H, S, D, eb=2, strides=None):
     return _lib.fa_tensor(BASE + slot * GAP, *st)
 
 
-def fwd_args(B=1, Hq=4, Hkv=2, Sq=64, Skv=64, D=64, dtype=_lib.FA_BF16, kind=1, shift=0):
+def fwd_args(B=1, Hq=4, Hkv=2, Sq=64, Skv=64, D=64, dtype=_lib.FA_BF16, kind=1, shift=0, window=(0, 0)):
     a = _lib.fa_fwd_args()
     a.dtype, a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = dtype, B, Hq, Hkv, Sq, Skv, D
     a.scale = 0.0
     a.q, a.k, a.v, a.o = _t(0, B, Hq, Sq, D), _t(1, B, Hkv, Skv, D), _t(2, B, Hkv, Skv, D), _t(3, B, Hq, Sq, D)
     a.lse = BASE + 4 * GAP
-    a.mask = _lib.fa_mask_desc(kind, shift, None)
+    a.mask = _lib.fa_mask_desc(kind, shift, None, *window)
     return a
 
 
@@ -108,6 +109,7 @@ FWD_CASES = [
     ("negative S", dict(Sq=-1), _lib.FA_ERR_INVALID_ARG, "negative size"),
     ("negative shift", dict(shift=-2), _lib.FA_ERR_INVALID_ARG, "causal_shift"),
     ("ttt skv not multiple", dict(kind=2, Sq=64, Skv=100), _lib.FA_ERR_INVALID_ARG, "multiple of Sq"),
+    ("negative window", dict(kind=3, window=(4, -1)), _lib.FA_ERR_INVALID_ARG, "negative window"),
 ]
 
 

@@ -14,7 +14,7 @@ from parity_util import check_case, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-FULL, CAUSAL, TTT = W.FULL, W.CAUSAL, W.TTT
+FULL, CAUSAL, TTT, WINDOW = W.FULL, W.CAUSAL, W.TTT, W.WINDOW
 
 
 def rnd(shape, seed, dtype):
@@ -104,6 +104,42 @@ def test_bf16_ttt_small_head_dim(D):
     check_case(q, k, v, do, TTT, "bf16", kv_valid=(100,), label=f"bf16 ttt D={D}")
 
 
+# WINDOW: (left, right) bands, with shift, padding, GQA, Sq != Skv, and
+# bands narrower than a 64-key tile, wider than several, and one-sided.
+WIN_CASES = [
+    # B, Hq, Hkv, Sq, Skv, shift, kv_valid, (left, right)
+    (2, 4, 2, 300, 300, 0, None, (63, 0)),
+    (2, 4, 4, 300, 300, 0, None, (40, 40)),
+    (1, 8, 2, 333, 333, 3, (290,), (100, 7)),
+    (2, 2, 1, 200, 333, 0, (333, 120), (5, 150)),
+    (1, 4, 2, 260, 260, 70, None, (0, 0)),
+]
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("case", WIN_CASES, ids=[f"w{c[7][0]}_{c[7][1]}_s{c[5]}" for c in WIN_CASES])
+def test_bf16_window(case, D):
+    B, Hq, Hkv, Sq, Skv, shift, kvv, win = case
+    q, k, v, do = inputs(B, Hq, Hkv, Sq, Skv, D, torch.bfloat16, seed=D + Sq + win[0])
+    # a band of one key: P = 1 and dS = 0 on every row, so dQ and dK are exactly 0
+    zero = ("dQ", "dK") if win == (0, 0) else ()
+    check_case(q, k, v, do, WINDOW, "bf16", shift=shift, kv_valid=kvv, window=win,
+               label=f"bf16 window {win} shift={shift} D={D}", zero_ref=zero)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_window_many_workgroups(D):
+    q, k, v, do = inputs(4, 128, 16, 300, 333, D, torch.bfloat16, seed=81 + D)
+    check_case(q, k, v, do, WINDOW, "bf16", shift=1, kv_valid=(333, 300, 77, 1), window=(90, 30),
+               label=f"bf16 many-WG window D={D}")
+
+
+def test_f32_window():
+    q, k, v, do = inputs(1, 4, 2, 150, 150, 64, torch.float32, seed=91)
+    check_case(q, k, v, do, WINDOW, "f32", shift=2, kv_valid=(140,), window=(20, 9),
+               label="f32 window")
+
+
 def test_bf16_bshd_strided_views():
     # q/k/v/dO as transposed views of [B, S, H, D] storage (no copies)
     B, S, Hq, Hkv, D = 2, 190, 4, 2, 64
@@ -147,17 +183,18 @@ def test_f32_ragged_gqa_ttt(D):
     check_case(q, k, v, do, CAUSAL, "f32", shift=2, label=f"f32 causal D={D}")
 
 
-@pytest.mark.parametrize("kind", [CAUSAL, TTT])
+@pytest.mark.parametrize("kind", [CAUSAL, TTT, WINDOW])
 def test_bitwise_determinism(kind):
     L = 384
     Skv = 3 * L if kind == TTT else L
     q, k, v, do = inputs(1, 8, 2, L, Skv, 128, torch.bfloat16, seed=47)
+    win = (100, 20) if kind == WINDOW else None
     say(f"[determinism] kind={kind}")
-    a = run_gpu(q, k, v, do, kind)
+    a = run_gpu(q, k, v, do, kind, window=win)
     # unrelated work in between, then the same call again
     x = torch.randn(4096, 4096, device="cuda")
     (x @ x).sum().item()
-    b = run_gpu(q, k, v, do, kind)
+    b = run_gpu(q, k, v, do, kind, window=win)
     for name in ("O", "LSE", "dQ", "dK", "dV"):
         assert np.array_equal(a[name], b[name]), name
 
@@ -209,6 +246,25 @@ def test_bf16_many_workgroups_small_head_dim(case, D):
     name, kind, Sq, Skv, shift, kvv = case
     q, k, v, do = inputs(4, 128, 16, Sq, Skv, D, torch.bfloat16, seed=71 + D)
     check_case(q, k, v, do, kind, "bf16", shift=shift, kv_valid=kvv, label=f"bf16 many-WG {name} D={D}")
+
+
+# At least 1024 key blocks of 256 (B * Hkv * ceil(keys / 256)): the D >= 32
+# dK/dV kernel then gives each block to one workgroup, which writes dK and dV
+# itself (no partial sums, no reduction).
+UNSPLIT = [
+    # name, B, Hq, Hkv, Sq, Skv, D, kind, shift, kv_valid, window
+    ("mha_causal_d128", 16, 64, 64, 256, 256, 128, CAUSAL, 0, None, None),
+    ("gqa_full_kvvalid_d128", 8, 256, 128, 200, 256, 128, FULL, 0, (256, 255, 130, 1, 64, 200, 7, 99), None),
+    ("ttt_d64", 8, 256, 128, 256, 512, 64, TTT, 0, None, None),
+    ("window_d32", 16, 64, 64, 256, 256, 32, WINDOW, 2, None, (30, 10)),
+]
+
+
+@pytest.mark.parametrize("case", UNSPLIT, ids=[c[0] for c in UNSPLIT])
+def test_bf16_dkdv_unsplit(case):
+    name, B, Hq, Hkv, Sq, Skv, D, kind, shift, kvv, win = case
+    q, k, v, do = inputs(B, Hq, Hkv, Sq, Skv, D, torch.bfloat16, seed=101 + D)
+    check_case(q, k, v, do, kind, "bf16", shift=shift, kv_valid=kvv, window=win, label=f"bf16 unsplit {name}")
 
 
 def test_bf16_many_workgroups_nan_padding():

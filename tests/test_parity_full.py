@@ -34,7 +34,7 @@ def run_like_bench(w, q, k, v, do):
     dev = "cuda"
     qg, kg, vg, dog = (x.to(dev) for x in (q, k, v, do))
     kvv = W.kv_valid_tensor(w, dev)
-    kw = dict(mask_kind=w.kind, causal_shift=w.shift, kv_valid=kvv, scale=w.scale)
+    kw = dict(mask_kind=w.kind, causal_shift=w.shift, kv_valid=kvv, scale=w.scale, window=w.window)
     o, lse = fa.fa_fwd(qg, kg, vg, **kw)
     dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
     ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(qg, kg)), dtype=torch.uint8, device=dev)
@@ -66,7 +66,8 @@ def check_identities(w, do, o, dk, dv, label):
         # from 0, causal shift s) only rows below s can be
         nonempty = np.ones(w.Sq, bool)
         probe = np.arange(min(w.Sq, 64 + w.shift))
-        nonempty[probe] = allowed(w.kind, w.Sq, w.Skv, w.shift, kvv_of(w, b), rows=probe).any(1)
+        nonempty[probe] = allowed(w.kind, w.Sq, w.Skv, w.shift, kvv_of(w, b), rows=probe,
+                                  window=w.window).any(1)
         for g in range(w.Hkv):
             dk_bg = f64(dk[b, g])
             dv_bg = f64(dv[b, g])
@@ -95,7 +96,7 @@ def test_full_size_whole_heads(w):
     for b, h in samples:
         sl = lambda x: x[b:b + 1, h:h + 1].double().numpy()
         ref = attention_ref(sl(q), sl(k), sl(v), sl(do), w.kind, w.shift,
-                            None if w.kv_valid is None else [w.kv_valid[b]], w.scale)
+                            None if w.kv_valid is None else [w.kv_valid[b]], w.scale, window=w.window)
         got = dict(O=o[b, h], LSE=lse[b, h], dQ=dq[b, h], dK=dk[b, h], dV=dv[b, h])
         errs = {}
         for name, g in got.items():
@@ -123,8 +124,8 @@ def complete_keys(w, b, lo, hi):
     """Keys every one of whose attending query rows lies in [lo, hi).
 
     Candidates are the keys at positions (mod Sq) from lo - shift - 1 on;
-    rows far below lo are not scanned (under causal and TTT masks they see
-    no such key).  Were that wrong, the oracle's dK/dV of a key would miss
+    rows far below lo are not scanned (under causal, TTT and right-closed
+    window masks they see no such key).  Were that wrong, the oracle's dK/dV of a key would miss
     contributions and the comparison would fail, never pass falsely."""
     L = w.Sq
     cand = np.arange(w.Skv)
@@ -132,9 +133,10 @@ def complete_keys(w, b, lo, hi):
     outside = np.concatenate([np.arange(max(0, lo - w.shift - 256), lo), np.arange(hi, w.Sq)])
     seen = np.zeros(len(cand), bool)
     for r0 in range(0, len(outside), 2048):
-        A = allowed(w.kind, w.Sq, w.Skv, w.shift, kvv_of(w, b), rows=outside[r0:r0 + 2048])
+        A = allowed(w.kind, w.Sq, w.Skv, w.shift, kvv_of(w, b), rows=outside[r0:r0 + 2048], window=w.window)
         seen |= A[:, cand].any(0)
-    inside = allowed(w.kind, w.Sq, w.Skv, w.shift, kvv_of(w, b), rows=np.arange(lo, hi))[:, cand].any(0)
+    inside = allowed(w.kind, w.Sq, w.Skv, w.shift, kvv_of(w, b), rows=np.arange(lo, hi),
+                     window=w.window)[:, cand].any(0)
     return cand[~seen & inside]
 
 
@@ -152,7 +154,7 @@ def test_full_size_grouped_row_samples(w):
     kvv = None if w.kv_valid is None else [w.kv_valid[b]]
     blocks = [(0, ROWS), (w.Sq // 2 - ROWS // 2, w.Sq // 2 + ROWS // 2), (w.Sq - ROWS, w.Sq)]
     for lo, hi in blocks:
-        ref = attention_ref(qs, ks, vs, dos, w.kind, w.shift, kvv, w.scale, rows=(lo, hi))
+        ref = attention_ref(qs, ks, vs, dos, w.kind, w.shift, kvv, w.scale, rows=(lo, hi), window=w.window)
         errs = {}
         for name, got in (("O", o), ("dQ", dq)):
             errs[name] = rel_err(f64(got[b, hs, lo:hi]), ref[name][0, :, lo:hi])

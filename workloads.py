@@ -18,15 +18,18 @@ Shapes follow the pages' own workloads:
   * the EAGLE3 TTT call at draft step t = 2 (keys/values of steps 0, 1, 2
     concatenated, Skv = 3 * Sq);
   * diffusion-transformer full self-attention and cross-attention with padded
-    keys (1000 valid of 1024), the ggml playbook's real geometries.
+    keys (1000 valid of 1024), the ggml playbook's real geometries;
+  * windowed self-attention, the playbook's third geometry (its window is
+    not given: a symmetric band of +-512 keys on the DiT shape), and a
+    causal sliding window of 4096 keys on the long-context GQA shape.
 """
 from dataclasses import dataclass, field, replace
 from typing import Optional
 
 import torch
 
-FULL, CAUSAL, TTT = 0, 1, 2
-KIND_NAMES = {FULL: "full", CAUSAL: "causal", TTT: "ttt"}
+FULL, CAUSAL, TTT, WINDOW = 0, 1, 2, 3
+KIND_NAMES = {FULL: "full", CAUSAL: "causal", TTT: "ttt", WINDOW: "window"}
 
 
 @dataclass(frozen=True)
@@ -43,6 +46,7 @@ class Workload:
     shift: int = 0
     kv_valid: Optional[tuple] = None   # per-batch valid key count, None = all
     scale: Optional[float] = None      # None -> 1/sqrt(D)
+    window: Optional[tuple] = None     # WINDOW: (left, right)
 
     def torch_dtype(self):
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
@@ -78,6 +82,14 @@ def dit_cross():
                     FULL, kv_valid=(1000, 1000))
 
 
+def dit_window(w=512):
+    return Workload(f"dit_window_S8192_w{w}", 2, 16, 16, 8192, 8192, 64, WINDOW, window=(w, w))
+
+
+def swa_gqa(S=16384, w=4096):
+    return Workload(f"swa_gqa_S{S}_w{w}", 1, 32, 4, S, S, 128, WINDOW, window=(w - 1, 0))
+
+
 HEADLINE = long_gqa(16384)
 
 
@@ -85,7 +97,7 @@ def all_workloads():
     ws = [tiny_fp32(CAUSAL), tiny_fp32(FULL)]
     ws += [grid(D, S) for D in (16, 32, 64) for S in (256, 1024, 4096)]
     ws += [long_gqa(16384), long_gqa(32768), ttt(16384, 2), dit_self(),
-           dit_cross()]
+           dit_cross(), dit_window(), swa_gqa()]
     return ws
 
 
