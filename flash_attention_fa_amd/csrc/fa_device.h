@@ -244,26 +244,31 @@ struct MaskB {
 // longer changes (a larger shift already leaves every row empty, a wider
 // window already covers every key), and the band arithmetic stays far from
 // int overflow.
-__device__ __forceinline__ MaskB resolve_mask(const Params& p, int b) {
+// `kv` is the batch entry's valid key count (any int; clamped here).
+__host__ __device__ __forceinline__ MaskB make_mask(int kind, int shift, int Sq, int Skv, int kv, int wl, int wr) {
   MaskB m;
-  const int lim = 2 * (p.Sq + p.Skv);
-  m.kind = p.mask.kind;
-  m.shift = min(p.mask.shift, lim);
-  m.Sq = p.Sq;
-  m.Skv = p.Skv;
-  m.L = p.Sq;
-  m.wl = min(p.mask.wl, lim);
-  m.wr = min(p.mask.wr, lim);
-  const int cap = p.mask.kind == MASK_TTT ? p.Sq : p.Skv;
-  int v = p.mask.kv_valid ? p.mask.kv_valid[b] : cap;
-  m.kvv = v < 0 ? 0 : (v > cap ? cap : v);
+  const int lim = 2 * (Sq + Skv);
+  m.kind = kind;
+  m.shift = shift < lim ? shift : lim;
+  m.Sq = Sq;
+  m.Skv = Skv;
+  m.L = Sq;
+  m.wl = wl < lim ? wl : lim;
+  m.wr = wr < lim ? wr : lim;
+  const int cap = kind == MASK_TTT ? Sq : Skv;
+  m.kvv = kv < 0 ? 0 : (kv > cap ? cap : kv);
   return m;
+}
+
+__device__ __forceinline__ MaskB resolve_mask(const Params& p, int b) {
+  return make_mask(p.mask.kind, p.mask.shift, p.Sq, p.Skv, p.mask.kv_valid ? p.mask.kv_valid[b] : p.Skv,
+                   p.mask.wl, p.mask.wr);
 }
 
 // May query i attend key j?  (The three mask kinds of fa.h.)  Written
 // without per-lane branches (the mask kind is uniform), so callers can use it
 // as a select on score registers.
-__device__ __forceinline__ bool allowed(const MaskB& m, int i, int j) {
+__host__ __device__ __forceinline__ bool allowed(const MaskB& m, int i, int j) {
   const bool valid = j < m.kvv;
   if (m.kind == MASK_FULL) return valid;
   if (m.kind == MASK_WINDOW) {
@@ -285,19 +290,19 @@ __device__ __forceinline__ int wave_id() {
 }
 
 // Is key j a real key (its K/V row may be used at all)?
-__device__ __forceinline__ bool key_valid(const MaskB& m, int j) {
+__host__ __device__ __forceinline__ bool key_valid(const MaskB& m, int j) {
   if (j >= m.Skv) return false;
   if (m.kind == MASK_TTT) return (j % m.L) < m.kvv;
   return j < m.kvv;
 }
 
 // key_valid without branches on the lane's key (the mask kind is uniform).
-__device__ __forceinline__ bool key_valid_nb(const MaskB& m, int j) {
+__host__ __device__ __forceinline__ bool key_valid_nb(const MaskB& m, int j) {
   const int jm = m.kind == MASK_TTT ? j - (j / m.L) * m.L : j;
   return (j < m.Skv) & (jm < m.kvv);
 }
 
-__device__ __forceinline__ int num_segments(const MaskB& m) {
+__host__ __device__ __forceinline__ int num_segments(const MaskB& m) {
   return m.kind == MASK_TTT ? (m.L > 0 ? m.Skv / m.L : 0) : 1;
 }
 
@@ -305,7 +310,7 @@ __device__ __forceinline__ int num_segments(const MaskB& m) {
 // is the causal (or full) range; TTT segment s >= 1 is the diagonal band of
 // step s.  Ranges are increasing in s; callers clip each start to the previous
 // end so no tile is visited twice.
-__device__ __forceinline__ void segment_tiles(const MaskB& m, int s, int qa, int qb, int TK,
+__host__ __device__ __forceinline__ void segment_tiles(const MaskB& m, int s, int qa, int qb, int TK,
                                               int& t0, int& t1) {
   int lo, hi;
   if (s == 0) {
@@ -322,7 +327,7 @@ __device__ __forceinline__ void segment_tiles(const MaskB& m, int s, int qa, int
 
 // Keys [k0, k1) against queries [qa, qb): skip, no predicate needed, or
 // predicate needed per element.
-__device__ __forceinline__ int rect_state(const MaskB& m, int k0, int k1, int qa, int qb) {
+__host__ __device__ __forceinline__ int rect_state(const MaskB& m, int k0, int k1, int qa, int qb) {
   if (qb <= qa || k1 <= k0) return TILE_SKIP;
   if (m.kind == MASK_FULL) return k1 <= m.kvv ? TILE_FULL : (k0 < m.kvv ? TILE_PART : TILE_SKIP);
   if (m.kind == MASK_WINDOW) {
@@ -351,20 +356,20 @@ __device__ __forceinline__ int rect_state(const MaskB& m, int k0, int k1, int qa
 // Number of leading TK-key tiles that every query row >= qa may attend in
 // full (keys below kv_valid and, unless FULL, at most qa - shift): tiles
 // [0, result) need neither classification nor a mask for rows >= qa.
-__device__ __forceinline__ int full_tiles_below(const MaskB& m, int qa, int TK) {
+__host__ __device__ __forceinline__ int full_tiles_below(const MaskB& m, int qa, int TK) {
   if (m.kind == MASK_WINDOW) return 0;   // a band has no fully visible prefix in general
   int lim = m.kvv;
   if (m.kind != MASK_FULL) lim = min(lim, qa - m.shift + 1);
   return lim > 0 ? lim / TK : 0;
 }
 
-__device__ __forceinline__ int tile_state(const MaskB& m, int k0, int TK, int qa, int qb) {
+__host__ __device__ __forceinline__ int tile_state(const MaskB& m, int k0, int TK, int qa, int qb) {
   return rect_state(m, k0, k0 + TK, qa, qb);
 }
 
 // Queries [lo, hi) that may attend some key in [k0, k1) (a hull; the caller
 // still classifies each query tile).
-__device__ __forceinline__ void query_hull(const MaskB& m, int k0, int k1, int& lo, int& hi) {
+__host__ __device__ __forceinline__ void query_hull(const MaskB& m, int k0, int k1, int& lo, int& hi) {
   lo = m.Sq; hi = 0;
   if (m.kind == MASK_FULL) {
     if (k0 < m.kvv) { lo = 0; hi = m.Sq; }
@@ -391,13 +396,13 @@ __device__ __forceinline__ void query_hull(const MaskB& m, int k0, int k1, int& 
 // Walks the tiles of all segments in increasing order, each tile once.
 struct TileWalk {
   int seg, nseg, t, t1, prev_end;
-  __device__ __forceinline__ void start(const MaskB& m, int qa, int qb, int TK) {
+  __host__ __device__ __forceinline__ void start(const MaskB& m, int qa, int qb, int TK) {
     nseg = num_segments(m);
     seg = -1; t = 0; t1 = 0; prev_end = 0;
     advance(m, qa, qb, TK);
   }
   // Move to the next segment with tiles left.
-  __device__ __forceinline__ void advance(const MaskB& m, int qa, int qb, int TK) {
+  __host__ __device__ __forceinline__ void advance(const MaskB& m, int qa, int qb, int TK) {
     while (t >= t1 && ++seg < nseg) {
       int a, b;
       segment_tiles(m, seg, qa, qb, TK, a, b);
@@ -405,8 +410,8 @@ struct TileWalk {
       if (a < b) { t = a; t1 = b; prev_end = b; }
     }
   }
-  __device__ __forceinline__ bool valid() const { return t < t1; }
-  __device__ __forceinline__ void next(const MaskB& m, int qa, int qb, int TK) {
+  __host__ __device__ __forceinline__ bool valid() const { return t < t1; }
+  __host__ __device__ __forceinline__ void next(const MaskB& m, int qa, int qb, int TK) {
     ++t;
     if (t >= t1) advance(m, qa, qb, TK);
   }
@@ -484,7 +489,7 @@ __host__ __device__ __forceinline__ int mask_instance(int kind) {
 }
 
 template <int MK>
-__device__ __forceinline__ void set_instance_kind(MaskB& m) {
+__host__ __device__ __forceinline__ void set_instance_kind(MaskB& m) {
   if constexpr (MK == MK_WIN) {
     m.kind = MASK_WINDOW;
   } else {
@@ -515,7 +520,7 @@ hipError_t launch_transpose_keys(const Params& p, const Tensor& src, void* dst, 
 // (batch, head) columns is a multiple of 8, each XCD gets a contiguous run of
 // columns (neighbouring heads share a K/V head, so its L2 serves them all) and
 // walks its ranks in order, rank 0 first.
-__device__ __forceinline__ void map_block(int bid, int ncol, int nrank, int& col, int& rank) {
+__host__ __device__ __forceinline__ void map_block(int bid, int ncol, int nrank, int& col, int& rank) {
   if ((ncol & 7) == 0) {
     const int x = bid & 7, slot = bid >> 3, c8 = ncol >> 3;
     rank = slot / c8;
