@@ -391,32 +391,41 @@ dq_dma_kernel(Params p) {
     }
   }
 
+  // Copy instructions: instruction idx (of 2 * NINS per tile) moves 1 KB,
+  // rows RPI*(idx % NINS) .. +RPI of K (idx < NINS) or V.  Wave w issues idx =
+  // w*LPW .. +LPW, all of one tensor; a lane's global offset is a per-
+  // instruction row step (uniform), the lane's row (rbase) and its swizzled
+  // chunk (cofs), so the copies are selects, not branches.
+  static_assert(NINS % LPW == 0, "a wave's copies all come from one tensor");
   const int crow = lane / CPR, cslot = lane % CPR;
-  int roff[LPW];
+  const unsigned lds0 = lds_addr_of(smem);
+  const bool wk = wave * LPW < NINS;
+  const bf16* Xg = wk ? Kg : Vg;
+  const int64_t xss = wk ? p.k.ss : p.v.ss;
+  const int rbase = (int)(crow * xss);
+  int cofs[LPW], rstep[LPW], ldso[LPW];
 #pragma unroll
   for (int x = 0; x < LPW; ++x) {
-    const int idx = wave * LPW + x;
-    const int ii = idx % NINS;
-    const int row = ii * RPI + crow;
-    const int64_t ss = idx / NINS == 0 ? p.k.ss : p.v.ss;
-    roff[x] = (int)(row * ss) + 8 * (cslot ^ swz<D>(row));
+    const int idx = wave * LPW + x, ii = idx % NINS;
+    cofs[x] = 8 * (cslot ^ swz<D>(ii * RPI + crow));
+    rstep[x] = (int)(ii * RPI * xss);
+    ldso[x] = (idx / NINS) * L::TILE + ii * 1024;
   }
   // Key tile t (K rows then V rows) into buffer k; keys that are not real
-  // (and every key when t < 0) come from key 0: finite, and masked.
+  // (and every key when t < 0) come from key 0: finite, and masked.  Keys
+  // below kv_valid are real (kv_valid <= the walked key count).
   auto copy_tile = [&](int t, int k) __attribute__((always_inline)) {
     const int tb = t * TK;
+    const int lim = t >= 0 ? (tb + TK <= m.kvv ? TK : m.kvv - tb) : 0;   // rows below lim are real keys
+    const bf16* base = Xg + (int64_t)tb * xss;
+    const unsigned lbuf = lds0 + k * L::BUF;
 #pragma unroll
     for (int x = 0; x < LPW; ++x) {
       const int idx = wave * LPW + x;
       if (ALL_COPY || idx < 2 * NINS) {
-        const int tensor = idx / NINS, ii = idx % NINS;
-        const int row = ii * RPI + crow;
-        const bool ok = (t >= 0) & key_valid_nb(m, tb + row);
-        const bf16* base = tensor == 0 ? Kg : Vg;
-        const int64_t ss = tensor == 0 ? p.k.ss : p.v.ss;
-        const int64_t o_real = (int64_t)tb * ss + roff[x];
-        const int64_t o_key0 = 8 * (cslot ^ swz<D>(row));
-        lds_dma16(base + (ok ? o_real : o_key0), smem + k * L::BUF + tensor * L::TILE + ii * 1024);
+        const bool ok = crow < lim - (idx % NINS) * RPI;
+        const bf16* g = ok ? base + (rstep[x] + rbase + cofs[x]) : Xg + cofs[x];
+        lds_dma16_at(g, lbuf + ldso[x]);
       }
     }
   };
@@ -439,33 +448,37 @@ dq_dma_kernel(Params p) {
 
   // tiles below full_end: every key allowed for every row of this wave
   const int full_end = full_tiles_below(m, wa, TK);
-  TileWalk cur;
-  cur.start(m, qa, qb, TK);
-  TileWalk nx1 = cur;
-  if (nx1.valid()) nx1.next(m, qa, qb, TK);
-  TileWalk nx2 = nx1;
-  if (nx2.valid()) nx2.next(m, qa, qb, TK);
-  TileWalk nx3 = nx2;
-  if (nx3.valid()) nx3.next(m, qa, qb, TK);
-  if (cur.valid()) {
-    copy_tile(cur.t, 0);
-    copy_tile(nx1.valid() ? nx1.t : -1, 1);
-    copy_tile(nx2.valid() ? nx2.t : -1, 2);
+  // The walk: key tiles [t, tend).  Every instance's mask is one segment
+  // here (FULL, CAUSAL or WINDOW; TTT's later steps were folded above), so
+  // the walk is a contiguous range.
+  int t, tend;
+  segment_tiles(m, 0, qa, qb, TK, t, tend);
+  auto tile_or_none = [&](int u) __attribute__((always_inline)) { return u < tend ? u : -1; };
+  if (t < tend) {
+    copy_tile(t, 0);
+    copy_tile(tile_or_none(t + 1), 1);
+    copy_tile(tile_or_none(t + 2), 2);
     wait_copies();
   }
   barrier_lds();
 
   auto step = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    copy_tile(nx3.valid() ? nx3.t : -1, (k + 3) % DQ_NBUF);
-    const int k0 = cur.t * TK;
-    const int state = cur.t < full_end ? TILE_FULL : tile_state(m, k0, TK, wa, wb);
+    copy_tile(tile_or_none(t + 3), (k + 3) % DQ_NBUF);
+    const int k0 = t * TK;
+    const int state = t < full_end ? TILE_FULL : tile_state(m, k0, TK, wa, wb);
     if (state != TILE_SKIP) {
       const unsigned char* Kt = smem + k * L::BUF;
       const unsigned char* Vt = Kt + L::TILE;
+      // dP^T accumulates onto -Delta (the lane's row), so it comes out as
+      // dP^T - Delta.
       f32x16 s[2], dp[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dp[kb][i] = -dlt;
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -494,7 +507,7 @@ dq_dma_kernel(Params p) {
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             const int i = 8 * st + u;
-            e[u] = exp2_fast(s[kb][i] * p.scale_log2 - l2) * (dp[kb][i] - dlt);
+            e[u] = exp2_fast(s[kb][i] * p.scale_log2 - l2) * dp[kb][i];
           }
           dsb[kb][st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
         }
@@ -514,13 +527,9 @@ dq_dma_kernel(Params p) {
     }
     wait_copies();
     barrier_lds();
-    cur = nx1;
-    nx1 = nx2;
-    nx2 = nx3;
-    if (nx3.valid()) nx3.next(m, qa, qb, TK);
-    return cur.valid();
+    return ++t < tend;
   };
-  if (cur.valid()) {
+  if (t < tend) {
     while (step(Buf<0>{}) && step(Buf<1>{}) && step(Buf<2>{}) && step(Buf<3>{})) {
     }
   }
@@ -971,7 +980,7 @@ dkdv_split_kernel(Params p) {
       const int q = sp.q0 + tid;
       const int64_t rb = ((int64_t)b * p.Hq + hk * p.G + sp.hs) * p.Sq;
       lrow = q < p.Sq ? p.lse2[rb + q] : 0.f;
-      drow = q < p.Sq ? p.delta[rb + q] : 0.f;
+      drow = q < p.Sq ? -p.delta[rb + q] : 0.f;   // staged as -Delta
     }
   };
   auto store_rowvals = [&](int buf) __attribute__((always_inline)) {
@@ -1023,7 +1032,7 @@ dkdv_split_kernel(Params p) {
     const unsigned char* Qt = smem + buf * L::STAGE;
     const unsigned char* Gt = Qt + L::TILE;
     const float* Ls = reinterpret_cast<const float*>(Qt + 2 * L::TILE);
-    const float* Ds = Ls + TQ;
+    const float* Ds = Ls + TQ;   // -Delta of the rows
 #pragma unroll 1
     for (int h = 0; h < TQ / 32; ++h) {   // 32-row sub-tiles, one at a time
     const int qa = cur.q0 + 32 * h;
@@ -1033,7 +1042,15 @@ dkdv_split_kernel(Params p) {
       if (state == TILE_FULL && qa + 32 > p.Sq) state = TILE_PART;   // rows past Sq
     }
     if (state != TILE_SKIP) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // dP accumulates onto -Delta of each register's row (q = qa + 8*(i/4) +
+      // 4*hh + i%4), so it comes out as dP - Delta.
+      f32x16 s = f32x16{}, dp;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 d4 = *FA_LDS(const f32x4, Ds + 32 * h + 8 * g + 4 * hh);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dp[4 * g + u] = d4[u];
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const bf16x8 aq = *FA_LDS(const bf16x8, Qt + h * 32 * 2 * D + roff[j]);
@@ -1057,13 +1074,12 @@ dkdv_split_kernel(Params p) {
         for (int g2 = 0; g2 < 2; ++g2) {
           const int g = 2 * st + g2;
           const f32x4 l4 = *FA_LDS(const f32x4, Ls + 32 * h + 8 * g + 4 * hh);
-          const f32x4 d4 = *FA_LDS(const f32x4, Ds + 32 * h + 8 * g + 4 * hh);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int i = 4 * g + u;
             const float pr = exp2_fast(s[i] * p.scale_log2 - l4[u]);
             pe[4 * g2 + u] = pr;
-            de[4 * g2 + u] = pr * (dp[i] - d4[u]);
+            de[4 * g2 + u] = pr * dp[i];
           }
         }
         pb[st] = cat8(to_bf16x4(pe[0], pe[1], pe[2], pe[3]), to_bf16x4(pe[4], pe[5], pe[6], pe[7]));

@@ -213,6 +213,20 @@ __device__ __forceinline__ void lds_dma16(const void* g, unsigned char* lds_base
                : "memory", "m0");
 }
 
+// The LDS byte address of a shared-memory pointer (uniform when p is).
+__device__ __forceinline__ unsigned lds_addr_of(const unsigned char* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p);
+}
+
+// lds_dma16 with the LDS byte address given directly (a uniform value).
+__device__ __forceinline__ void lds_dma16_at(const void* g, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // s_waitcnt with only the vector-memory counter constrained (<= n).
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -282,6 +296,13 @@ __host__ __device__ __forceinline__ bool allowed(const MaskB& m, int i, int j) {
   const int jm = j - (j / m.L) * m.L;
   return causal | ((j >= m.L) & (j < m.Skv) & (jm == i) & (jm < m.kvv));
 }
+
+// Instruction-class masks of the scheduler's group barriers, and a group
+// barrier: the next `n` instructions of class `mask` in the current
+// straight-line block are placed here, in order.
+enum : int { SCHED_VALU = 0x002, SCHED_SALU = 0x004, SCHED_MFMA = 0x008, SCHED_VMEM_READ = 0x020,
+             SCHED_DS_READ = 0x100, SCHED_DS_WRITE = 0x200, SCHED_TRANS = 0x400 };
+#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 // The wave index as a provably uniform (scalar) value, so everything derived
 // from it (tile ranges, tile states, loop bounds) stays in scalar registers.

@@ -161,48 +161,51 @@ fwd_kernel(Params p) {
     }
   }
 
-
-  // Asynchronous copy of key tile t into ring buffer k: this wave's share of
-  // the 2 * NINS instructions (K rows first, then V^T rows; which kind a
-  // wave copies is uniform).  K rows that are not real keys (and every row
-  // when t < 0) are fetched from key 0 instead: a real row, so the scores
-  // stay finite, and the mask drops them.  (Only reached when the walk has
-  // a tile, so key 0 is real.)  V^T rows need no selection: the pre-pass
-  // zeroed every position that is not a real key, and t < 0 reads tile 0.
+  // Copy instructions: instruction idx (of 2 * NINS per ring step) moves 1 KB,
+  // K rows RPI*idx .. +RPI when idx < NINS, else V^T d rows 8*(idx - NINS)
+  // .. +8.  Wave w issues idx = w*LPW .. +LPW, all of one kind (wk).  A lane's
+  // global offset is a per-wave row step (uniform), the lane's row (rbase)
+  // and its swizzled chunk (cofs); the copies are selects, not branches.
+  static_assert(NINS % LPW == 0, "a wave's copies are all K rows or all V^T rows");
   const int crow = lane / CPR, cslot = lane % CPR;
-  int roff[LPW], zoff[LPW];
+  const unsigned lds0 = lds_addr_of(smem);
+  const bool wk = wave * LPW < NINS;
+  const int rbase = wk ? (int)(crow * p.k.ss) : (int)((lane / (TK / 8)) * p.vt_ss);
+  int cofs[LPW], rstep[LPW], ldso[LPW];
 #pragma unroll
   for (int x = 0; x < LPW; ++x) {
     const int idx = wave * LPW + x;
-    if (idx < NINS) {
-      const int row = idx * RPI + crow;
-      const int gch = cslot ^ swz<D>(row);
-      roff[x] = (int)(row * p.k.ss) + 8 * gch;
-      zoff[x] = 8 * gch;
+    if (wk) {
+      cofs[x] = 8 * (cslot ^ swz<D>(idx * RPI + crow));
+      rstep[x] = (int)(idx * RPI * p.k.ss);
+      ldso[x] = idx * 1024;
     } else {
       const int row = (idx - NINS) * (64 / (TK / 8)) + lane / (TK / 8);   // d row of V^T
-      const int slot = lane % (TK / 8);
-      roff[x] = (int)(row * p.vt_ss) + 8 * (slot ^ vt_swz(row));
-      zoff[x] = roff[x];
+      cofs[x] = 8 * ((lane % (TK / 8)) ^ vt_swz(row));
+      rstep[x] = (int)((idx - NINS) * (64 / (TK / 8)) * p.vt_ss);
+      ldso[x] = L::VT_BASE + (idx - NINS) * 1024;
     }
   }
-  // Keys below kv_valid are real (kv_valid <= the walked key count).
-  auto copy_tile = [&](int t, int k) __attribute__((always_inline)) {
+  // Asynchronous copy of key tile t into ring buffer k (K rows and V^T rows):
+  // this wave's share of the 2 * NINS instructions.  K rows that are not real
+  // keys (and every row when t < 0) are fetched from key 0 instead: a real
+  // row, so the scores stay finite, and the mask drops them.  (Only reached
+  // when the walk has a tile, so key 0 is real.)  V^T rows need no
+  // selection: the pre-pass zeroed every position that is not a real key,
+  // and t < 0 reads tile 0.  Keys below kv_valid are real (kv_valid <= the
+  // walked key count).
+  auto copy_tiles = [&](int t, int k) __attribute__((always_inline)) {
     const int tb = t * TK;
-    const int lim = t >= 0 ? (tb + TK <= m.kvv ? TK : m.kvv - tb) : 0;   // rows below lim are real keys
+    const int lim = t >= 0 ? (tb + TK <= m.kvv ? TK : m.kvv - tb) : 0;   // K rows below lim are real keys
+    const bf16* base = wk ? Kg + (int64_t)tb * p.k.ss : VTg + (t >= 0 ? tb : 0);
+    const unsigned lbuf = lds0 + k * L::TILE_BYTES;
 #pragma unroll
     for (int x = 0; x < LPW; ++x) {
       const int idx = wave * LPW + x;
       if (ALL_COPY || idx < 2 * NINS) {
-        if (idx < NINS) {
-          const int row = idx * RPI + crow;
-          const bool ok = row < lim;
-          const bf16* g = ok ? Kg + (int64_t)tb * p.k.ss + roff[x] : Kg + zoff[x];
-          lds_dma16(g, smem + k * L::TILE_BYTES + idx * 1024);
-        } else {
-          lds_dma16(VTg + (t >= 0 ? tb : 0) + roff[x],
-                    smem + L::VT_BASE + k * L::TILE_BYTES + (idx - NINS) * 1024);
-        }
+        const bool ok = !wk || crow < lim - idx * RPI;
+        const bf16* g = ok ? base + (rstep[x] + rbase + cofs[x]) : Kg + cofs[x];
+        lds_dma16_at(g, lbuf + ldso[x]);
       }
     }
   };
@@ -259,6 +262,15 @@ fwd_kernel(Params p) {
       if (n + PF < NOP) va[(n + PF) % (PF + 1)] = vread(n + PF);
       const int c = n % NDB, ks = n / NDB;
       acc[c] = mfma32(va[n % (PF + 1)], pb[ks >> 1][ks & 1], acc[c]);
+    }
+    // Keep the reads ahead of their products: left alone, the scheduler
+    // moves each read next to its product and the wave waits out every
+    // read's latency.
+    sched_group(SCHED_DS_READ, PF);
+#pragma unroll
+    for (int n = 0; n < NOP; ++n) {
+      sched_group(SCHED_MFMA, 1);
+      if (n + PF < NOP) sched_group(SCHED_DS_READ, 1);
     }
   };
   // P of a tile against the running max, rounded to bf16, and its row sum
@@ -351,36 +363,33 @@ fwd_kernel(Params p) {
     }
   };
 
-  // Tiles i (cur) .. i+3 (nx3) of the walk.
-  TileWalk cur;
-  cur.start(m, qa, qb, TK);
-  TileWalk nx1 = cur;
-  if (nx1.valid()) nx1.next(m, qa, qb, TK);
-  TileWalk nx2 = nx1;
-  if (nx2.valid()) nx2.next(m, qa, qb, TK);
-  TileWalk nx3 = nx2;
-  if (nx3.valid()) nx3.next(m, qa, qb, TK);
+  // The walk: key tiles [t, tend).  Every instance's mask is one segment
+  // here (FULL, CAUSAL or WINDOW; TTT's later steps were folded above), so
+  // the walk is a contiguous range.
+  int t, tend;
+  segment_tiles(m, 0, qa, qb, TK, t, tend);
+  auto tile_or_none = [&](int u) __attribute__((always_inline)) { return u < tend ? u : -1; };
 
   f32x16 scur[2], snxt[2];
-  if (cur.valid()) {
-    copy_tile(cur.t, 0);
-    copy_tile(nx1.valid() ? nx1.t : -1, 1);
-    copy_tile(nx2.valid() ? nx2.t : -1, 2);
+  if (t < tend) {
+    copy_tiles(t, 0);
+    copy_tiles(tile_or_none(t + 1), 1);
+    copy_tiles(tile_or_none(t + 2), 2);
     wait_copies();
   }
   barrier_lds();
-  if (cur.valid()) {
+  if (t < tend) {
     qk(Buf<0>{}, scur);
-    mask(cur.t, scur);
+    mask(t, scur);
   }
 
   // One iteration with tile i in buffer k; false when the walk has ended.
   auto step = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    copy_tile(nx3.valid() ? nx3.t : -1, (k + 3) & (NBUF - 1));
-    // QK^T of tile i+1 (its buffer may hold a stale tile at the end: unused).
-    // QK^T of tile i+1 with the exponentials of tile i spread between its
-    // products (they are independent: matrix cores and vector ALUs overlap).
+    copy_tiles(tile_or_none(t + 3), (k + 3) & (NBUF - 1));
+    // QK^T of tile i+1 (its buffer may hold a stale tile at the end: unused)
+    // with the exponentials of tile i spread between its products (they are
+    // independent: matrix cores and vector ALUs overlap).
     bf16x8 pb[2][2];
     float ls = qk_softmax(Buf<(k + 1) & (NBUF - 1)>{}, snxt, scur, pb);
     if (__any(!(ls <= kSumLimit))) {
@@ -389,18 +398,14 @@ fwd_kernel(Params p) {
     }
     lsum += ls;
     pv(kc, pb);
-    if (nx1.valid()) mask(nx1.t, snxt);
+    if (t + 1 < tend) mask(t + 1, snxt);
     wait_copies();
     barrier_lds();
     scur[0] = snxt[0];
     scur[1] = snxt[1];
-    cur = nx1;
-    nx1 = nx2;
-    nx2 = nx3;
-    if (nx3.valid()) nx3.next(m, qa, qb, TK);
-    return cur.valid();
+    return ++t < tend;
   };
-  if (cur.valid()) {
+  if (t < tend) {
     while (step(Buf<0>{}) && step(Buf<1>{}) && step(Buf<2>{}) && step(Buf<3>{})) {
     }
   }
