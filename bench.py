@@ -40,6 +40,19 @@ prints one JSON line per workload: fwd / bwd / step times, TFLOP/s, the
 fraction of the dense peak of the arithmetic type, the attainable rate
 min(peak, AI x 8 TB/s) from the algorithmic bytes, and the peak device memory
 of one fwd+bwd.  No oracle timing.
+
+    python bench.py --loss [--workload lsm_loss_B1_T16384_V32000] [--loss-all]
+
+times the soft-target log-softmax loss (fa_lsm_loss_fwd + fa_lsm_loss_bwd,
+the EAGLE3 loss after attention) on the SpecForge page's (B, T, V)
+configurations: one JSON line per configuration with the forward, backward
+and step times and their HBM throughput over the algorithmic bytes (forward:
+logits and targets read once, 8 bytes per element; backward: both read and
+the gradient written over the logits, 12 bytes per element) against the
+8 TB/s peak, the peak device memory above the inputs, and (first
+configuration only) the fp64 oracle timed on a sample of rows.  The logits
+are restored from a pristine copy before each step, outside the timed
+events.
 """
 import argparse
 import hashlib
@@ -272,6 +285,77 @@ def sweep(fa, dev, steps, warmup):
     return 0
 
 
+def loss_bench(fa, w, dev, steps, warmup, cpu):
+    """One JSON line for the log-softmax loss workload w (see the module
+    docstring)."""
+    x0, t, mask = W.make_loss_inputs(w, seed=0, device=dev)
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated(dev)
+    x = torch.empty_like(x0)
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(marks=None):
+        x.copy_(x0)
+        if marks:
+            marks[0].record(stream)
+        loss, row, m, d, tsum = fa.lsm_loss_fwd(x, t, mask, stream=stream)
+        if marks:
+            marks[1].record(stream)
+        fa.lsm_loss_bwd(x, t, mask, m, d, tsum, one, stream=stream)
+        if marks:
+            marks[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for s_ in range(steps):
+        step(ev[s_])
+    torch.cuda.synchronize()
+    f_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    b_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    nv = w.N * w.V
+    fb, bb = 8 * nv + 5 * 4 * w.N + 4, 12 * nv + 5 * 4 * w.N
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    st_gbs = gbs(fb + bb, f_ms + b_ms)
+    out = {"metric": "soft-target log-softmax loss fwd+bwd HBM GB/s at 1 MI355X",
+           "value": round(st_gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+           "ms_per_step": round(f_ms + b_ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded 4*N(0,1) logits, u**8-normalised soft targets, prompt rows masked)",
+           "config": {"workload": w.name, "B": w.B, "T": w.T, "V": w.V},
+           "fwd": {"ms_median": round(f_ms, 4), "gbs": round(gbs(fb, f_ms), 1)},
+           "bwd": {"ms_median": round(b_ms, 4), "gbs": round(gbs(bb, b_ms), 1)},
+           "roofline": {"kernel": "lsm_loss_fwd_kernel + lsm_loss_bwd_kernel (+ the mean)", "bound": "hbm",
+                        "achieved": round(st_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(st_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+           "memory": {"peak_above_inputs_bytes": int(peak), "inputs_bytes": int(mem0),
+                      "explicit_chain_intermediates_bytes": 4 * nv * 4}}
+    if cpu:
+        from threadpoolctl import threadpool_info
+        from oracle import logsoftmax_loss_forward, logsoftmax_loss_backward
+        rows = min(w.N, 256)
+        X = x0[:rows].double().cpu().numpy()
+        T = t[:rows].double().cpu().numpy()
+        M = mask[:rows].double().cpu().numpy()
+        t0 = time.perf_counter()
+        logsoftmax_loss_forward(X, T, M)
+        logsoftmax_loss_backward(X, T, M)
+        sec = time.perf_counter() - t0
+        threads = max([q.get("num_threads", 1) for q in threadpool_info()] or [1])
+        out["cpu_baseline"] = {"value": round((fb + bb) * rows / w.N / sec / 1e9, 3), "unit": "GB/s",
+                               "cores": int(threads), "kind": "oracle",
+                               "sample": f"fp64 numpy oracle, fwd+bwd of the first {rows} rows of {w.name} "
+                                         f"({sec:.2f} s, host nproc {os.cpu_count()})"}
+    print(json.dumps(out), flush=True)
+    del x, x0, t, mask
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +367,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time every named workload, one JSON line each, and exit")
+    ap.add_argument("--loss", action="store_true",
+                    help="time the soft-target log-softmax loss instead of attention")
+    ap.add_argument("--loss-all", action="store_true",
+                    help="with --loss: every configuration of the page's loss table")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy (counter calibration) and exit")
     a = ap.parse_args()
@@ -298,6 +386,12 @@ def main():
     torch.cuda.set_device(dev)
     if a.sweep:
         return sweep(fa, dev, a.steps, a.warmup)
+    if a.loss:
+        ws = W.loss_workloads() if a.loss_all else \
+            [x for x in W.loss_workloads() if x.name == a.workload] or [W.LOSS_HEADLINE]
+        for i, lw in enumerate(ws):
+            loss_bench(fa, lw, dev, a.steps, a.warmup, cpu=(i == 0 and not a.no_cpu_baseline))
+        return 0
     w = find_workload(a.workload)
     q, k, v, do = W.make_inputs(w, seed=0)
     r = measure(fa, w, dev, a.steps, a.warmup, (q, k, v, do))

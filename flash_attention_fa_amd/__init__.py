@@ -35,7 +35,8 @@ FULL, CAUSAL, TTT, WINDOW = FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_TTT, FA_MASK_W
 
 __all__ = ["fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes",
            "fa_last_error", "FA_BWD_DELTA", "FA_BWD_DKDV", "FA_BWD_DQ",
-           "attention", "FAError", "FULL", "CAUSAL", "TTT", "WINDOW"]
+           "attention", "FAError", "FULL", "CAUSAL", "TTT", "WINDOW",
+           "lsm_loss_fwd", "lsm_loss_bwd", "logsoftmax_loss"]
 
 
 def _dtype_code(t):
@@ -211,3 +212,73 @@ def attention(q, k, v, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None
 
 def default_scale(D):
     return 1.0 / math.sqrt(D)
+
+
+# ---- soft-target log-softmax loss (fa_lsm_loss_fwd / fa_lsm_loss_bwd) -------
+
+def _loss_args(logits, target, mask):
+    if logits.dim() != 2 or target.shape != logits.shape:
+        raise FAError(_lib.FA_ERR_INVALID_ARG, "logits and target must be [N, V] of one shape")
+    for name, t in (("logits", logits), ("target", target)):
+        if t.dtype != torch.float32:
+            raise FAError(_lib.FA_ERR_UNSUPPORTED, f"{name} must be float32")
+        if t.shape[1] > 1 and t.stride(1) != 1:
+            raise FAError(_lib.FA_ERR_INVALID_ARG, f"{name}: the vocabulary dimension must have unit stride")
+    a = _lib.fa_lsm_loss_args()
+    a.N, a.V = int(logits.shape[0]), int(logits.shape[1])
+    a.logits, a.logits_ss = logits.data_ptr(), logits.stride(0)
+    a.target, a.target_ss = target.data_ptr(), target.stride(0)
+    if mask is not None:
+        if mask.dtype != torch.float32 or not mask.is_contiguous() or mask.numel() != a.N:
+            raise FAError(_lib.FA_ERR_INVALID_ARG, "mask must be a contiguous float32 tensor of N elements")
+        a.mask = mask.data_ptr()
+    return a
+
+
+def lsm_loss_fwd(logits, target, mask=None, *, stream=None):
+    """Soft-target log-softmax loss (fp32).  Returns (loss [1], row_loss [N],
+    m [N], d [N], tsum [N]); see fa_lsm_loss_fwd in include/fa.h."""
+    N = logits.shape[0]
+    a = _loss_args(logits, target, mask)
+    f = lambda n: torch.empty(n, dtype=torch.float32, device=logits.device)
+    loss, row, m, d, tsum = f(1), f(N), f(N), f(N), f(N)
+    a.m, a.d, a.tsum, a.row_loss, a.loss = m.data_ptr(), d.data_ptr(), tsum.data_ptr(), row.data_ptr(), loss.data_ptr()
+    _lib.check(_lib.lib().fa_lsm_loss_fwd(a, _stream(logits, stream)))
+    return loss, row, m, d, tsum
+
+
+def lsm_loss_bwd(logits, target, mask, m, d, tsum, grad_loss, *, stream=None):
+    """Overwrites ``logits`` with grad_loss * dloss/dlogits and returns it."""
+    a = _loss_args(logits, target, mask)
+    for t in (m, d, tsum, grad_loss):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise FAError(_lib.FA_ERR_INVALID_ARG, "m, d, tsum and grad_loss must be contiguous float32")
+    a.m, a.d, a.tsum, a.grad_loss = m.data_ptr(), d.data_ptr(), tsum.data_ptr(), grad_loss.data_ptr()
+    _lib.check(_lib.lib().fa_lsm_loss_bwd(a, _stream(logits, stream)))
+    return logits
+
+
+class _LogSoftmaxLoss(torch.autograd.Function):
+    """The loss as an autograd function that keeps no gradient buffer of its
+    own: the backward writes the gradient over the saved logits (detached, as
+    the SpecForge page's LogSoftmaxLoss does) and returns that tensor."""
+
+    @staticmethod
+    def forward(ctx, logits, target, mask):
+        loss, _row, m, d, tsum = lsm_loss_fwd(logits, target, mask)
+        ctx.save_for_backward(logits.detach(), target, m, d, tsum)
+        ctx.mask = mask
+        return loss.reshape(())
+
+    @staticmethod
+    def backward(ctx, g):
+        logits, target, m, d, tsum = ctx.saved_tensors
+        g = g.reshape(1).to(torch.float32).contiguous()
+        return lsm_loss_bwd(logits, target, ctx.mask, m, d, tsum, g), None, None
+
+
+def logsoftmax_loss(logits, target, mask=None):
+    """-mean over rows of mask * sum_v target * log_softmax(logits), with the
+    gradient written over ``logits``' storage in the backward (so ``logits``
+    must not be needed after the backward)."""
+    return _LogSoftmaxLoss.apply(logits, target, mask)

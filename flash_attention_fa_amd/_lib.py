@@ -26,7 +26,7 @@ FA_MASK_TTT = 2
 FA_MASK_WINDOW = 3
 
 EXPORTED = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes",
-            "fa_last_error")
+            "fa_last_error", "fa_lsm_loss_fwd", "fa_lsm_loss_bwd")
 
 
 FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2
@@ -59,6 +59,15 @@ class fa_bwd_args(ctypes.Structure):
                          ("o", fa_tensor), ("dout", fa_tensor), ("lse", ctypes.c_void_p),
                          ("dq", fa_tensor), ("dk", fa_tensor), ("dv", fa_tensor),
                          ("mask", fa_mask_desc)]
+
+
+class fa_lsm_loss_args(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("logits", ctypes.c_void_p), ("logits_ss", ctypes.c_int64),
+                ("target", ctypes.c_void_p), ("target_ss", ctypes.c_int64),
+                ("mask", ctypes.c_void_p), ("m", ctypes.c_void_p), ("d", ctypes.c_void_p),
+                ("tsum", ctypes.c_void_p), ("row_loss", ctypes.c_void_p), ("loss", ctypes.c_void_p),
+                ("grad_loss", ctypes.c_void_p)]
 
 
 class FAError(RuntimeError):
@@ -94,6 +103,9 @@ def lib():
         L.fa_bwd_stage.restype = ctypes.c_int
         L.fa_bwd_workspace_bytes.argtypes = [ctypes.POINTER(fa_bwd_args)]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        for name in ("fa_lsm_loss_fwd", "fa_lsm_loss_bwd"):
+            getattr(L, name).argtypes = [ctypes.POINTER(fa_lsm_loss_args), ctypes.c_void_p]
+            getattr(L, name).restype = ctypes.c_int
         L.fa_last_error.argtypes = []
         L.fa_last_error.restype = ctypes.c_char_p
         _lib = L

@@ -335,3 +335,88 @@ fa_status fa_bwd_stage(const fa_bwd_args* a, int stage, void* ws, size_t ws_byte
 }
 
 }  // extern "C"
+
+// ---- soft-target log-softmax loss ------------------------------------------
+
+namespace {
+
+// Byte range of n floats at p (empty when n == 0 or p is null).
+Range span_f(const void* p, int64_t n) {
+  if (p == nullptr || n <= 0) return Range{0, 0, true};
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + (uintptr_t)n * 4, false};
+}
+
+// Checks shared by the loss forward and backward; fills the launch params.
+fa_status check_loss(const fa_lsm_loss_args* a, bool backward, fa::LossParams& p) {
+  const char* fn = backward ? "fa_lsm_loss_bwd" : "fa_lsm_loss_fwd";
+  if (!a) return fail(FA_ERR_INVALID_ARG, "%s: args is NULL", fn);
+  if (a->N < 0) return fail(FA_ERR_INVALID_ARG, "%s: negative N=%d", fn, a->N);
+  if (a->V < 1) return fail(FA_ERR_INVALID_ARG, "%s: V=%d (needs at least one column)", fn, a->V);
+  const int64_t N = a->N, V = a->V;
+  if (N > 0) {
+    if (!a->logits || !a->target) return fail(FA_ERR_INVALID_ARG, "%s: NULL logits or target", fn);
+    if (!a->m || !a->d || !a->tsum) return fail(FA_ERR_INVALID_ARG, "%s: NULL m, d or tsum", fn);
+    if (!backward && !a->row_loss) return fail(FA_ERR_INVALID_ARG, "%s: NULL row_loss", fn);
+    if (backward && !a->grad_loss) return fail(FA_ERR_INVALID_ARG, "%s: NULL grad_loss", fn);
+    if (a->logits_ss < V || a->target_ss < V)
+      return fail(FA_ERR_INVALID_ARG, "%s: row stride below V (logits_ss %lld, target_ss %lld, V %d)", fn,
+                  (long long)a->logits_ss, (long long)a->target_ss, a->V);
+    if (reinterpret_cast<uintptr_t>(a->logits) % 4 || reinterpret_cast<uintptr_t>(a->target) % 4)
+      return fail(FA_ERR_ALIGNMENT, "%s: logits and target must be 4-byte aligned", fn);
+    if ((N - 1) * std::max(a->logits_ss, a->target_ss) + V >= (int64_t(1) << 40))
+      return fail(FA_ERR_UNSUPPORTED, "%s: [N, V] matrices too large", fn);
+  }
+  if (!backward && !a->loss) return fail(FA_ERR_INVALID_ARG, "%s: NULL loss", fn);
+  for (const void* q : {(const void*)a->mask, (const void*)a->m, (const void*)a->d, (const void*)a->tsum,
+                        (const void*)a->row_loss, (const void*)a->loss, (const void*)a->grad_loss})
+    if (reinterpret_cast<uintptr_t>(q) % 4)
+      return fail(FA_ERR_ALIGNMENT, "%s: a per-row array or scalar is not 4-byte aligned", fn);
+  const Range rx = N ? span_f(a->logits, (N - 1) * a->logits_ss + V) : Range{0, 0, true};
+  const Range rt = N ? span_f(a->target, (N - 1) * a->target_ss + V) : Range{0, 0, true};
+  const Range rw = span_f(a->mask, N), rm = span_f(a->m, N), rd = span_f(a->d, N), rs = span_f(a->tsum, N);
+  if (!backward) {
+    const Range rr = span_f(a->row_loss, N), rl = span_f(a->loss, 1);
+    const Range outs[5] = {rm, rd, rs, rr, rl};
+    for (int o = 0; o < 5; ++o) {
+      if (overlap(outs[o], rx) || overlap(outs[o], rt) || overlap(outs[o], rw))
+        return fail(FA_ERR_ALIAS, "%s: an output overlaps logits, target or mask", fn);
+      for (int o2 = 0; o2 < o; ++o2)
+        if (overlap(outs[o], outs[o2])) return fail(FA_ERR_ALIAS, "%s: two outputs overlap", fn);
+    }
+  } else {
+    const Range rg = span_f(a->grad_loss, 1);
+    for (const Range* in : {&rt, &rw, &rm, &rd, &rs, &rg})
+      if (overlap(rx, *in)) return fail(FA_ERR_ALIAS, "%s: logits (the gradient's buffer) overlap an input", fn);
+  }
+  p = fa::LossParams{a->N, a->V, a->logits, a->logits_ss, a->target, a->target_ss, a->mask,
+                     a->m, a->d, a->tsum, a->row_loss, a->loss, a->grad_loss};
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_lsm_loss_fwd(const fa_lsm_loss_args* a, hipStream_t stream) {
+  fa::LossParams p{};
+  fa_status st = check_loss(a, false, p);
+  if (st != FA_OK) return st;
+  if ((st = check_device())) return st;
+  hipError_t e = fa::launch_lsm_loss_fwd(p, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_lsm_loss_fwd launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+fa_status fa_lsm_loss_bwd(const fa_lsm_loss_args* a, hipStream_t stream) {
+  fa::LossParams p{};
+  fa_status st = check_loss(a, true, p);
+  if (st != FA_OK) return st;
+  if (a->N == 0) return FA_OK;   // nothing to write
+  if ((st = check_device())) return st;
+  hipError_t e = fa::launch_lsm_loss_bwd(p, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_lsm_loss_bwd launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+}  // extern "C"

@@ -56,6 +56,23 @@ inline bool dkdv_split(int B, int Hkv, int keys) {
 // Backward stages: Delta = rowsum(dO * O), then the dK/dV and dQ kernels
 // (independent of each other once Delta exists).
 enum { STAGE_DELTA = 0, STAGE_DKDV = 1, STAGE_DQ = 2 };
+// Soft-target log-softmax loss (fa_lsm_loss_fwd / _bwd), validated by the
+// dispatcher.
+struct LossParams {
+  int N, V;
+  float* x;              // logits [N, V] (backward: overwritten with the gradient)
+  int64_t x_ss;
+  const float* t;        // targets [N, V]
+  int64_t t_ss;
+  const float* w;        // row weights [N] or nullptr (all 1)
+  float *m, *d, *tsum;   // per-row max, normaliser, target sum
+  float* row;            // per-row loss term
+  float* loss;           // [1] mean
+  const float* g;        // [1] upstream gradient of the mean
+};
+hipError_t launch_lsm_loss_fwd(const LossParams& p, hipStream_t s);
+hipError_t launch_lsm_loss_bwd(const LossParams& p, hipStream_t s);
+
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t s);
 hipError_t launch_bwd_bf16(const Params& p, int stage, hipStream_t s);
 hipError_t launch_fwd_f32(const Params& p, hipStream_t s);

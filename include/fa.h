@@ -174,6 +174,58 @@ typedef enum {
 fa_status fa_bwd_stage(const fa_bwd_args* args, int stage, void* ws,
                        size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Soft-target log-softmax loss, the loss EAGLE3 training takes after the
+ * draft model's attention and LM head ("Flex Attention and Triton,
+ * Supporting Long Context Training in SpecForge", section "In-place Gradient
+ * Calculation").  For N rows (batch x positions) of V logits x, soft targets
+ * t and per-row mask weights w:
+ *
+ *   m_i = max_v x_iv,  d_i = sum_v exp(x_iv - m_i),  tsum_i = sum_v t_iv
+ *   row_i = -w_i * sum_v t_iv * (x_iv - m_i - ln d_i)
+ *   loss  = (1/N) * sum_i row_i          (masked rows count in the mean)
+ *   dloss/dx_iv = w_i / N * (exp(x_iv - m_i) / d_i * tsum_i - t_iv)
+ *
+ * The forward reads each row once (an online max and normaliser, as the
+ * page's kernel keeps m and d) and saves m, d, tsum; the backward writes the
+ * gradient, times the upstream gradient, over the logits in place (the
+ * page's memory saving: no second [N, V] buffer).  All arithmetic is fp32.
+ * The mean is a fixed-order sum, so reruns are bitwise identical. */
+typedef struct {
+  int32_t N;                 /* rows, >= 0 */
+  int32_t V;                 /* vocabulary size (columns), >= 1 */
+  float* logits;             /* [N, V], row stride logits_ss elements: read by the
+                                forward; overwritten with the gradient by the
+                                backward (in place) */
+  int64_t logits_ss;
+  const float* target;       /* [N, V] soft targets, row stride target_ss */
+  int64_t target_ss;
+  const float* mask;         /* [N] row weights w_i, or NULL for all 1 */
+  float* m;                  /* [N] row max: forward writes, backward reads */
+  float* d;                  /* [N] sum_v exp(x_iv - m_i): forward writes, backward reads */
+  float* tsum;               /* [N] sum_v t_iv: forward writes, backward reads */
+  float* row_loss;           /* [N] row_i: forward writes (backward ignores) */
+  float* loss;               /* [1] the mean loss: forward writes (backward ignores) */
+  const float* grad_loss;    /* [1] upstream gradient of loss: backward reads
+                                (forward ignores) */
+} fa_lsm_loss_args;
+
+/* Forward of the loss: writes m, d, tsum, row_loss and loss.  All pointers
+ * are device pointers, 4-byte aligned (else FA_ERR_ALIGNMENT); row strides
+ * are at least V (rows that start 16-byte aligned, and whose logits and
+ * target rows sit at the same offset from a 16-byte boundary, are read
+ * with 16-byte loads; others element by element).  The
+ * outputs must not overlap logits, target, mask or each other
+ * (FA_ERR_ALIAS).  N = 0 writes loss = 0 and nothing else.  Validation runs
+ * before any launch; asynchronous on `stream`. */
+fa_status fa_lsm_loss_fwd(const fa_lsm_loss_args* args, hipStream_t stream);
+
+/* Backward of the loss: overwrites logits with grad_loss[0] * dloss/dx, from
+ * the m, d, tsum the forward wrote for these logits and targets (logits must
+ * still hold the forward's values).  Same alignment and aliasing rules (m,
+ * d, tsum and grad_loss must not overlap logits). */
+fa_status fa_lsm_loss_bwd(const fa_lsm_loss_args* args, hipStream_t stream);
+
 /* Text describing the last non-OK status returned on this thread
  * ("" if none).  The pointer stays valid until the thread's next call. */
 const char* fa_last_error(void);

@@ -121,3 +121,46 @@ def kv_valid_tensor(w: Workload, device="cpu"):
     if w.kv_valid is None:
         return None
     return torch.tensor(list(w.kv_valid), dtype=torch.int32, device=device)
+
+
+# ---- soft-target log-softmax loss workloads ---------------------------------
+# The (B, T, V) configurations of the SpecForge page's loss benchmark (section
+# "In-place Gradient Calculation").  Recipe: a generator on ``device`` seeded
+# with ``seed`` draws the logits, float32 N(0, 1) times ``logit_std`` (4: the
+# page gives no distribution), then u ~ U(0, 1), and the soft targets are
+# u**8 normalised over the vocabulary (a peaked distribution, made without
+# the loss's own arithmetic).  The first ``prompt_frac`` of each sequence's
+# positions have mask 0 (the prompt, which EAGLE3 masks out), the rest 1.
+
+@dataclass(frozen=True)
+class LossWorkload:
+    name: str
+    B: int
+    T: int
+    V: int
+    logit_std: float = 4.0
+    prompt_frac: float = 0.1
+
+    @property
+    def N(self):
+        return self.B * self.T
+
+
+def loss_workloads():
+    return [LossWorkload(f"lsm_loss_B{B}_T{T}_V{V}", B, T, V)
+            for B, T, V in ((1, 1024, 32000), (1, 4096, 32000), (1, 4096, 64000),
+                            (1, 8192, 32000), (1, 8192, 64000), (1, 16384, 32000))]
+
+
+LOSS_HEADLINE = loss_workloads()[-1]
+
+
+def make_loss_inputs(w: LossWorkload, seed: int = 0, device="cpu"):
+    """(logits [N, V], target [N, V], mask [N]), float32 on ``device``."""
+    g = torch.Generator(device).manual_seed(seed)
+    x = torch.randn(w.N, w.V, generator=g, device=device) * w.logit_std
+    u = torch.rand(w.N, w.V, generator=g, device=device) ** 8
+    t = u / u.sum(dim=1, keepdim=True)
+    pos = torch.arange(w.T, device=device).repeat(w.B)
+    mask = (pos >= int(w.prompt_frac * w.T)).to(torch.float32)
+    return x, t, mask
