@@ -121,6 +121,9 @@ def kernel_flops(w):
     return {"fwd": 4 * w.D * pairs, "dkdv": 8 * w.D * pairs, "dq": 2 * w.D * pairs}
 
 
+# Sources compiled into the loss kernels (the same rule for their summary).
+LOSS_SOURCES = ("flash_attention_fa_amd/csrc/fa_loss.hip", "flash_attention_fa_amd/csrc/fa_internal.h",
+                "flash_attention_fa_amd/build.py")
 # Sources compiled into the dK/dV kernel: a counter summary taken on other
 # sources no longer describes it.
 DKDV_SOURCES = ("flash_attention_fa_amd/csrc/fa_bwd.hip", "flash_attention_fa_amd/csrc/fa_device.h",
@@ -135,10 +138,10 @@ def sources_sha256(paths):
     return h.hexdigest()
 
 
-def measured_traffic(kernel, workload, sources):
-    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.md, or
+def measured_traffic(kernel, workload, sources, prefix="traffic"):
+    """HBM bytes per launch from profiles/<prefix>_<kernel>_<workload>.md, or
     None when there is no summary or it was taken on other sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{kernel}_{workload}.md" if kernel else f"{prefix}_{workload}.md")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -332,7 +335,10 @@ def loss_bench(fa, w, dev, steps, warmup, cpu):
            "bwd": {"ms_median": round(b_ms, 4), "gbs": round(gbs(bb, b_ms), 1)},
            "roofline": {"kernel": "lsm_loss_fwd_kernel + lsm_loss_bwd_kernel (+ the mean)", "bound": "hbm",
                         "achieved": round(st_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(st_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                        "frac": round(st_gbs / PEAK_HBM_GBS, 4),
+                        "traffic": measured_traffic(None, w.name, LOSS_SOURCES, prefix="kernels"),
+                        "traffic_unit": "HBM bytes per step (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated, "
+                                        "forward and backward kernels)"},
            "memory": {"peak_above_inputs_bytes": int(peak), "inputs_bytes": int(mem0),
                       "explicit_chain_intermediates_bytes": 4 * nv * 4}}
     if cpu:
