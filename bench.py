@@ -99,9 +99,19 @@ def pair_count(w):
     return out
 
 
+def frozen_pair_count(w):
+    """Allowed pairs (per head, summed over batch) whose key is frozen: their
+    dK/dV products are not computed (the prefix workloads)."""
+    if not getattr(w, "frozen", 0):
+        return 0
+    return sum(pair_count(w.with_(Skv=min(w.Skv, w.frozen), kv_valid=None if w.kv_valid is None else
+                                  tuple(min(x, w.frozen) for x in w.kv_valid))))
+
+
 def flops(w):
     pairs = sum(pair_count(w)) * w.Hq
-    return 4 * w.D * pairs, 10 * w.D * pairs
+    fz = frozen_pair_count(w) * w.Hq
+    return 4 * w.D * pairs, 10 * w.D * pairs - 4 * w.D * fz
 
 
 def algorithmic_bytes(w):
@@ -118,7 +128,8 @@ def algorithmic_bytes(w):
 def kernel_flops(w):
     """Algorithmic flops of one launch of each kernel."""
     pairs = sum(pair_count(w)) * w.Hq
-    return {"fwd": 4 * w.D * pairs, "dkdv": 8 * w.D * pairs, "dq": 2 * w.D * pairs}
+    fz = frozen_pair_count(w) * w.Hq
+    return {"fwd": 4 * w.D * pairs, "dkdv": 8 * w.D * (pairs - fz), "dq": 2 * w.D * pairs}
 
 
 # Sources compiled into the loss kernels (the same rule for their summary).
@@ -220,7 +231,7 @@ def measure(fa, w, dev, steps, warmup, inputs):
     fws = torch.empty(max(1, fa.fa_fwd_workspace_bytes(qg, kg)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     kw = dict(mask_kind=w.kind, causal_shift=w.shift, kv_valid=kvv, scale=w.scale, window=w.window,
-              stream=stream)
+              frozen_keys=w.frozen, stream=stream)
 
     def fwd():
         fa.fa_fwd(qg, kg, vg, out=o, lse=lse, workspace=fws, **kw)

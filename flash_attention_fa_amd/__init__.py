@@ -55,7 +55,7 @@ def _tensor(t):
     return _lib.fa_tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
-def _mask(kind, causal_shift, kv_valid, window=None):
+def _mask(kind, causal_shift, kv_valid, window=None, frozen_keys=0):
     ptr = None
     if kv_valid is not None:
         if kv_valid.dtype != torch.int32 or not kv_valid.is_contiguous():
@@ -64,7 +64,7 @@ def _mask(kind, causal_shift, kv_valid, window=None):
     if int(kind) == WINDOW and window is None:
         raise FAError(_lib.FA_ERR_INVALID_ARG, "mask_kind WINDOW needs window=(left, right)")
     left, right = (0, 0) if window is None else (int(window[0]), int(window[1]))
-    return _lib.fa_mask_desc(int(kind), int(causal_shift), ptr, left, right)
+    return _lib.fa_mask_desc(int(kind), int(causal_shift), ptr, left, right, int(frozen_keys))
 
 
 def _stream(t, stream):
@@ -95,7 +95,7 @@ def fa_fwd_workspace_bytes(q, k):
 
 
 def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=None, scale=None,
-           out=None, lse=None, workspace=None, stream=None):
+           out=None, lse=None, workspace=None, stream=None, frozen_keys=0):
     """Forward attention.  Returns (O [B,Hq,Sq,D] in q's dtype, LSE [B,Hq,Sq] fp32).
 
     ``workspace`` (uint8 device tensor of at least ``fa_fwd_workspace_bytes``
@@ -109,7 +109,7 @@ def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=Non
     a.scale = 0.0 if scale is None else float(scale)
     a.q, a.k, a.v, a.o = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
     a.lse = lse.data_ptr()
-    a.mask = _mask(mask_kind, causal_shift, kv_valid, window)
+    a.mask = _mask(mask_kind, causal_shift, kv_valid, window, frozen_keys)
     for t in (k, v, out):
         if t.dtype != q.dtype:
             raise FAError(_lib.FA_ERR_INVALID_ARG, "q, k, v and out must share one dtype")
@@ -121,7 +121,8 @@ def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=Non
     return out, lse
 
 
-def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window=None):
+def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window=None,
+              frozen_keys=0):
     B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
     a = _lib.fa_bwd_args()
     a.dtype = _dtype_code(q)
@@ -131,7 +132,7 @@ def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_val
     a.lse = None if lse is None else lse.data_ptr()
     if dq is not None:
         a.dq, a.dk, a.dv = _tensor(dq), _tensor(dk), _tensor(dv)
-    a.mask = _mask(mask_kind, causal_shift, kv_valid, window)
+    a.mask = _mask(mask_kind, causal_shift, kv_valid, window, frozen_keys)
     return a
 
 
@@ -141,12 +142,12 @@ def fa_bwd_workspace_bytes(q, k, *, mask_kind=FULL):
     B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
     a.dtype = _dtype_code(q)
     a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
-    a.mask = _lib.fa_mask_desc(int(mask_kind), 0, None, 0, 0)
+    a.mask = _lib.fa_mask_desc(int(mask_kind), 0, None, 0, 0, 0)
     return int(_lib.lib().fa_bwd_workspace_bytes(a))
 
 
 def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=None,
-           scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+           scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None, frozen_keys=0):
     """Backward attention.  Returns (dQ, dK, dV) in q's dtype."""
     if dq is None:
         dq = torch.empty_like(q, memory_format=torch.contiguous_format)
@@ -154,7 +155,8 @@ def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=No
         dk = torch.empty_like(k, memory_format=torch.contiguous_format)
     if dv is None:
         dv = torch.empty_like(v, memory_format=torch.contiguous_format)
-    a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window)
+    a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window,
+                  frozen_keys)
     need = int(_lib.lib().fa_bwd_workspace_bytes(a))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -165,13 +167,14 @@ def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=No
 
 
 def fa_bwd_stage(stage, q, k, v, o, lse, dout, dq, dk, dv, workspace, *, mask_kind=FULL,
-                 causal_shift=0, kv_valid=None, window=None, scale=None, stream=None):
+                 causal_shift=0, kv_valid=None, window=None, scale=None, stream=None, frozen_keys=0):
     """One stage (FA_BWD_DELTA, FA_BWD_DKDV or FA_BWD_DQ) of ``fa_bwd``.
 
     The caller provides the outputs and the workspace; DKDV and DQ read the
     Delta that a DELTA stage left in ``workspace``.
     """
-    a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window)
+    a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window,
+                  frozen_keys)
     _lib.check(_lib.lib().fa_bwd_stage(a, int(stage), workspace.data_ptr(),
                                        workspace.numel() * workspace.element_size(),
                                        _stream(q, stream)))
@@ -183,31 +186,34 @@ def fa_last_error():
 
 class _Attention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, mask_kind, causal_shift, kv_valid, scale, window):
+    def forward(ctx, q, k, v, mask_kind, causal_shift, kv_valid, scale, window, frozen_keys):
         o, lse = fa_fwd(q, k, v, mask_kind=mask_kind, causal_shift=causal_shift,
                         kv_valid=kv_valid, window=window, scale=scale)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.cfg = (mask_kind, causal_shift, kv_valid, scale, window)
+        ctx.cfg = (mask_kind, causal_shift, kv_valid, scale, window, frozen_keys)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        mask_kind, causal_shift, kv_valid, scale, window = ctx.cfg
+        mask_kind, causal_shift, kv_valid, scale, window, frozen_keys = ctx.cfg
         if do.stride(-1) != 1:
             do = do.contiguous()
         dq, dk, dv = fa_bwd(q, k, v, o, lse, do, mask_kind=mask_kind, causal_shift=causal_shift,
-                            kv_valid=kv_valid, window=window, scale=scale)
-        return dq, dk, dv, None, None, None, None, None
+                            kv_valid=kv_valid, window=window, scale=scale, frozen_keys=frozen_keys)
+        return dq, dk, dv, None, None, None, None, None, None
 
 
-def attention(q, k, v, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None, window=None):
+def attention(q, k, v, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None, window=None,
+              frozen_keys=0):
     """Fused attention O = softmax(scale q k^T + mask) v, differentiable.
 
     ``scale`` defaults to 1/sqrt(D); ``window`` = (left, right) for WINDOW.
-    Saves only O and LSE for the backward.
+    A negative ``causal_shift`` -P with CAUSAL shows every query a P-key
+    prefix; ``frozen_keys`` = P then leaves the prefix's dK, dV at zero
+    without computing them.  Saves only O and LSE for the backward.
     """
-    return _Attention.apply(q, k, v, mask_kind, causal_shift, kv_valid, scale, window)
+    return _Attention.apply(q, k, v, mask_kind, causal_shift, kv_valid, scale, window, frozen_keys)
 
 
 def default_scale(D):

@@ -76,8 +76,10 @@ fa_status check_shape(const Shape& s, const fa_mask_desc& m) {
     return fail(FA_ERR_UNSUPPORTED, "unknown mask kind %d", m.kind);
   if (m.kind == FA_MASK_WINDOW && (m.window_left < 0 || m.window_right < 0))
     return fail(FA_ERR_INVALID_ARG, "negative window (left %d, right %d)", m.window_left, m.window_right);
-  if (m.causal_shift < 0)
-    return fail(FA_ERR_INVALID_ARG, "negative causal_shift %d", m.causal_shift);
+  if (m.causal_shift < 0 && m.kind == FA_MASK_TTT)
+    return fail(FA_ERR_INVALID_ARG, "negative causal_shift %d with the TTT mask", m.causal_shift);
+  if (m.frozen_keys < 0)
+    return fail(FA_ERR_INVALID_ARG, "negative frozen_keys %d", m.frozen_keys);
   if (m.kind == FA_MASK_TTT) {
     if (s.Sq <= 0 && s.Skv != 0)
       return fail(FA_ERR_INVALID_ARG, "TTT mask needs Sq > 0 (Sq is the step length)");
@@ -148,6 +150,7 @@ void fill_common(fa::Params& p, const Shape& s, float scale, const fa_mask_desc&
   p.mask.kv_valid = m.kv_valid;
   p.mask.wl = m.kind == FA_MASK_WINDOW ? m.window_left : 0;
   p.mask.wr = m.kind == FA_MASK_WINDOW ? m.window_right : 0;
+  p.mask.frozen = m.frozen_keys;
 }
 
 // One float32 [B, Hq, Sq] array, rounded up to 256 bytes.

@@ -642,6 +642,7 @@ dkdv_kernel(Params p) {
 
   int qlo, qhi;
   query_hull(m, ka, kbnd, qlo, qhi);
+  if (kbnd <= p.mask.frozen) qhi = qlo;   // every key frozen: no steps, zeros written
   const int t_first = qlo < qhi ? qlo / TQ : 0;
   const int t_last = qlo < qhi ? (qhi + TQ - 1) / TQ : 0;
   const int ntile = t_last - t_first;
@@ -806,6 +807,10 @@ dkdv_kernel(Params p) {
         for (int i = 0; i < 16; ++i) acc[c][i] += X[((kblk * NDB + c) * 16 + i) * 64 + lane];
       if (key < p.Skv) {
         const float sc = which == 0 ? p.scale : 1.0f;
+        if (key < p.mask.frozen) {   // a frozen key: written as exact zeros
+#pragma unroll
+          for (int c = 0; c < NDB; ++c) acc[c] = f32x16{};
+        }
         bf16* dst_row = (which == 0 ? DKg + (int64_t)key * p.dk.ss : DVg + (int64_t)key * p.dv.ss);
 #pragma unroll
         for (int c = 0; c < NDB; ++c)
@@ -926,6 +931,7 @@ dkdv_split_kernel(Params p) {
 
   int qlo, qhi;
   query_hull(m, ka, kbnd, qlo, qhi);
+  if (kbnd <= p.mask.frozen) qhi = qlo;   // every key frozen: no steps, zeros written
   const int t_first = qlo < qhi ? qlo / TQ : 0;
   const int t_last = qlo < qhi ? (qhi + TQ - 1) / TQ : 0;
   // The block's (query tile, head) steps, tiles from the last down with the
@@ -1113,6 +1119,13 @@ dkdv_split_kernel(Params p) {
   // Without SPLIT: dK = scale * dK^T sums, dV = dV^T sums, rounded to bf16;
   // lane (key, hh) holds d = 32c + 8g + 4hh + u.  Keys no query attends
   // hold exact zeros (every product added 0).
+  if (key < p.mask.frozen) {   // a frozen key: written as exact zeros
+#pragma unroll
+    for (int c = 0; c < NDB; ++c) {
+      dka[c] = f32x16{};
+      dva[c] = f32x16{};
+    }
+  }
   if (!SPLIT) {
     if (key < nkeys) {
       bf16* DK = static_cast<bf16*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh + (int64_t)key * p.dk.ss;
@@ -1228,6 +1241,10 @@ __global__ void __launch_bounds__(256) ttt_dkdv_kernel(Params p) {
   }
   bf16* DK = static_cast<bf16*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh + (int64_t)j * p.dk.ss + 8 * sub;
   bf16* DV = static_cast<bf16*>(const_cast<void*>(p.dv.ptr)) + b * p.dv.sb + hk * p.dv.sh + (int64_t)j * p.dv.ss + 8 * sub;
+  if (j < p.mask.frozen) {   // a frozen key: written as exact zeros
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dk[e] = dv[e] = 0.f;
+  }
   const float sc = p.scale;
   *reinterpret_cast<bf16x8*>(DK) = cat8(to_bf16x4(dk[0] * sc, dk[1] * sc, dk[2] * sc, dk[3] * sc),
                                         to_bf16x4(dk[4] * sc, dk[5] * sc, dk[6] * sc, dk[7] * sc));

@@ -254,16 +254,16 @@ struct MaskB {
   int wl, wr;                        // WINDOW band: keys before / after the diagonal
 };
 
-// Shift and window are clamped to 2 (Sq + Skv): past that the predicate no
-// longer changes (a larger shift already leaves every row empty, a wider
-// window already covers every key), and the band arithmetic stays far from
-// int overflow.
+// Shift and window are clamped to +-2 (Sq + Skv): past that the predicate no
+// longer changes (a larger shift already leaves every row empty, a more
+// negative one already shows every row every key, a wider window already
+// covers every key), and the band arithmetic stays far from int overflow.
 // `kv` is the batch entry's valid key count (any int; clamped here).
 __host__ __device__ __forceinline__ MaskB make_mask(int kind, int shift, int Sq, int Skv, int kv, int wl, int wr) {
   MaskB m;
   const int lim = 2 * (Sq + Skv);
   m.kind = kind;
-  m.shift = shift < lim ? shift : lim;
+  m.shift = shift < lim ? (shift > -lim ? shift : -lim) : lim;
   m.Sq = Sq;
   m.Skv = Skv;
   m.L = Sq;

@@ -235,8 +235,12 @@ __global__ void __launch_bounds__(F_ROWS) dkdv_f32_kernel(Params p) {
   if (j < p.Skv) {
     float* DKg = static_cast<float*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh + (int64_t)j * p.dk.ss;
     float* DVg = static_cast<float*>(const_cast<void*>(p.dv.ptr)) + b * p.dv.sb + hk * p.dv.sh + (int64_t)j * p.dv.ss;
+    const bool frozen = j < p.mask.frozen;   // written as exact zeros
 #pragma unroll
-    for (int d = 0; d < D; ++d) { DKg[d] = dk[d] * p.scale; DVg[d] = dv[d]; }
+    for (int d = 0; d < D; ++d) {
+      DKg[d] = frozen ? 0.0f : dk[d] * p.scale;
+      DVg[d] = frozen ? 0.0f : dv[d];
+    }
   }
 }
 

@@ -13,9 +13,10 @@ struct Tensor {
 
 struct Mask {
   int kind;            // 0 FULL, 1 CAUSAL, 2 TTT, 3 WINDOW
-  int shift;           // causal shift (>= 0)
+  int shift;           // causal shift (negative: a prefix of -shift keys before the diagonal)
   const int* kv_valid; // device [B] or nullptr
   int wl, wr;          // WINDOW: keys allowed before / after the (shifted) diagonal
+  int frozen;          // keys below it get dK = dV = 0, not computed
 };
 
 // Keys per V^T tile of the forward workspace (the forward's key tile).

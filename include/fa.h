@@ -34,6 +34,11 @@
  *                   Measurement discipline", names windowed self-attention
  *                   among the diffusion trainer's geometries without fixing
  *                   the window's form).
+ *   Prefix (the rectangular-plus-causal mask a frozen KV prefix needs; the
+ *   ggml playbook's per-trainer checklist names it for a trainer with a
+ *   frozen KV prefix): FA_MASK_CAUSAL with causal_shift = -P, Skv = P + Sq,
+ *   so every query sees keys [0, P) and the causal part behind them;
+ *   frozen_keys = P then skips the gradients of the frozen prefix.
  *   A query row with no allowed key gets O = 0 and LSE = 0, and contributes
  *   no gradient; a key no query may attend gets dK = dV = 0 exactly (ggml
  *   playbook, "6. Trap list", items 8 and 9).
@@ -92,12 +97,20 @@ typedef struct {
 
 typedef struct {
   int32_t kind;              /* fa_mask_kind */
-  int32_t causal_shift;      /* >= 0; used by CAUSAL, WINDOW and TTT's step-0 part */
+  int32_t causal_shift;      /* used by CAUSAL, WINDOW and TTT's step-0 part; >= 0
+                                for TTT, any value for CAUSAL and WINDOW (a negative
+                                shift -P shows every query the first P keys before
+                                the diagonal: CAUSAL with Skv = P + Sq is a causal
+                                sequence behind a P-key prefix) */
   const int32_t* kv_valid;   /* device int32 [B] valid key count per batch
                                 (clamped to [0, Skv] for FULL/CAUSAL/WINDOW and
                                 to [0, Sq] for TTT), or NULL = all keys valid */
   int32_t window_left;       /* WINDOW only: >= 0 keys before the diagonal */
   int32_t window_right;      /* WINDOW only: >= 0 keys after the diagonal */
+  int32_t frozen_keys;       /* >= 0: keys j < frozen_keys are frozen (a prefix
+                                whose K/V are not trained): the backward writes
+                                dK = dV = 0 there and does not compute them; the
+                                forward and dQ are unchanged.  0 = none */
 } fa_mask_desc;
 
 typedef struct {

@@ -6,7 +6,7 @@ Tolerances (per tensor, over rows that have at least one allowed key):
   * bfloat16: max|err| / max|ref| <= 2e-2 on O and <= 5e-2 on dQ, dK, dV,
     and max |err| <= 1e-2 on LSE.
 Rows with no allowed key must hold exactly O = 0, LSE = 0, dQ = 0, and keys
-no query may attend must hold exactly dK = dV = 0.
+no query may attend, and frozen keys, must hold exactly dK = dV = 0.
 """
 import sys
 
@@ -30,14 +30,14 @@ def to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(q, k, v, do, kind, shift=0, kv_valid=None, scale=None, device="cuda", window=None):
+def run_gpu(q, k, v, do, kind, shift=0, kv_valid=None, scale=None, device="cuda", window=None, frozen=0):
     """Forward + backward through the library; returns numpy float64 arrays."""
     qg, kg, vg, dog = (x.to(device) for x in (q, k, v, do))
     kvv = None if kv_valid is None else torch.tensor(list(kv_valid), dtype=torch.int32, device=device)
     o, lse = fa.fa_fwd(qg, kg, vg, mask_kind=kind, causal_shift=shift, kv_valid=kvv, scale=scale,
-                       window=window)
+                       window=window, frozen_keys=frozen)
     dq, dk, dv = fa.fa_bwd(qg, kg, vg, o, lse, dog, mask_kind=kind, causal_shift=shift,
-                           kv_valid=kvv, scale=scale, window=window)
+                           kv_valid=kvv, scale=scale, window=window, frozen_keys=frozen)
     torch.cuda.synchronize()
     return dict(O=to_np(o), LSE=to_np(lse), dQ=to_np(dq), dK=to_np(dk), dV=to_np(dv))
 
@@ -53,7 +53,7 @@ def structure(kind, B, Sq, Skv, shift, kv_valid, window=None):
     return rows, keys
 
 
-def compare(got, ref, dtype, kind, shift=0, kv_valid=None, label="", zero_ref=(), window=None):
+def compare(got, ref, dtype, kind, shift=0, kv_valid=None, label="", zero_ref=(), window=None, frozen=0):
     """Assert the tolerance bar; returns the error summary dict.
 
     ``zero_ref`` names tensors whose exact value is identically zero (e.g.
@@ -63,6 +63,7 @@ def compare(got, ref, dtype, kind, shift=0, kv_valid=None, label="", zero_ref=()
     B, Hq, Sq, D = ref["O"].shape
     Skv = ref["dK"].shape[2]
     rows, keys = structure(kind, B, Sq, Skv, shift, kv_valid, window)
+    keys[:, :frozen] = False      # frozen keys: dK = dV = 0 exactly
     errs = {}
     for name in ("O", "LSE", "dQ", "dK", "dV"):
         g, r = got[name], ref[name]
@@ -100,13 +101,13 @@ def compare(got, ref, dtype, kind, shift=0, kv_valid=None, label="", zero_ref=()
 
 
 def check_case(q, k, v, do, kind, dtype, shift=0, kv_valid=None, scale=None, label="",
-               zero_ref=(), ref_inputs=None, window=None):
+               zero_ref=(), ref_inputs=None, window=None, frozen=0):
     say(f"[parity] {label} q{tuple(q.shape)} k{tuple(k.shape)} kind={kind} shift={shift} "
-        f"kv_valid={kv_valid} window={window} dtype={dtype}")
-    got = run_gpu(q, k, v, do, kind, shift, kv_valid, scale, window=window)
+        f"kv_valid={kv_valid} window={window} frozen={frozen} dtype={dtype}")
+    got = run_gpu(q, k, v, do, kind, shift, kv_valid, scale, window=window, frozen=frozen)
     ref_in = (q, k, v, do) if ref_inputs is None else ref_inputs
     ref = attention_ref(*(x.double().numpy() for x in ref_in), kind, shift, kv_valid, scale,
                         window=window)
-    errs = compare(got, ref, dtype, kind, shift, kv_valid, label, zero_ref, window)
+    errs = compare(got, ref, dtype, kind, shift, kv_valid, label, zero_ref, window, frozen)
     say(f"[parity] {label} ok {errs}")
     return errs

@@ -34,7 +34,8 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layout_matches_header():
     # offsets a C compiler gives the structs of fa.h on x86-64
     assert ctypes.sizeof(_lib.fa_tensor) == 32
-    assert ctypes.sizeof(_lib.fa_mask_desc) == 24
+    assert ctypes.sizeof(_lib.fa_mask_desc) == 32
+    assert _lib.fa_mask_desc.frozen_keys.offset == 24
     assert _lib.fa_mask_desc.kv_valid.offset == 8 and _lib.fa_mask_desc.window_right.offset == 20
     assert _lib.fa_fwd_args.q.offset == 32
     assert _lib.fa_fwd_args.lse.offset == 32 + 4 * 32
@@ -48,13 +49,14 @@ def _t(slot, B, H, S, D, eb=2, strides=None):
     return _lib.fa_tensor(BASE + slot * GAP, *st)
 
 
-def fwd_args(B=1, Hq=4, Hkv=2, Sq=64, Skv=64, D=64, dtype=_lib.FA_BF16, kind=1, shift=0, window=(0, 0)):
+def fwd_args(B=1, Hq=4, Hkv=2, Sq=64, Skv=64, D=64, dtype=_lib.FA_BF16, kind=1, shift=0, window=(0, 0),
+             frozen=0):
     a = _lib.fa_fwd_args()
     a.dtype, a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = dtype, B, Hq, Hkv, Sq, Skv, D
     a.scale = 0.0
     a.q, a.k, a.v, a.o = _t(0, B, Hq, Sq, D), _t(1, B, Hkv, Skv, D), _t(2, B, Hkv, Skv, D), _t(3, B, Hq, Sq, D)
     a.lse = BASE + 4 * GAP
-    a.mask = _lib.fa_mask_desc(kind, shift, None, *window)
+    a.mask = _lib.fa_mask_desc(kind, shift, None, *window, frozen)
     return a
 
 
@@ -107,10 +109,20 @@ FWD_CASES = [
     ("gqa not dividing", dict(Hq=6, Hkv=4), _lib.FA_ERR_INVALID_ARG, "multiple of Hkv"),
     ("zero heads", dict(Hq=0), _lib.FA_ERR_INVALID_ARG, "non-positive"),
     ("negative S", dict(Sq=-1), _lib.FA_ERR_INVALID_ARG, "negative size"),
-    ("negative shift", dict(shift=-2), _lib.FA_ERR_INVALID_ARG, "causal_shift"),
+    ("negative shift with TTT", dict(kind=2, Sq=64, Skv=128, shift=-2), _lib.FA_ERR_INVALID_ARG, "causal_shift"),
+    ("negative frozen_keys", dict(frozen=-1), _lib.FA_ERR_INVALID_ARG, "frozen_keys"),
     ("ttt skv not multiple", dict(kind=2, Sq=64, Skv=100), _lib.FA_ERR_INVALID_ARG, "multiple of Sq"),
     ("negative window", dict(kind=3, window=(4, -1)), _lib.FA_ERR_INVALID_ARG, "negative window"),
 ]
+
+
+def test_prefix_masks_are_accepted():
+    # a negative shift (a prefix before the diagonal) with CAUSAL and WINDOW,
+    # and frozen keys, pass validation (and fail only for want of a device)
+    for kw in (dict(kind=1, shift=-16, Skv=80), dict(kind=3, shift=-4, window=(8, 0)),
+               dict(kind=1, shift=-16, Skv=80, frozen=16)):
+        st, msg = fwd(fwd_args(**kw))
+        assert st == _lib.FA_ERR_HIP, (kw, msg)
 
 
 @pytest.mark.parametrize("name,kw,status,text", FWD_CASES, ids=[c[0] for c in FWD_CASES])

@@ -396,3 +396,33 @@ def test_window_predicate_brute_force():
         for j in range(Skv):
             expect = (i - shift - left <= j <= i - shift + right) and j < seq
             assert A[i, j] == expect, (i, j)
+
+
+# --------------------------------------------------------------------------
+# Prefix: CAUSAL with a negative shift -P (every query sees P prefix keys,
+# then the causal part behind them)
+
+@pytest.mark.parametrize("Hq,Hkv,Sq,P", [(2, 2, 11, 5), (4, 2, 16, 16), (8, 1, 9, 1)])
+def test_prefix_matches_torch_sdpa_block_mask(Hq, Hkv, Sq, P):
+    # the mask built as blocks: ones for the prefix columns beside a
+    # lower-triangular block for the sequence (torch.ones, torch.tril)
+    B, D = 2, 8
+    Skv = P + Sq
+    q, k, v = _rand((B, Hq, Sq, D), 90), _rand((B, Hkv, Skv, D), 91), _rand((B, Hkv, Skv, D), 92)
+    do = _rand((B, Hq, Sq, D), 93)
+    mask = torch.cat([torch.ones(Sq, P, dtype=torch.bool), torch.ones(Sq, Sq, dtype=torch.bool).tril()], dim=1)
+    r = attention_ref(q, k, v, do, CAUSAL, -P)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, enable_gqa=Hq != Hkv)
+    out.backward(torch.tensor(do))
+    np.testing.assert_allclose(r["O"], out.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(r["dQ"], tq.grad.numpy(), atol=1e-11)
+    for name, t in (("dK", tk), ("dV", tv)):
+        assert np.abs(t.grad.numpy()[:, :, :P]).max() > 1e-3   # the prefix keys get gradient
+        np.testing.assert_allclose(r[name], t.grad.numpy(), atol=1e-11, err_msg=name)
+    # the predicate, pair by pair: j < P, or j - P <= i
+    A = allowed(CAUSAL, Sq, Skv, -P)
+    for i in range(Sq):
+        for j in range(Skv):
+            assert A[i, j] == (j < P or j - P <= i), (i, j)
+    assert allowed_pair_count(CAUSAL, Sq, Skv, -P) == Sq * P + Sq * (Sq + 1) // 2

@@ -279,3 +279,45 @@ def test_bf16_many_workgroups_nan_padding():
     dirty = run_gpu(q, k2, v2, do, FULL, 0, kv_valid)
     for nm in ("O", "LSE", "dQ", "dK", "dV"):
         assert np.array_equal(clean[nm], dirty[nm]), nm
+
+
+# Prefix: CAUSAL with a negative shift -P over Skv = P + Sq keys (every query
+# sees the P prefix keys, then the causal part), with and without the prefix
+# frozen (its dK, dV exactly 0, the rest unchanged).
+PREFIX = [
+    # name, B, Hq, Hkv, Sq, P, frozen
+    ("p37", 2, 4, 2, 200, 37, 0),
+    ("p37_frozen", 2, 4, 2, 200, 37, 37),
+    ("p256_frozen", 1, 8, 2, 300, 256, 256),
+    ("p300_frozen_part", 2, 4, 4, 130, 300, 170),   # frozen part of the prefix only
+]
+
+
+@pytest.mark.parametrize("D", [16, 64, 128])
+@pytest.mark.parametrize("case", PREFIX, ids=[c[0] for c in PREFIX])
+def test_bf16_prefix(case, D):
+    name, B, Hq, Hkv, Sq, P, frozen = case
+    q, k, v, do = inputs(B, Hq, Hkv, Sq, P + Sq, D, torch.bfloat16, seed=131 + D)
+    check_case(q, k, v, do, CAUSAL, "bf16", shift=-P, frozen=frozen, label=f"bf16 prefix {name} D={D}")
+
+
+def test_bf16_prefix_window_and_f32():
+    q, k, v, do = inputs(2, 4, 2, 150, 190, 64, torch.bfloat16, seed=141)
+    check_case(q, k, v, do, WINDOW, "bf16", shift=-40, window=(60, 10), frozen=20, label="bf16 window shift=-40")
+    q, k, v, do = inputs(1, 2, 1, 100, 164, 64, torch.float32, seed=142)
+    check_case(q, k, v, do, CAUSAL, "f32", shift=-64, frozen=64, label="f32 prefix P=64 frozen")
+
+
+def test_bf16_prefix_many_workgroups_and_ttt_frozen():
+    # 512+ forward workgroups, the split dK/dV kernel with frozen blocks
+    q, k, v, do = inputs(4, 128, 16, 300, 556, 128, torch.bfloat16, seed=151)
+    check_case(q, k, v, do, CAUSAL, "bf16", shift=-256, frozen=256, label="bf16 many-WG prefix 256 frozen")
+    # TTT keys of later steps below frozen_keys are frozen too
+    q, k, v, do = inputs(1, 4, 2, 100, 300, 128, torch.bfloat16, seed=152)
+    check_case(q, k, v, do, TTT, "bf16", frozen=150, label="bf16 ttt frozen 150")
+
+
+def test_bf16_prefix_unsplit_frozen():
+    # 1024+ key blocks: the unsplit dK/dV kernel writes frozen keys itself
+    q, k, v, do = inputs(16, 64, 64, 128, 384, 64, torch.bfloat16, seed=161)
+    check_case(q, k, v, do, CAUSAL, "bf16", shift=-256, frozen=200, label="bf16 unsplit prefix frozen 200")

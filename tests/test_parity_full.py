@@ -34,7 +34,8 @@ def run_like_bench(w, q, k, v, do):
     dev = "cuda"
     qg, kg, vg, dog = (x.to(dev) for x in (q, k, v, do))
     kvv = W.kv_valid_tensor(w, dev)
-    kw = dict(mask_kind=w.kind, causal_shift=w.shift, kv_valid=kvv, scale=w.scale, window=w.window)
+    kw = dict(mask_kind=w.kind, causal_shift=w.shift, kv_valid=kvv, scale=w.scale, window=w.window,
+              frozen_keys=w.frozen)
     o, lse = fa.fa_fwd(qg, kg, vg, **kw)
     dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
     ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(qg, kg)), dtype=torch.uint8, device=dev)
@@ -59,7 +60,13 @@ def kvv_of(w, b):
 
 
 def check_identities(w, do, o, dk, dv, label):
-    """sum_j dK_j = 0 and sum_j dV_j = sum over non-empty rows of dO, per (b, kv head)."""
+    """sum_j dK_j = 0 and sum_j dV_j = sum over non-empty rows of dO, per (b, kv head).
+    With frozen keys (their dK, dV left at zero) the sums are not over all
+    keys, so the check is that the frozen rows are exactly zero instead."""
+    if w.frozen:
+        assert torch.all(dk[:, :, :w.frozen] == 0) and torch.all(dv[:, :, :w.frozen] == 0), \
+            f"{label}: frozen keys must hold exactly zero dK, dV"
+        return
     G = w.Hq // w.Hkv
     for b in range(w.B):
         # a row is empty iff no key is allowed; with these masks (valid keys
@@ -129,8 +136,9 @@ def complete_keys(w, b, lo, hi):
     contributions and the comparison would fail, never pass falsely."""
     L = w.Sq
     cand = np.arange(w.Skv)
-    cand = cand[(cand % L) >= max(0, lo - w.shift - 1)]
-    outside = np.concatenate([np.arange(max(0, lo - w.shift - 256), lo), np.arange(hi, w.Sq)])
+    pos = cand % L if w.kind == W.TTT else cand
+    cand = cand[pos >= max(0, lo - w.shift - 1)]
+    outside = np.concatenate([np.arange(max(0, lo - max(w.shift, 0) - 256), lo), np.arange(hi, w.Sq)])
     seen = np.zeros(len(cand), bool)
     for r0 in range(0, len(outside), 2048):
         A = allowed(w.kind, w.Sq, w.Skv, w.shift, kvv_of(w, b), rows=outside[r0:r0 + 2048], window=w.window)

@@ -55,7 +55,8 @@ def cases():
     out = []
     tiles = [(32, 32, 32), (64, 64, 256), (256, 64, 256), (64, 32, 32)]
     for Sq, Skv in [(1, 1), (7, 7), (64, 64), (100, 130), (130, 100), (200, 200)]:
-        for shift, kv in itertools.product((0, 1, 5, 70), (None, 0, 1, 61)):
+        # negative shifts: a prefix of -shift keys before the diagonal
+        for shift, kv in itertools.product((0, 1, 5, 70, -1, -30, -64, -300), (None, 0, 1, 61)):
             for TQ, TK, TKW in tiles:
                 kvv = Skv if kv is None else min(kv, Skv)
                 out.append((FULL, Sq, Skv, 0, kvv, 0, 0, TQ, TK, TKW, 0))

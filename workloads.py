@@ -21,7 +21,10 @@ Shapes follow the pages' own workloads:
     keys (1000 valid of 1024), the ggml playbook's real geometries;
   * windowed self-attention, the playbook's third geometry (its window is
     not given: a symmetric band of +-512 keys on the DiT shape), and a
-    causal sliding window of 4096 keys on the long-context GQA shape.
+    causal sliding window of 4096 keys on the long-context GQA shape;
+  * a causal sequence behind a frozen KV prefix (the playbook's per-trainer
+    checklist names a trainer with a frozen/trained KV prefix and no sizes:
+    4096 prefix keys before the 16K long-context GQA shape, prefix frozen).
 """
 from dataclasses import dataclass, field, replace
 from typing import Optional
@@ -47,6 +50,7 @@ class Workload:
     kv_valid: Optional[tuple] = None   # per-batch valid key count, None = all
     scale: Optional[float] = None      # None -> 1/sqrt(D)
     window: Optional[tuple] = None     # WINDOW: (left, right)
+    frozen: int = 0                    # keys below it are frozen (no dK/dV)
 
     def torch_dtype(self):
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
@@ -90,6 +94,12 @@ def swa_gqa(S=16384, w=4096):
     return Workload(f"swa_gqa_S{S}_w{w}", 1, 32, 4, S, S, 128, WINDOW, window=(w - 1, 0))
 
 
+def prefix_gqa(S=16384, P=4096):
+    # a causal sequence behind a frozen P-key prefix (the rectangular mask a
+    # frozen KV prefix needs): CAUSAL with shift -P over P + S keys
+    return Workload(f"prefix_gqa_S{S}_P{P}_frozen", 1, 32, 4, S, P + S, 128, CAUSAL, shift=-P, frozen=P)
+
+
 HEADLINE = long_gqa(16384)
 
 
@@ -97,7 +107,7 @@ def all_workloads():
     ws = [tiny_fp32(CAUSAL), tiny_fp32(FULL)]
     ws += [grid(D, S) for D in (16, 32, 64) for S in (256, 1024, 4096)]
     ws += [long_gqa(16384), long_gqa(32768), ttt(16384, 2), dit_self(),
-           dit_cross(), dit_window(), swa_gqa()]
+           dit_cross(), dit_window(), swa_gqa(), prefix_gqa()]
     return ws
 
 
