@@ -1039,8 +1039,10 @@ dkdv_split_kernel(Params p) {
     const unsigned char* Gt = Qt + L::TILE;
     const float* Ls = reinterpret_cast<const float*>(Qt + 2 * L::TILE);
     const float* Ds = Ls + TQ;   // -Delta of the rows
-#pragma unroll 1
-    for (int h = 0; h < TQ / 32; ++h) {   // 32-row sub-tiles, one at a time
+    // 32-row sub-tiles; unrolled where registers allow (D <= 64), so one
+    // sub-tile's products can overlap the other's exponentials
+#pragma unroll(D <= 64 ? TQ / 32 : 1)
+    for (int h = 0; h < TQ / 32; ++h) {
     const int qa = cur.q0 + 32 * h;
     int state = TILE_FULL;
     if (!(qa >= qfull && qa + 32 <= p.Sq)) {
