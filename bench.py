@@ -227,7 +227,7 @@ def measure(fa, w, dev, steps, warmup, inputs):
     o = torch.empty_like(qg)
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
-    ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(qg, kg)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(qg, kg, mask_kind=w.kind)), dtype=torch.uint8, device=dev)
     fws = torch.empty(max(1, fa.fa_fwd_workspace_bytes(qg, kg)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     kw = dict(mask_kind=w.kind, causal_shift=w.shift, kv_valid=kvv, scale=w.scale, window=w.window,

@@ -23,8 +23,6 @@ plus the key at the query's own position in each later step) and ``WINDOW``
 right).  ``kv_valid`` is an optional int32 device tensor [B] of valid key
 counts.
 """
-import math
-
 import torch
 
 from . import _lib
@@ -75,6 +73,22 @@ def _stream(t, stream):
     return None
 
 
+def _scratch(nbytes, device, stream):
+    """A workspace the binding allocates for one call.  It is freed when the
+    call returns, while the kernels may still be running on ``stream``: the
+    caching allocator must not hand its memory out again before that stream
+    has finished with it (record_stream).  For a raw stream handle that
+    cannot be recorded, the caller has to pass a workspace."""
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if stream is not None:
+        if not isinstance(stream, torch.cuda.Stream):
+            raise FAError(_lib.FA_ERR_INVALID_ARG,
+                          "with a raw stream handle, pass workspace= (the binding cannot keep "
+                          "its own scratch alive until that stream is done with it)")
+        ws.record_stream(stream)
+    return ws
+
+
 def _shape(q, k):
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
@@ -115,7 +129,7 @@ def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=Non
             raise FAError(_lib.FA_ERR_INVALID_ARG, "q, k, v and out must share one dtype")
     need = int(_lib.lib().fa_fwd_workspace_bytes(a))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     _lib.check(_lib.lib().fa_fwd(a, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                  _stream(q, stream)))
     return out, lse
@@ -159,7 +173,7 @@ def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=No
                   frozen_keys)
     need = int(_lib.lib().fa_bwd_workspace_bytes(a))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     ws_ptr = workspace.data_ptr()
     _lib.check(_lib.lib().fa_bwd(a, ws_ptr, workspace.numel() * workspace.element_size(),
                                  _stream(q, stream)))
@@ -214,10 +228,6 @@ def attention(q, k, v, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None
     without computing them.  Saves only O and LSE for the backward.
     """
     return _Attention.apply(q, k, v, mask_kind, causal_shift, kv_valid, scale, window, frozen_keys)
-
-
-def default_scale(D):
-    return 1.0 / math.sqrt(D)
 
 
 # ---- soft-target log-softmax loss (fa_lsm_loss_fwd / fa_lsm_loss_bwd) -------

@@ -22,7 +22,7 @@ package is "parity unpinned".
 from .attention import (  # noqa: F401
     FULL, CAUSAL, TTT, WINDOW,
     allowed, attention_forward, attention_backward, attention_ref,
-    allowed_pair_count,
+    allowed_pair_count, attention_key_grads,
 )
 from .ttt_steps import ttt_stepwise_forward  # noqa: F401
 from .loss import logsoftmax_loss_forward, logsoftmax_loss_backward  # noqa: F401

@@ -192,6 +192,60 @@ def attention_backward(q, k, v, do, kind=FULL, shift=0, kv_valid=None,
     return dQ, dK, dV, Delta
 
 
+def attention_key_grads(q, k, v, do, keys, kind=FULL, shift=0, kv_valid=None, scale=None,
+                        window=None):
+    """dK, dV (float64) of the keys [keys[0], keys[1]) only, over every query
+    row and every head of each group: [B, Hkv, k1 - k0, D] each.
+
+    The gradient of one key needs every query row that may attend it, and of
+    those rows the logsumexp and output over their complete key sets.  So:
+    the rows that may attend some key of the range are found from the mask;
+    their LSE and O come from ``attention_forward`` (complete rows); then, as
+    the CS336 page's backward does, P of the range's keys is recomputed from
+    the scores and the saved logsumexp, P_ij = exp(s q_i.k_j - LSE_i) on
+    allowed pairs (0 elsewhere), and with dP_ij = dO_i.v_j,
+    Delta_i = sum_d dO_id O_id (which equals sum_j P_ij dP_ij, because
+    O_i = sum_j P_ij v_j) and dS = P (dP - Delta):
+        dV_j = sum_i P_ij dO_i,    dK_j = s sum_i dS_ij q_i,
+    summed over the query heads of the key's group.  The same values as
+    ``attention_backward``'s dK, dV on those keys, without materialising the
+    other keys' gradients.
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
+    G = Hq // Hkv
+    s = 1.0 / np.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    kvv = _kv_valid_list(B, Skv, kv_valid)
+    k0, k1 = int(keys[0]), int(keys[1])
+    dK = np.zeros((B, Hkv, k1 - k0, D))
+    dV = np.zeros((B, Hkv, k1 - k0, D))
+    for b in range(B):
+        # rows that may attend a key of the range (scanned in row blocks)
+        att = np.zeros(Sq, bool)
+        for rb in _row_blocks(Sq, None):
+            att[rb] = allowed(kind, Sq, Skv, shift, kvv[b], rb, window)[:, k0:k1].any(1)
+        rows = np.nonzero(att)[0]
+        if len(rows) == 0:
+            continue
+        lo, hi = int(rows[0]), int(rows[-1]) + 1
+        for g in range(Hkv):
+            heads = list(range(g * G, (g + 1) * G))
+            O, LSE = attention_forward(q[b:b + 1], k[b:b + 1], v[b:b + 1], kind, shift,
+                                       [kvv[b]], s, heads=heads, rows=(lo, hi), window=window)
+            for rb in _row_blocks(Sq, (lo, hi)):
+                A = allowed(kind, Sq, Skv, shift, kvv[b], rb, window)[:, k0:k1]
+                for h in heads:
+                    S = s * (q[b, h, rb] @ k[b, g, k0:k1].T)
+                    P = np.where(A, np.exp(np.where(A, S, 0.0) - LSE[0, h, rb][:, None]), 0.0)
+                    dO = do[b, h, rb]
+                    dP = dO @ v[b, g, k0:k1].T
+                    delta = (dO * O[0, h, rb]).sum(axis=1)
+                    dS = P * (dP - delta[:, None])
+                    dV[b, g] += P.T @ dO
+                    dK[b, g] += s * (dS.T @ q[b, h, rb])
+    return dK, dV
+
+
 def attention_ref(q, k, v, do, kind=FULL, shift=0, kv_valid=None, scale=None,
                   heads=None, rows=None, window=None):
     """Forward and backward together: dict with O, LSE, dQ, dK, dV, Delta."""

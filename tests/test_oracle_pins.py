@@ -426,3 +426,54 @@ def test_prefix_matches_torch_sdpa_block_mask(Hq, Hkv, Sq, P):
         for j in range(Skv):
             assert A[i, j] == (j < P or j - P <= i), (i, j)
     assert allowed_pair_count(CAUSAL, Sq, Skv, -P) == Sq * P + Sq * (Sq + 1) // 2
+
+
+# --------------------------------------------------------------------------
+# The key-range gradient (attention_key_grads), which the full-size parity
+# tests use to check dK/dV of sampled key blocks over every attending row
+
+def _torch_mask(kind, Sq, Skv, shift, kvv, window):
+    """The allowed-pair matrix built from torch.tril / torch.triu / torch.eye
+    and a column bound (not from the oracle's predicate)."""
+    cols = torch.arange(Skv)[None, :]
+    if kind == FULL:
+        return (cols < kvv).expand(Sq, Skv).clone()
+    if kind == WINDOW:
+        return _band(Sq, Skv, shift, *window) & (cols < kvv)
+    tri = torch.ones(Sq, Skv, dtype=torch.bool).tril(-shift)
+    if kind == CAUSAL:
+        return tri & (cols < kvv)
+    L = Sq   # TTT: the causal step-0 block, then one diagonal per later step
+    blocks = [tri[:, :L] & (cols[:, :L] < kvv)]
+    rows_ok = (torch.arange(L) < kvv)[:, None]
+    for _ in range(1, Skv // L):
+        blocks.append(torch.eye(L, dtype=torch.bool) & rows_ok)
+    return torch.cat(blocks, dim=1)
+
+
+@pytest.mark.parametrize("kind,Sq,Skv,shift,kvv,win,keys", [
+    (CAUSAL, 24, 24, 0, (24, 17), None, (5, 13)),
+    (CAUSAL, 20, 30, -10, (30, 30), None, (0, 12)),      # a prefix before the diagonal
+    (FULL, 16, 21, 0, (21, 9), None, (7, 21)),
+    (TTT, 12, 36, 0, (12, 7), None, (8, 30)),
+    (TTT, 10, 30, 2, (10, 10), None, (0, 30)),
+    (WINDOW, 22, 22, 1, (22, 15), (4, 2), (3, 19)),
+])
+def test_key_grads_match_torch_sdpa_autograd(kind, Sq, Skv, shift, kvv, win, keys):
+    from oracle import attention_key_grads
+    B, Hq, Hkv, D = 2, 4, 2, 8
+    q, k, v = _rand((B, Hq, Sq, D), 100), _rand((B, Hkv, Skv, D), 101), _rand((B, Hkv, Skv, D), 102)
+    do = _rand((B, Hq, Sq, D), 103)
+    dK, dV = attention_key_grads(q, k, v, do, keys, kind, shift, kvv, window=win)
+    k0, k1 = keys
+    for b in range(B):
+        mask = _torch_mask(kind, Sq, Skv, shift, kvv[b], win)
+        rows = mask.any(1)                     # SDPA gives NaN on rows with no key
+        tq, tk, tv = (torch.tensor(x[b:b + 1], requires_grad=True) for x in (q, k, v))
+        out = torch.nn.functional.scaled_dot_product_attention(
+            tq[:, :, rows], tk, tv, attn_mask=mask[rows], enable_gqa=True)
+        out.backward(torch.tensor(do[b:b + 1][:, :, rows.numpy()]))
+        gk, gv = tk.grad.numpy()[0, :, k0:k1], tv.grad.numpy()[0, :, k0:k1]
+        assert np.abs(gk).max() > 1e-3 and np.abs(gv).max() > 1e-3
+        np.testing.assert_allclose(dK[b], gk, atol=1e-11, err_msg=f"dK b={b}")
+        np.testing.assert_allclose(dV[b], gv, atol=1e-11, err_msg=f"dV b={b}")

@@ -211,7 +211,7 @@ def test_staged_backward_equals_fa_bwd(dtype, D):
     o, lse = fa.fa_fwd(q, k, v, mask_kind=CAUSAL)
     ref = fa.fa_bwd(q, k, v, o, lse, do, mask_kind=CAUSAL)
     dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
-    ws = torch.empty(fa.fa_bwd_workspace_bytes(q, k), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(q, k, mask_kind=CAUSAL), dtype=torch.uint8, device="cuda")
     # the gradient stages in the opposite order: they are independent once Delta exists
     for stage in (fa.FA_BWD_DELTA, fa.FA_BWD_DQ, fa.FA_BWD_DKDV):
         fa.fa_bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, mask_kind=CAUSAL)

@@ -11,18 +11,25 @@ case compares what it can compute exactly:
   group, and dK, dV of the keys that only those rows may attend (for the last
   block that is the final keys of the causal part and, under TTT, the later
   steps' keys at those positions), all exact;
+* grouped shapes again: dK, dV of sampled 256-key blocks (an early one, at
+  an eighth of the sequence, and a middle one; under TTT also a block of the
+  step-1 keys) element by element, from the oracle over every query row that
+  attends them, in every head of the group;
 * everywhere: two identities that hold at any size for every (batch, K/V
   head): the dK rows sum to zero (each softmax-gradient row dS_i sums to zero)
   and the dV rows sum to the dO rows of the group's non-empty query rows (each
   P row sums to one).
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
+from threadpoolctl import threadpool_limits
 
 import flash_attention_fa_amd as fa
 import workloads as W
-from oracle import allowed, attention_ref
+from oracle import allowed, attention_key_grads, attention_ref
 from parity_util import TOL_BF16, TOL_LSE_BF16, say
 
 pytestmark = pytest.mark.gpu
@@ -38,7 +45,7 @@ def run_like_bench(w, q, k, v, do):
               frozen_keys=w.frozen)
     o, lse = fa.fa_fwd(qg, kg, vg, **kw)
     dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
-    ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(qg, kg)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(qg, kg, mask_kind=w.kind)), dtype=torch.uint8, device=dev)
     for stage in (fa.FA_BWD_DELTA, fa.FA_BWD_DKDV, fa.FA_BWD_DQ):
         fa.fa_bwd_stage(stage, qg, kg, vg, o, lse, dog, dq, dk, dv, ws, **kw)
     torch.cuda.synchronize()
@@ -180,6 +187,58 @@ def test_full_size_grouped_row_samples(w):
         if (lo, hi) == blocks[-1]:
             assert len(keys) >= ROWS // 2, "the last row block should own some keys outright"
     check_identities(w, do, o, dk, dv, w.name)
+
+
+KEY_BLOCK = 256
+
+
+def sampled_key_blocks(w):
+    """An early and a middle 256-key block of the walked keys (past a frozen
+    prefix, whose gradients are exact zeros and checked as such), and under
+    TTT a block of the step-1 keys."""
+    L = w.Sq if w.kind == W.TTT else w.Skv
+    base = w.frozen
+    span = L - base
+    starts = [base + (span // 8) // KEY_BLOCK * KEY_BLOCK, base + (span // 2) // KEY_BLOCK * KEY_BLOCK]
+    if w.kind == W.TTT:
+        starts.append(w.Sq + (w.Sq // 2) // KEY_BLOCK * KEY_BLOCK)
+    return [(s, min(w.Skv, s + KEY_BLOCK)) for s in starts]
+
+
+def oracle_key_block(w, q, k, v, do, b, g, keys):
+    """dK, dV of keys [k0, k1) of (b, K/V head g) from the oracle, one query
+    head per worker thread (the group's heads summed in order afterwards)."""
+    G = w.Hq // w.Hkv
+    kvv = None if w.kv_valid is None else [w.kv_valid[b]]
+    K, V = (x[b:b + 1, g:g + 1].double().numpy() for x in (k, v))
+
+    def one(h):
+        Q, DO = (x[b:b + 1, h:h + 1].double().numpy() for x in (q, do))
+        return attention_key_grads(Q, K, V, DO, keys, w.kind, w.shift, kvv, w.scale, window=w.window)
+
+    with threadpool_limits(limits=2), ThreadPoolExecutor(max_workers=G) as ex:
+        parts = list(ex.map(one, range(g * G, (g + 1) * G)))
+    dK = sum(p[0][0, 0] for p in parts)
+    dV = sum(p[1][0, 0] for p in parts)
+    return dK, dV
+
+
+@pytest.mark.parametrize("w", grouped_cases(), ids=lambda w: w.name)
+def test_full_size_grouped_key_blocks(w):
+    """dK, dV of sampled key blocks of one K/V group, element by element,
+    against the oracle over every query row (of every head of the group) that
+    attends them."""
+    say(f"[full] {w.name} key blocks {sampled_key_blocks(w)}")
+    q, k, v, do = W.make_inputs(w, seed=1)
+    o, lse, dq, dk, dv = run_like_bench(w, q, k, v, do)
+    b, g = w.B - 1, 0
+    for k0, k1 in sampled_key_blocks(w):
+        rk, rv = oracle_key_block(w, q, k, v, do, b, g, (k0, k1))
+        errs = {}
+        for name, got, ref in (("dK", dk, rk), ("dV", dv, rv)):
+            errs[name] = rel_err(f64(got[b, g, k0:k1]), ref)
+            assert errs[name] <= TOL_BF16[name], f"{w.name} keys [{k0},{k1}) {name} {errs[name]:.2e}"
+        say(f"[full] {w.name} keys [{k0},{k1}) ok {errs}")
 
 
 def test_peak_memory_linear_in_S():

@@ -133,6 +133,50 @@ def kv_valid_tensor(w: Workload, device="cpu"):
     return torch.tensor(list(w.kv_valid), dtype=torch.int32, device=device)
 
 
+# ---- stress inputs for the forward's running-max refresh ---------------------
+# Scores of N(0, 1) inputs stay within a few units of the first key tile's
+# maximum, so a forward that keeps a lazy running max (refreshed only when a
+# tile's sum of exp(score - max) grows large) never rescales accumulators that
+# already hold values on them.  These recipes make some keys score far above
+# the ones before them (the SpecForge page warns that unbounded inputs break
+# naive references; here every value stays bounded and finite).
+#   spike:   u a seeded random unit vector of R^D.  q_i = sqrt(D) u + 0.1 n_i;
+#            k_j = 0.1 m_j, except for the keys listed in `spikes`, where
+#            k_j = level * u + 0.1 m_j; so with the default scale 1/sqrt(D)
+#            scores are about 0 and, on the spike keys, about `level`.
+#            v_j = +1 + 0.5 w_j (every component), and -1 + 0.5 w_j on the
+#            spike keys, so the output before and after a spike differ in
+#            sign.  n, m, w and dO are i.i.d. N(0, 1).
+#   peaky:   the standard recipe with Q multiplied by 4.
+#   uniform: Q, K, V, dO i.i.d. U(-1, 1).
+# One CPU generator seeded with `seed` draws, in order: u (spike only), Q, K,
+# V, dO.
+
+def make_stress_inputs(recipe, B, Hq, Hkv, Sq, Skv, D, seed=0, spikes=(), level=7.0,
+                       dtype=torch.bfloat16):
+    g = torch.Generator("cpu").manual_seed(seed)
+    qs, ks = (B, Hq, Sq, D), (B, Hkv, Skv, D)
+    f64 = torch.float64
+    if recipe == "spike":
+        u = torch.randn(D, generator=g, dtype=f64)
+        u = u / u.norm()
+        hot = torch.zeros(Skv, dtype=f64)
+        hot[list(spikes)] = 1.0
+        q = D ** 0.5 * u + 0.1 * torch.randn(qs, generator=g, dtype=f64)
+        k = (level * hot)[:, None] * u + 0.1 * torch.randn(ks, generator=g, dtype=f64)
+        v = (1.0 - 2.0 * hot)[:, None] + 0.5 * torch.randn(ks, generator=g, dtype=f64)
+        do = torch.randn(qs, generator=g, dtype=f64)
+    elif recipe == "peaky":
+        q = 4.0 * torch.randn(qs, generator=g, dtype=f64)
+        k, v = (torch.randn(ks, generator=g, dtype=f64) for _ in range(2))
+        do = torch.randn(qs, generator=g, dtype=f64)
+    elif recipe == "uniform":
+        q, k, v, do = (2 * torch.rand(s, generator=g, dtype=f64) - 1 for s in (qs, ks, ks, qs))
+    else:
+        raise ValueError(f"unknown recipe {recipe}")
+    return tuple(x.to(dtype) for x in (q, k, v, do))
+
+
 # ---- soft-target log-softmax loss workloads ---------------------------------
 # The (B, T, V) configurations of the SpecForge page's loss benchmark (section
 # "In-place Gradient Calculation").  Recipe: a generator on ``device`` seeded
