@@ -47,7 +47,10 @@
  *
  * Layout.  Every tensor is a logical [B, H, S, D] array with unit stride in
  * D and arbitrary element strides for B, H and S (so BHSD and BSHD views both
- * work without a copy).  LSE is a contiguous float32 [B, Hq, Sq] array.
+ * work without a copy: the ggml playbook's "3. Per-trainer porting
+ * checklist" requires the fused ops to accept non-contiguous q/k/v views,
+ * since copying them to a contiguous layout spends the memory the fused
+ * path saves).  LSE is a contiguous float32 [B, Hq, Sq] array.
  * All tensor pointers are device pointers.  Element type: FA_BF16 (bfloat16
  * storage, float32 accumulation; O, dQ, dK, dV rounded to nearest even) or
  * FA_F32 (float32 throughout).
@@ -58,7 +61,17 @@
  *
  * Errors.  All arguments are validated before anything is launched; on a
  * non-OK status nothing was launched and fa_last_error() describes why.
- * There is no fallback path of any kind.
+ * There is no fallback path of any kind (the ggml playbook, "2. The adoption
+ * contract", item 2: an unsupported request must be a named hard error,
+ * because a silent fallback to another implementation produces numbers that
+ * look like a pass).
+ *
+ * Calling convention.  The problem statement of the path names two calls,
+ * forward and backward, each taking its arguments and a stream.  Here both
+ * also take a caller-owned workspace (pointer and size), because the library
+ * allocates nothing: the backward's holds Delta and the dK/dV partial sums,
+ * the forward's a transposed copy of V that the P.V product reads (one pass
+ * over V, linear in Skv).  The *_workspace_bytes calls give the sizes.
  */
 #ifndef FA_H
 #define FA_H
@@ -87,7 +100,10 @@ typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
 
 typedef enum { FA_MASK_FULL = 0, FA_MASK_CAUSAL = 1, FA_MASK_TTT = 2, FA_MASK_WINDOW = 3 } fa_mask_kind;
 
-/* One [B, H, S, D] tensor: base pointer and element strides (D stride = 1). */
+/* One [B, H, S, D] tensor: base pointer and element strides (D stride = 1).
+ * Any outer strides that are multiples of 16 bytes are accepted, so a BSHD
+ * or otherwise strided view is passed as is (the ggml playbook, "3.
+ * Per-trainer porting checklist": non-contiguous q/k/v views, no copies). */
 typedef struct {
   void* data;
   int64_t stride_b;
@@ -95,6 +111,11 @@ typedef struct {
   int64_t stride_s;
 } fa_tensor;
 
+/* The mask descriptor: which (query, key) pairs may attend, the same for
+ * every head ("Flex Attention and Triton, Supporting Long Context Training in
+ * SpecForge", section "Flex Attention": the causal, padding and suffix mask
+ * functions, broadcast over heads, with per-batch sequence lengths; the
+ * WINDOW and prefix forms are described above). */
 typedef struct {
   int32_t kind;              /* fa_mask_kind */
   int32_t causal_shift;      /* used by CAUSAL, WINDOW and TTT's step-0 part; >= 0
@@ -113,6 +134,11 @@ typedef struct {
                                 forward and dQ are unchanged.  0 = none */
 } fa_mask_desc;
 
+/* Forward arguments: the shapes, the softmax scale (1/sqrt(d_k) by default,
+ * as in the SpecForge page's section "EAGLE3 Training"), Q, K, V and the
+ * outputs.  Hkv < Hq is grouped-query attention and Sq != Skv is allowed (the
+ * ggml playbook's "3. Per-trainer porting checklist" lists both among what
+ * the fused ops must take). */
 typedef struct {
   int32_t dtype;             /* fa_dtype */
   int32_t B, Hq, Hkv, Sq, Skv, D;
@@ -125,6 +151,10 @@ typedef struct {
   fa_mask_desc mask;
 } fa_fwd_args;
 
+/* Backward arguments: the forward's, plus its saved O and LSE and the
+ * upstream gradient dO, and the three gradient outputs (the ggml playbook,
+ * "1. What exists": the backward consumes the forward's O and LSE and
+ * produces dQ, dK, dV). */
 typedef struct {
   int32_t dtype;
   int32_t B, Hq, Hkv, Sq, Skv, D;
@@ -153,7 +183,11 @@ size_t fa_fwd_workspace_bytes(const fa_fwd_args* args);
  * (0 = null stream). */
 fa_status fa_fwd(const fa_fwd_args* args, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Bytes of device scratch fa_bwd needs for these arguments: two float32
+/* Bytes of device scratch fa_bwd needs for these arguments.  It is linear
+ * in the sequence lengths: the backward never holds the S x S score or
+ * probability matrix, it rebuilds P tile by tile from the saved logsumexp
+ * (CS336 "Flash Attention (Triton)", How it works: only O and the
+ * logsumexp are kept for the backward).  The bytes: two float32
  * [B, Hq, Sq] arrays (Delta, and LSE in log2 units), each rounded up to 256
  * bytes, and for FA_BF16 with D >= 32 the dK/dV kernel's float32 partial
  * sums, four [B, Hkv, Skv, D] arrays (two halves of each key block's query
@@ -178,7 +212,10 @@ typedef enum {
   FA_BWD_DQ = 2      /* dQ: one workgroup per query block */
 } fa_bwd_stage_id;
 
-/* Runs one stage of fa_bwd with the same arguments, validation and workspace.
+/* Runs one stage of fa_bwd with the same arguments, validation and workspace
+ * (the ggml playbook, "4. Measurement discipline", attributes the fused
+ * backward's cost kernel by kernel before changing any; this is the call
+ * that lets a caller time or overlap the stages one by one).
  * DKDV and DQ read what a DELTA stage left in `ws` (on the same
  * stream, or ordered after it by the caller); given that, running DELTA,
  * DKDV, DQ in turn writes bitwise the same dQ, dK, dV as fa_bwd.  For callers
@@ -240,7 +277,10 @@ fa_status fa_lsm_loss_fwd(const fa_lsm_loss_args* args, hipStream_t stream);
 fa_status fa_lsm_loss_bwd(const fa_lsm_loss_args* args, hipStream_t stream);
 
 /* Text describing the last non-OK status returned on this thread
- * ("" if none).  The pointer stays valid until the thread's next call. */
+ * ("" if none).  The pointer stays valid until the thread's next call.
+ * Every refusal names its reason here (the ggml playbook, "2. The adoption
+ * contract", item 2: an unsupported case is reported as a named error, never
+ * absorbed by a fallback). */
 const char* fa_last_error(void);
 
 #ifdef __cplusplus

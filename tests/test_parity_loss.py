@@ -176,11 +176,13 @@ def test_logsoftmax_loss_autograd_in_place():
 
 def test_loss_full_size_sampled_rows():
     # the page's largest configuration, in the benchmark's launch: every row
-    # computed, sampled rows checked against the oracle, the mean against the
-    # library's own row terms
+    # computed; every row term and the mean checked against the oracle (row
+    # blocks of the fp64 oracle over the whole matrix), the gradient on
+    # sampled rows
     w_ = W.LOSS_HEADLINE
     say(f"loss full size {w_.name}: N={w_.N} V={w_.V}")
     x, t, w = W.make_loss_inputs(w_, seed=1, device="cuda")
+    x0 = x.clone()
     rows = np.unique(np.concatenate([[0, 1, w_.N // 2, w_.N - 1],
                                      np.random.default_rng(5).integers(0, w_.N, 28)]))
     xs, ts = x[rows].cpu(), t[rows].cpu()
@@ -200,5 +202,19 @@ def test_loss_full_size_sampled_rows():
     gref = lbwd(X, T, Wt) * len(rows) / w_.N
     G = np64(gx[rows])
     assert np.all(np.abs(G - gref).max(axis=1) <= 1e-5 * np.abs(gref).max(axis=1) + 1e-12)
+    # every row term and the mean against the oracle, 1024 rows at a time
     r = np64(row)
-    assert abs(np64(loss)[0] - r.sum() / w_.N) <= 1e-5 * np.abs(r).mean()
+    ref_rows = np.empty(w_.N)
+    bound = np.empty(w_.N)
+    Wall = np64(w)
+    for r0 in range(0, w_.N, 1024):
+        sl = slice(r0, min(w_.N, r0 + 1024))
+        Xb, Tb = np64(x0[sl]), np64(t[sl])
+        _, rb, mb, db, _ = lfwd(Xb, Tb, Wall[sl])
+        ref_rows[sl] = rb
+        bound[sl] = 2e-5 * (np.abs(Tb) * (np.abs(Xb) + np.abs(mb + np.log(db))[:, None])).sum(axis=1) + 1e-6
+    assert np.all(np.abs(r - ref_rows) <= bound), "row terms"
+    mean_ref = ref_rows.sum() / w_.N
+    err = abs(np64(loss)[0] - mean_ref)
+    say(f"loss full size: mean {np64(loss)[0]:.8f} oracle {mean_ref:.8f} |err| {err:.2e}")
+    assert err <= bound.sum() / w_.N
