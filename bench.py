@@ -215,10 +215,76 @@ def dkdv_label(w):
     return "dK/dV stage (fa_bwd_stage FA_BWD_DKDV: one kernel)"
 
 
+class ClockSampler:
+    """Samples the GPU's current shader clock (MHz) from the driver's DPM
+    table in sysfs (the level marked '*' in pp_dpm_sclk) every few
+    milliseconds on a host thread while the timed steps run.  Where no such
+    file is readable the samples stay empty and the clock is reported as
+    unknown (never guessed)."""
+
+    def __init__(self, period_s=0.005):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples = {}
+        self.period = period_s
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        v = line.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                        return float(v.replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for p in self.paths:
+                v = self._read(p)
+                if v is not None:
+                    self.samples.setdefault(p, []).append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        """The busiest card's samples (the one under load reads the highest
+        median), or None when nothing could be read."""
+        if not self.samples:
+            return None
+        path, vals = max(self.samples.items(), key=lambda kv: float(np.median(kv[1])))
+        return {"sclk_mhz_median": float(np.median(vals)), "sclk_mhz_min": float(np.min(vals)),
+                "sclk_mhz_max": float(np.max(vals)), "samples": len(vals),
+                "source": path + " (DPM level marked '*', sampled during the timed steps)"}
+
+
+NRUNS = 3
+
+
+def run_sizes(steps, nruns=NRUNS):
+    """The timed steps split into nruns runs (sizes differ by at most one)."""
+    nruns = max(1, min(nruns, steps))
+    return [steps // nruns + (1 if i < steps % nruns else 0) for i in range(nruns)]
+
+
 def measure(fa, w, dev, steps, warmup, inputs):
     """Times `steps` fwd+bwd steps of workload w after `warmup` untimed ones,
     with HIP events on the launch stream around the forward and after each
-    backward stage."""
+    backward stage.  The timed steps run as three runs separated by a device
+    synchronisation (each step itself interleaves the forward and backward
+    arms); the clock is sampled throughout."""
     qg, kg, vg, dog = (x.to(dev) for x in inputs)
     kvv = W.kv_valid_tensor(w, dev)
     torch.cuda.synchronize()
@@ -252,21 +318,35 @@ def measure(fa, w, dev, steps, warmup, inputs):
 
     # events: step start, fwd end, Delta end, dK/dV end, dQ end (= step end)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(steps):
-        ev[s][0].record(stream)
-        fwd()
-        ev[s][1].record(stream)
-        bwd(ev[s][2:])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    sizes = run_sizes(steps)
+    runs = []
+    wall = 0.0
+    s = 0
+    with ClockSampler() as clock:
+        for n in sizes:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            first = s
+            for _ in range(n):
+                ev[s][0].record(stream)
+                fwd()
+                ev[s][1].record(stream)
+                bwd(ev[s][2:])
+                s += 1
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+            runs.append((first, s))
     span = lambda i, j: [e[i].elapsed_time(e[j]) for e in ev]
+    run_ms = [ev[a][0].elapsed_time(ev[b - 1][4]) / (b - a) for a, b in runs]
+    run_fwd = [float(np.median([ev[k][0].elapsed_time(ev[k][1]) for k in range(a, b)])) for a, b in runs]
+    run_bwd = [float(np.median([ev[k][1].elapsed_time(ev[k][4]) for k in range(a, b)])) for a, b in runs]
     # inputs + outputs + workspace resident during the step
     resident = sum(t.numel() * t.element_size() for t in (qg, kg, vg, dog, o, lse, dq, dk, dv, ws, fws))
     return {"fwd_ms": span(0, 1), "bwd_ms": span(1, 4),
             "stage_ms": {"delta": span(1, 2), "dkdv": span(2, 3), "dq": span(3, 4)},
-            "ms_step": ev[0][0].elapsed_time(ev[-1][4]) / steps,
+            "ms_step": sum(r * n for r, n in zip(run_ms, sizes)) / steps,
+            "runs": {"steps": sizes, "ms_per_step": run_ms, "fwd_ms_median": run_fwd, "bwd_ms_median": run_bwd},
+            "clock": clock.summary(),
             "peak_mem": int(peak_mem), "resident": int(resident), "mem0": int(mem0), "wall": wall}
 
 
@@ -373,6 +453,38 @@ def loss_bench(fa, w, dev, steps, warmup, cpu):
     torch.cuda.empty_cache()
 
 
+def runs_summary(r, f_fwd, f_bwd, tf):
+    """The three runs of the timed steps: per-run step, forward and backward
+    times, and their median and spread (max - min over the median, %)."""
+    rr = r["runs"]
+    out = {"steps": rr["steps"], "ms_per_step": [round(x, 4) for x in rr["ms_per_step"]],
+           "fwd_ms_median": [round(x, 4) for x in rr["fwd_ms_median"]],
+           "bwd_ms_median": [round(x, 4) for x in rr["bwd_ms_median"]]}
+    for key in ("ms_per_step", "fwd_ms_median", "bwd_ms_median"):
+        v = rr[key]
+        med = float(np.median(v))
+        out[key.replace("_median", "") + "_median_of_runs"] = round(med, 4)
+        out[key.replace("_median", "") + "_spread_pct"] = round(100 * (max(v) - min(v)) / med, 2)
+    out["fwd_pct_of_peak_median_of_runs"] = round(
+        100 * tf(f_fwd, float(np.median(rr["fwd_ms_median"]))) / PEAK_BF16_TFLOPS, 2)
+    out["step_pct_of_peak_median_of_runs"] = round(
+        100 * tf(f_fwd + f_bwd, float(np.median(rr["ms_per_step"]))) / PEAK_BF16_TFLOPS, 2)
+    return out
+
+
+PEAK_SCLK_MHZ = 2400.0   # the clock the published dense peak is quoted at
+
+
+def clock_summary(clock, value):
+    """The sampled clock and the fraction of the dense peak scaled to it."""
+    if clock is None:
+        return {"sclk_mhz_median": None, "source": "no readable pp_dpm_sclk on this host",
+                "pct_of_peak_clock_adjusted": None}
+    adj = PEAK_BF16_TFLOPS * clock["sclk_mhz_median"] / PEAK_SCLK_MHZ
+    return dict(clock, peak_tflops_at_sclk=round(adj, 1),
+                pct_of_peak_clock_adjusted=round(100 * value / adj, 2))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -463,6 +575,8 @@ def main():
         "memory": {"peak_above_inputs_bytes": int(peak_mem), "resident_bytes": int(resident),
                    "inputs_bytes": int(mem0)},
         "wall_s_timed": round(wall, 3),
+        "runs": runs_summary(r, f_fwd, f_bwd, tf),
+        "clock": clock_summary(r["clock"], value),
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, a.cpu_heads)

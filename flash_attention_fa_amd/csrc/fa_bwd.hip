@@ -470,60 +470,78 @@ dq_dma_kernel(Params p) {
     if (state != TILE_SKIP) {
       const unsigned char* Kt = smem + k * L::BUF;
       const unsigned char* Vt = Kt + L::TILE;
-      // dP^T accumulates onto -Delta (the lane's row), so it comes out as
-      // dP^T - Delta.
-      f32x16 s[2], dp[2];
+      // The tile's two 32-key blocks one after the other (a wave cannot
+      // overlap a block's exponentials with its own products anyway, and one
+      // block's S^T and dP^T hold half the registers of two): S^T and dP^T of
+      // the block, whose A operands (K and V rows) are read PF products ahead
+      // of their use; dS^T; then the block's dQ^T products, whose transposed
+      // K operands are read before the exponentials so their latency hides
+      // behind them.
+      constexpr int NSD = 2 * NJ;   // S^T and dP^T products of one key block
+      constexpr int NDQ = 2 * NDB;  // dQ^T products of one key block
+      constexpr int PF = 3;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
+        // dP^T accumulates onto -Delta (the lane's row), so it comes out as
+        // dP^T - Delta.
+        f32x16 s = f32x16{}, dp;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dp[kb][i] = -dlt;
-      }
+        for (int i = 0; i < 16; ++i) dp[i] = -dlt;
+        auto opread = [&](int n) __attribute__((always_inline)) {
+          return *FA_LDS(const bf16x8, ((n & 1) ? Vt : Kt) + 2 * kb * ROW16 + koff[n >> 1]);
+        };
+        bf16x8 op[PF + 1];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+        for (int n = 0; n < PF; ++n) op[n] = opread(n);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ak = *FA_LDS(const bf16x8, Kt + 2 * kb * ROW16 + koff[j]);
-          const bf16x8 av = *FA_LDS(const bf16x8, Vt + 2 * kb * ROW16 + koff[j]);
-          s[kb] = mfma32(ak, qreg[j], s[kb]);
-          dp[kb] = mfma32(av, greg[j], dp[kb]);
+        for (int n = 0; n < NSD; ++n) {
+          if (n + PF < NSD) op[(n + PF) % (PF + 1)] = opread(n + PF);
+          if (n & 1) dp = mfma32(op[n % (PF + 1)], greg[n >> 1], dp);
+          else s = mfma32(op[n % (PF + 1)], qreg[n >> 1], s);
         }
-      if (state == TILE_PART) {
+        // keep the operand reads ahead of their products
+        sched_group(SCHED_DS_READ, PF);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int n = 0; n < NSD; ++n) {
+          sched_group(SCHED_MFMA, 1);
+          if (n + PF < NSD) sched_group(SCHED_DS_READ, 1);
+        }
+        // K^T operands of this block's dQ^T products (two transposing reads each)
+        auto tread = [&](int n) __attribute__((always_inline)) {
+          const int rows = (2 * kb + n / NDB) * ROW16, c = n % NDB;
+          return cat8(lds_read_tr4(reinterpret_cast<const bf16*>(Kt + rows + toff[0][c])),
+                      lds_read_tr4(reinterpret_cast<const bf16*>(Kt + rows + toff[1][c])));
+        };
+        constexpr int TPF = 2;
+        bf16x8 ta[TPF + 1];
+#pragma unroll
+        for (int n = 0; n < TPF; ++n) ta[n] = tread(n);
+        if (state == TILE_PART) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-            s[kb][i] = allowed(m, qi, key) ? s[kb][i] : -INFINITY;
+            s[i] = allowed(m, qi, key) ? s[i] : -INFINITY;
           }
-      }
-      // dS^T = P^T (dP^T - Delta), rounded to bf16 for the K^T dS^T product.
-      bf16x8 dsb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        }
+        // dS^T = P^T (dP^T - Delta), rounded to bf16 for the K^T dS^T product.
+        bf16x8 dsb[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           float e[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             const int i = 8 * st + u;
-            e[u] = exp2_fast(s[kb][i] * p.scale_log2 - l2) * dp[kb][i];
+            e[u] = exp2_fast(s[i] * p.scale_log2 - l2) * dp[i];
           }
-          dsb[kb][st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
+          dsb[st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
         }
-      // dQ^T += K^T dS^T, K^T read transposed from the K rows.
+        // dQ^T += K^T dS^T, K^T read transposed from the K rows.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int rows = (2 * kb + st) * ROW16;
-#pragma unroll
-          for (int c = 0; c < NDB; ++c) {
-            const bf16x8 a = cat8(lds_read_tr4(reinterpret_cast<const bf16*>(Kt + rows + toff[0][c])),
-                                  lds_read_tr4(reinterpret_cast<const bf16*>(Kt + rows + toff[1][c])));
-            acc[c] = mfma32(a, dsb[kb][st], acc[c]);
-          }
+        for (int n = 0; n < NDQ; ++n) {
+          if (n + TPF < NDQ) ta[(n + TPF) % (TPF + 1)] = tread(n + TPF);
+          acc[n % NDB] = mfma32(ta[n % (TPF + 1)], dsb[n / NDB], acc[n % NDB]);
         }
+      }
     }
     wait_copies();
     barrier_lds();
