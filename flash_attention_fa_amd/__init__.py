@@ -5,6 +5,7 @@ computation runs in the library's HIP kernels; PyTorch only provides device
 memory and the current stream.  The functions mirror the C entry points:
 
     fa_fwd(q, k, v, ...)                     -> (o, lse)
+    fa_fwd_noalloc(q, k, v, ...)             -> (o, lse), workspace from the library's static array
     fa_fwd_workspace_bytes(q, k, ...)        -> int
     fa_bwd(q, k, v, o, lse, dout, ...)       -> (dq, dk, dv)
     fa_bwd_stage(stage, q, k, v, ..., dq, dk, dv, workspace)   (one stage of fa_bwd)
@@ -31,7 +32,7 @@ from ._lib import (FAError, FA_BF16, FA_F32, FA_MASK_FULL, FA_MASK_CAUSAL,  # no
 
 FULL, CAUSAL, TTT, WINDOW = FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_TTT, FA_MASK_WINDOW
 
-__all__ = ["fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes",
+__all__ = ["fa_fwd", "fa_fwd_noalloc", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes",
            "fa_last_error", "FA_BWD_DELTA", "FA_BWD_DKDV", "FA_BWD_DQ",
            "attention", "FAError", "FULL", "CAUSAL", "TTT", "WINDOW",
            "lsm_loss_fwd", "lsm_loss_bwd", "logsoftmax_loss"]
@@ -132,6 +133,30 @@ def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=Non
         workspace = _scratch(need, q.device, stream)
     _lib.check(_lib.lib().fa_fwd(a, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                  _stream(q, stream)))
+    return out, lse
+
+
+def fa_fwd_noalloc(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=None, scale=None,
+                   out=None, lse=None, stream=None, frozen_keys=0):
+    """fa_fwd without a workspace argument: the library's static device
+    scratch holds the transposed V (for callers that cannot allocate, e.g.
+    under graph capture; pass ``out`` and ``lse`` there, since allocating
+    them here would defeat the purpose).  Same results as fa_fwd, bitwise.
+    Calls that overlap in time on one device share the scratch and race."""
+    B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    a = _fwd_shape_args(q, k)
+    a.scale = 0.0 if scale is None else float(scale)
+    a.q, a.k, a.v, a.o = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
+    a.lse = lse.data_ptr()
+    a.mask = _mask(mask_kind, causal_shift, kv_valid, window, frozen_keys)
+    for t in (k, v, out):
+        if t.dtype != q.dtype:
+            raise FAError(_lib.FA_ERR_INVALID_ARG, "q, k, v and out must share one dtype")
+    _lib.check(_lib.lib().fa_fwd_noalloc(a, _stream(q, stream)))
     return out, lse
 
 

@@ -25,8 +25,12 @@ FA_MASK_CAUSAL = 1
 FA_MASK_TTT = 2
 FA_MASK_WINDOW = 3
 
-EXPORTED = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_bytes",
-            "fa_last_error", "fa_lsm_loss_fwd", "fa_lsm_loss_bwd")
+EXPORTED = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_fwd_noalloc", "fa_bwd", "fa_bwd_stage",
+            "fa_bwd_workspace_bytes", "fa_last_error", "fa_lsm_loss_fwd", "fa_lsm_loss_bwd")
+
+# Bytes of the static device array fa_fwd_noalloc takes its workspace from
+# (FA_FWD_NOALLOC_SCRATCH_BYTES in include/fa.h).
+FWD_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2
@@ -93,6 +97,8 @@ def lib():
         L.fa_fwd.argtypes = [ctypes.POINTER(fa_fwd_args), ctypes.c_void_p,
                              ctypes.c_size_t, ctypes.c_void_p]
         L.fa_fwd.restype = ctypes.c_int
+        L.fa_fwd_noalloc.argtypes = [ctypes.POINTER(fa_fwd_args), ctypes.c_void_p]
+        L.fa_fwd_noalloc.restype = ctypes.c_int
         L.fa_fwd_workspace_bytes.argtypes = [ctypes.POINTER(fa_fwd_args)]
         L.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.fa_bwd.argtypes = [ctypes.POINTER(fa_bwd_args), ctypes.c_void_p,

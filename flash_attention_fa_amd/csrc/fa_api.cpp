@@ -11,7 +11,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 
 namespace {
 
@@ -198,20 +200,42 @@ fa_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   return FA_OK;
 }
 
-}  // namespace
+// ---- the forward's allocation-free variant: a static scratch array ---------
+// fa_fwd_noalloc takes its workspace (the forward's V^T copy) from this
+// device array instead of the caller.  Each device the library runs on holds
+// its own copy for the life of the process.  Host code never uses the
+// array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocScratchBytes = FA_FWD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
-extern "C" {
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_ptr;   // device ordinal -> scratch's address there
 
-const char* fa_last_error(void) { return g_error.c_str(); }
-
-size_t fa_fwd_workspace_bytes(const fa_fwd_args* a) {
-  if (!a) return 0;
-  Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
-  return fwd_ws_bytes(s);
+fa_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_noalloc: no current device (%s)", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(FA_ERR_HIP, "fa_fwd_noalloc: the scratch array has no address on device %d (%s)", dev,
+                  hipGetErrorString(e));
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return FA_OK;
 }
 
-fa_status fa_fwd(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!a) return fail(FA_ERR_INVALID_ARG, "fa_fwd: args is NULL");
+// fa_fwd and fa_fwd_noalloc: validation, then the launches.  With
+// static_ws the workspace is the scratch array (its size is ws_bytes; its
+// address is looked up only once everything else is valid).
+fa_status fwd_run(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t stream, bool static_ws) {
+  const char* fn = static_ws ? "fa_fwd_noalloc" : "fa_fwd";
+  if (!a) return fail(FA_ERR_INVALID_ARG, "%s: args is NULL", fn);
   Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
   fa_status st = check_shape(s, a->mask);
   if (st != FA_OK) return st;
@@ -232,8 +256,16 @@ fa_status fa_fwd(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t st
   if (s.dtype == FA_BF16 && vt_keys(s) >= (int64_t(1) << 24))
     return fail(FA_ERR_UNSUPPORTED, "Skv=%d is too large (limit 2^24 - 64)", s.Skv);
   const size_t need = fwd_ws_bytes(s);
-  if ((st = check_ws(ws, ws_bytes, need))) return st;
-  Range rw{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + need, need == 0};
+  if (static_ws) {
+    if (need > ws_bytes)
+      return fail(FA_ERR_UNSUPPORTED,
+                  "fa_fwd_noalloc: these shapes need %zu bytes of scratch (B*Hkv*D*Skv rounded up, bf16); "
+                  "its static scratch holds %zu; call fa_fwd with a workspace instead", need, ws_bytes);
+  } else if ((st = check_ws(ws, ws_bytes, need))) {
+    return st;
+  }
+  // (the static scratch cannot overlap a caller's buffer: its address is never handed out)
+  Range rw{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + need, need == 0 || static_ws};
   for (const Range* in : {&rq, &rk, &rv}) {
     if (overlap(ro, *in)) return fail(FA_ERR_ALIAS, "o overlaps an input tensor");
     if (overlap(rl, *in)) return fail(FA_ERR_ALIAS, "lse overlaps an input tensor");
@@ -246,6 +278,7 @@ fa_status fa_fwd(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t st
     return fail(FA_ERR_ALIGNMENT, "kv_valid: pointer is not 4-byte aligned");
   if (!rows) return FA_OK;  // nothing to compute
   if ((st = check_device())) return st;
+  if (static_ws && need > 0 && (st = scratch_address(&ws))) return st;
 
   fa::Params p{};
   fill_common(p, s, a->scale, a->mask);
@@ -254,8 +287,28 @@ fa_status fa_fwd(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t st
   p.vt = ws;
   p.vt_ss = vt_keys(s);
   hipError_t e = s.dtype == FA_BF16 ? fa::launch_fwd_bf16(p, stream) : fa::launch_fwd_f32(p, stream);
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s launch failed: %s", fn, hipGetErrorString(e));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_last_error(void) { return g_error.c_str(); }
+
+size_t fa_fwd_workspace_bytes(const fa_fwd_args* a) {
+  if (!a) return 0;
+  Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
+  return fwd_ws_bytes(s);
+}
+
+fa_status fa_fwd(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fwd_run(a, ws, ws_bytes, stream, false);
+}
+
+fa_status fa_fwd_noalloc(const fa_fwd_args* a, hipStream_t stream) {
+  return fwd_run(a, nullptr, kNoAllocScratchBytes, stream, true);
 }
 
 size_t fa_bwd_workspace_bytes(const fa_bwd_args* a) {

@@ -183,6 +183,21 @@ size_t fa_fwd_workspace_bytes(const fa_fwd_args* args);
  * (0 = null stream). */
 fa_status fa_fwd(const fa_fwd_args* args, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and results as fa_fwd, bitwise, with the workspace taken
+ * from a static device array of FA_FWD_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each device it runs on until the process ends.  The
+ * caller still passes the inputs and outputs; the call itself allocates
+ * nothing.  Shapes whose fa_fwd_workspace_bytes exceed the array are refused
+ * with FA_ERR_UNSUPPORTED (before any launch).  Every call on one device
+ * shares that device's array: calls that overlap in time on one device (on
+ * different streams, or from different threads without ordering) race, and
+ * must be ordered by the caller.  Nothing in the array needs to start at
+ * zero (each call writes every element it reads). */
+#define FA_FWD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fa_status fa_fwd_noalloc(const fa_fwd_args* args, hipStream_t stream);
+
 /* Bytes of device scratch fa_bwd needs for these arguments.  It is linear
  * in the sequence lengths: the backward never holds the S x S score or
  * probability matrix, it rebuilds P tile by tile from the saved logsumexp

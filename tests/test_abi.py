@@ -281,3 +281,43 @@ def test_bwd_stage_validates_like_bwd():
     a = bwd_args()
     for stage in (_lib.FA_BWD_DELTA, _lib.FA_BWD_DKDV, _lib.FA_BWD_DQ):
         assert _lib.lib().fa_bwd_stage(a, stage, WS, 16, None) == _lib.FA_ERR_INVALID_ARG
+
+
+# ---- fa_fwd_noalloc: the forward with the library's static scratch --------
+
+def fwd_noalloc(a):
+    st = _lib.lib().fa_fwd_noalloc(a, None)
+    return st, _lib.last_error()
+
+
+def test_noalloc_validates_like_fa_fwd():
+    for name, kw, status, text in FWD_CASES:
+        st, msg = fwd_noalloc(fwd_args(**kw))
+        assert st == status and text in msg, (name, msg)
+    assert _lib.lib().fa_fwd_noalloc(None, None) == _lib.FA_ERR_INVALID_ARG
+    a = fwd_args()
+    a.o.data = a.q.data + 64                  # output inside an input
+    assert fwd_noalloc(a)[0] == _lib.FA_ERR_ALIAS
+    for kw in (dict(B=0), dict(Sq=0)):        # empty: a no-op
+        assert fwd_noalloc(fwd_args(**kw))[0] == _lib.FA_OK
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch():
+    cap = _lib.FWD_NOALLOC_SCRATCH_BYTES
+    # V^T of B*Hkv*D*Skv bf16 values: 64 MiB holds Skv = 65536 at Hkv=4, D=128,
+    # and not 65600 (rounded up to 65600 keys, 64.06 MiB)
+    ok = fwd_args(B=1, Hq=32, Hkv=4, Sq=64, Skv=65536, D=128, kind=0)
+    big = fwd_args(B=1, Hq=32, Hkv=4, Sq=64, Skv=65600, D=128, kind=0)
+    assert _lib.lib().fa_fwd_workspace_bytes(ok) == cap
+    assert _lib.lib().fa_fwd_workspace_bytes(big) > cap
+    st, msg = fwd_noalloc(big)
+    assert st == _lib.FA_ERR_UNSUPPORTED and "scratch" in msg and "fa_fwd" in msg
+
+
+@no_device
+def test_noalloc_valid_request_without_device_fails_cleanly():
+    st, msg = fwd_noalloc(fwd_args())
+    assert st == _lib.FA_ERR_HIP, msg
+    # fp32 needs no scratch at any size: never refused for its size
+    st, msg = fwd_noalloc(fwd_args(B=1, Hq=32, Hkv=4, Sq=64, Skv=65600, D=128, kind=0, dtype=_lib.FA_F32))
+    assert st == _lib.FA_ERR_HIP, msg
