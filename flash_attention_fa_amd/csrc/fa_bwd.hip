@@ -414,11 +414,28 @@ dq_dma_kernel(Params p) {
   // Key tile t (K rows then V rows) into buffer k; keys that are not real
   // (and every key when t < 0) come from key 0: finite, and masked.  Keys
   // below kv_valid are real (kv_valid <= the walked key count).
+  // A tile whose rows are all real keys takes the scalar-base form (per-lane
+  // byte offsets computed once, no vector instructions per copy); a negative
+  // sequence stride, a ragged last tile and tiles past the end take the
+  // general form.
+  unsigned voff[LPW];
+#pragma unroll
+  for (int x = 0; x < LPW; ++x) voff[x] = 2u * (unsigned)(rstep[x] + rbase + cofs[x]);
+  const bool soff_ok = xss >= 0;
   auto copy_tile = [&](int t, int k) __attribute__((always_inline)) {
     const int tb = t * TK;
-    const int lim = t >= 0 ? (tb + TK <= m.kvv ? TK : m.kvv - tb) : 0;   // rows below lim are real keys
-    const bf16* base = Xg + (int64_t)tb * xss;
     const unsigned lbuf = lds0 + k * L::BUF;
+    if (soff_ok && t >= 0 && tb + TK <= m.kvv) {
+      const bf16* sbase = Xg + (int64_t)tb * xss;
+#pragma unroll
+      for (int x = 0; x < LPW; ++x) {
+        const int idx = wave * LPW + x;
+        if (ALL_COPY || idx < 2 * NINS) lds_dma16_s(sbase, voff[x], lbuf + ldso[x]);
+      }
+      return;
+    }
+    const int lim = t >= 0 ? m.kvv - tb : 0;   // rows below lim are real keys
+    const bf16* base = Xg + (int64_t)tb * xss;
 #pragma unroll
     for (int x = 0; x < LPW; ++x) {
       const int idx = wave * LPW + x;
@@ -984,10 +1001,23 @@ dkdv_split_kernel(Params p) {
   auto advance = [&](StepPos& sp) __attribute__((always_inline)) {
     if (++sp.hs == hend) { sp.hs = hbeg; sp.q0 -= TQ; }
   };
+  // Whole tiles (every row below Sq) with a non-negative row stride take the
+  // scalar-base form: per-lane byte offsets computed once, no vector
+  // instructions per copy.
+  unsigned qvoff[QLPW];
+#pragma unroll
+  for (int x = 0; x < QLPW; ++x) qvoff[x] = 2u * (unsigned)(((cidx0 % QINS + x) * RPI + crow) * (int)sss + schunk[x]);
+  const unsigned lds_stage0 = lds_addr_of(smem) + (stage_g ? L::TILE : 0);
   auto stage_rows = [&](const StepPos& sp, int buf) __attribute__((always_inline)) {
     const bf16* Sg = Sbase + (int64_t)(hk * p.G + sp.hs) * ssh + (int64_t)sp.q0 * sss;
     unsigned char* dst = smem + buf * L::STAGE + (stage_g ? L::TILE : 0);
     const bool whole = sp.q0 + TQ <= p.Sq;   // every row real: no per-lane select
+    if (whole && sss >= 0) {
+#pragma unroll
+      for (int x = 0; x < QLPW; ++x)
+        lds_dma16_s(Sg, qvoff[x], lds_stage0 + buf * L::STAGE + (cidx0 % QINS + x) * 1024);
+      return;
+    }
 #pragma unroll
     for (int x = 0; x < QLPW; ++x) {
       const int ii = cidx0 % QINS + x;

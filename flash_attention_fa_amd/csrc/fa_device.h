@@ -227,6 +227,27 @@ __device__ __forceinline__ void lds_dma16_at(const void* g, unsigned lds_addr) {
                : "memory", "m0");
 }
 
+// lds_dma16_at with a wave-uniform 64-bit base address (held in scalar
+// registers) and a per-lane 32-bit byte offset: lane l's 16 bytes at
+// sbase + voff land at lds_addr + 16 l.  The address arithmetic of a tile's
+// copies then costs no vector instructions: the offsets are computed once and
+// only the scalar base moves from tile to tile.
+// A wave-uniform pointer moved to scalar registers (both 32-bit halves read
+// from the first active lane).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(lo | (hi << 32));
+}
+
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, unsigned voff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(uniform_ptr(sbase)), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // s_waitcnt with only the vector-memory counter constrained (<= n).
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -194,11 +194,29 @@ fwd_kernel(Params p) {
   // selection: the pre-pass zeroed every position that is not a real key,
   // and t < 0 reads tile 0.  Keys below kv_valid are real (kv_valid <= the
   // walked key count).
+  // A tile whose K rows are all real keys (every tile but a ragged last one)
+  // takes the scalar-base form: per-lane byte offsets computed once (voff),
+  // the tile's base in scalar registers, no vector instructions.  The offsets
+  // are unsigned there, so a K view with a negative sequence stride always
+  // takes the general form.
+  unsigned voff[LPW];
+#pragma unroll
+  for (int x = 0; x < LPW; ++x) voff[x] = 2u * (unsigned)(rstep[x] + rbase + cofs[x]);
+  const bool soff_ok = p.k.ss >= 0;
   auto copy_tiles = [&](int t, int k) __attribute__((always_inline)) {
     const int tb = t * TK;
-    const int lim = t >= 0 ? (tb + TK <= m.kvv ? TK : m.kvv - tb) : 0;   // K rows below lim are real keys
-    const bf16* base = wk ? Kg + (int64_t)tb * p.k.ss : VTg + (t >= 0 ? tb : 0);
     const unsigned lbuf = lds0 + k * L::TILE_BYTES;
+    if (soff_ok && t >= 0 && tb + TK <= m.kvv) {
+      const bf16* sbase = wk ? Kg + (int64_t)tb * p.k.ss : VTg + tb;
+#pragma unroll
+      for (int x = 0; x < LPW; ++x) {
+        const int idx = wave * LPW + x;
+        if (ALL_COPY || idx < 2 * NINS) lds_dma16_s(sbase, voff[x], lbuf + ldso[x]);
+      }
+      return;
+    }
+    const int lim = t >= 0 ? m.kvv - tb : 0;   // K rows below lim are real keys
+    const bf16* base = wk ? Kg + (int64_t)tb * p.k.ss : VTg + (t >= 0 ? tb : 0);
 #pragma unroll
     for (int x = 0; x < LPW; ++x) {
       const int idx = wave * LPW + x;
