@@ -372,10 +372,15 @@ static fa_status bwd_run(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStr
   p.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + row_array_bytes(s));
   p.dkv_part = part_bytes(s, a->mask.kind) ? reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * row_array_bytes(s))
                                             : nullptr;
+  // The whole backward in bf16 runs the two gradient stages as one
+  // (fa::STAGE_GRADS): the same workgroups, bitwise the same results.
+  const bool whole = first_stage == fa::STAGE_DELTA && last_stage == fa::STAGE_DQ && s.dtype == FA_BF16;
   for (int stage = first_stage; stage <= last_stage; ++stage) {
-    hipError_t e = s.dtype == FA_BF16 ? fa::launch_bwd_bf16(p, stage, stream)
-                                      : fa::launch_bwd_f32(p, stage, stream);
+    const int run = whole && stage == fa::STAGE_DKDV ? fa::STAGE_GRADS : stage;
+    hipError_t e = s.dtype == FA_BF16 ? fa::launch_bwd_bf16(p, run, stream)
+                                      : fa::launch_bwd_f32(p, run, stream);
     if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_bwd launch failed: %s", hipGetErrorString(e));
+    if (run == fa::STAGE_GRADS) break;
   }
   return FA_OK;
 }

@@ -302,8 +302,7 @@ struct DqDma {
 // s*L + i of each later step s to row i's dQ with vector arithmetic
 // (ttt_fold).
 template <int D, int NW, int MK>
-__global__ void __launch_bounds__(NW * 64, 2)
-dq_dma_kernel(Params p) {
+__device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
   constexpr bool TTT = MK == MK_TTT;
   using L = DqDma<D>;
   constexpr int TQ = NW * 32;
@@ -325,7 +324,7 @@ dq_dma_kernel(Params p) {
 
   const int nq = (p.Sq + TQ - 1) / TQ;
   int col, rank;
-  map_block(blockIdx.x, p.B * p.Hq, nq, col, rank);
+  map_block(bid, p.B * p.Hq, nq, col, rank);
   const int b = col / p.Hq, h = col % p.Hq, hk = h / p.G;
   const int qtile = p.mask.kind == MASK_FULL ? rank : nq - 1 - rank;
   MaskB m = resolve_mask(p, b);
@@ -582,6 +581,12 @@ dq_dma_kernel(Params p) {
             to_bf16x4(acc[c][4 * g] * sc, acc[c][4 * g + 1] * sc, acc[c][4 * g + 2] * sc, acc[c][4 * g + 3] * sc);
       }
   }
+}
+
+template <int D, int NW, int MK>
+__global__ void __launch_bounds__(NW * 64, 2)
+dq_dma_kernel(Params p) {
+  dq_dma_body<D, NW, MK>(p, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -903,8 +908,7 @@ struct KvSplit {
 // dkdv_split); without it one workgroup takes every step of its block and
 // writes dK, dV.
 template <int D, int MK, bool SPLIT>
-__global__ void __launch_bounds__(512)
-dkdv_split_kernel(Params p) {
+__device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
   using L = KvSplit<D>;
   constexpr int NW = L::NW, TKW = L::TKW, TQ = L::TQ;
   constexpr int NJ = D / 16, NDB = D / 32;
@@ -930,7 +934,7 @@ dkdv_split_kernel(Params p) {
   const int nkeys = walk_keys(p);
   const int nkt = (nkeys + TKW - 1) / TKW;
   int col, rank;
-  map_block(blockIdx.x, p.B * p.Hkv * (SPLIT ? 2 : 1), nkt, col, rank);
+  map_block(bid, p.B * p.Hkv * (SPLIT ? 2 : 1), nkt, col, rank);
   const int half = SPLIT ? col & 1 : 0, bh = SPLIT ? col >> 1 : col;
   const int b = bh / p.Hkv, hk = bh % p.Hkv;
   MaskB m = resolve_mask(p, b);
@@ -1212,6 +1216,31 @@ dkdv_split_kernel(Params p) {
   }
 }
 
+template <int D, int MK, bool SPLIT>
+__global__ void __launch_bounds__(512)
+dkdv_split_kernel(Params p) {
+  dkdv_split_body<D, MK, SPLIT>(p, blockIdx.x);
+}
+
+// The two gradient kernels in one launch (D >= 32, the 8-wave dQ): blocks
+// [0, nkv) are dkdv_split_kernel's workgroups, blocks [nkv_pad, gridDim) the
+// dQ kernel's (nkv_pad is nkv rounded up to a multiple of 8, so the dQ blocks
+// keep their XCD placement; the blocks in between do nothing).  Each block
+// computes exactly what it computes in its own kernel, so the results are
+// bitwise those of the two launches in turn; as the dK/dV workgroups drain,
+// dQ workgroups take over their compute units instead of leaving them idle
+// until the dK/dV launch ends.
+template <int D, int MKKV, bool SPLIT, int MKQ>
+__global__ void __launch_bounds__(512, 2)
+grads_kernel(Params p, int nkv, int nkv_pad) {
+  const int bid = blockIdx.x;
+  if (bid < nkv_pad) {
+    if (bid < nkv) dkdv_split_body<D, MKKV, SPLIT>(p, bid);
+    return;
+  }
+  dq_dma_body<D, 8, MKQ>(p, bid - nkv_pad);
+}
+
 // dK = scale * (half 0 + half 1), dV = half 0 + half 1, rounded to bf16; 8
 // consecutive d of one key per thread.
 template <int D>
@@ -1317,9 +1346,65 @@ hipError_t launch_dq(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// After the dK/dV products of the step-0 keys: the reduction of the two
+// halves' partial sums (split blocks) and, under TTT, the later steps' keys.
+template <int D>
+hipError_t launch_dkdv_rest(const Params& p, bool split, hipStream_t stream) {
+  hipError_t e;
+  const int nkeys = walk_keys(p);
+  if (split) {
+    const int64_t n8 = (int64_t)p.B * p.Hkv * nkeys * D / 8;
+    hipLaunchKernelGGL(dkdv_reduce_kernel<D>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t nlate = (int64_t)p.B * p.Hkv * (p.Skv - nkeys);
+  if (p.mask.kind == MASK_TTT && nlate > 0) {
+    constexpr int KPB = 256 / (D / 8);
+    hipLaunchKernelGGL(ttt_dkdv_kernel<D>, dim3((unsigned)((nlate + KPB - 1) / KPB)), dim3(256), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// dK/dV and dQ as one grads_kernel launch, when both take 512-thread
+// workgroups (D >= 32 and enough query rows for the 8-wave dQ kernel) and both
+// have work; sets `done`.  Otherwise leaves `done` false and launches nothing.
+template <int D>
+hipError_t launch_grads(const Params& p, hipStream_t stream, bool& done) {
+  done = false;
+  if constexpr (D >= 32) {
+    using LD = KvSplit<D>;
+    const int nkeys = walk_keys(p);
+    const int64_t ndq = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
+    const bool split = dkdv_split(p.B, p.Hkv, nkeys);
+    const int64_t nkv = (int64_t)p.B * p.Hkv * (split ? 2 : 1) * ((nkeys + LD::TKW - 1) / LD::TKW);
+    if (ndq < 512 || nkv == 0) return hipSuccess;
+    const int64_t nkv_pad = (nkv + 7) / 8 * 8;
+    if (nkv_pad + ndq > INT_MAX) return hipSuccess;
+    const int mk = mask_instance(p.mask.kind);
+    auto k = mk == MK_WIN ? (split ? grads_kernel<D, MK_WIN, true, MK_WIN> : grads_kernel<D, MK_WIN, false, MK_WIN>)
+           : mk == MK_TTT ? (split ? grads_kernel<D, MK_FC, true, MK_TTT> : grads_kernel<D, MK_FC, false, MK_TTT>)
+                          : (split ? grads_kernel<D, MK_FC, true, MK_FC> : grads_kernel<D, MK_FC, false, MK_FC>);
+    const int lds = LD::BYTES > DqDma<D>::BYTES ? LD::BYTES : DqDma<D>::BYTES;
+    hipError_t e;
+    if ((e = set_lds(k, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3((unsigned)(nkv_pad + ndq)), dim3(512), lds, stream, p, (int)nkv, (int)nkv_pad);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    done = true;
+    return launch_dkdv_rest<D>(p, split, stream);
+  }
+  return hipSuccess;
+}
+
 template <int D>
 hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
   hipError_t e;
+  if (stage == STAGE_GRADS) {
+    bool done = false;
+    if ((e = launch_grads<D>(p, stream, done)) != hipSuccess || done) return e;
+    if ((e = launch_stage<D>(p, STAGE_DKDV, stream)) != hipSuccess) return e;
+    return launch_stage<D>(p, STAGE_DQ, stream);
+  }
   const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
   if (stage == STAGE_DELTA && rows > 0) {
     constexpr int RPB = 256 / (D / 8);
@@ -1339,17 +1424,9 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
         if ((e = set_lds(k, LD::BYTES)) != hipSuccess) return e;
         hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(LD::NW * 64), LD::BYTES, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (split) {
-          const int64_t n8 = (int64_t)p.B * p.Hkv * nkeys * D / 8;
-          hipLaunchKernelGGL(dkdv_reduce_kernel<D>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p);
-          if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
-      }
-      const int64_t nlate = (int64_t)p.B * p.Hkv * (p.Skv - nkeys);
-      if (p.mask.kind == MASK_TTT && nlate > 0) {
-        constexpr int KPB = 256 / (D / 8);
-        hipLaunchKernelGGL(ttt_dkdv_kernel<D>, dim3((unsigned)((nlate + KPB - 1) / KPB)), dim3(256), 0, stream, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_dkdv_rest<D>(p, split, stream)) != hipSuccess) return e;
+      } else if ((e = launch_dkdv_rest<D>(p, false, stream)) != hipSuccess) {
+        return e;
       }
     }
   } else if (stage == STAGE_DKDV) {

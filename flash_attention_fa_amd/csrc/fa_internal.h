@@ -55,8 +55,9 @@ inline bool dkdv_split(int B, int Hkv, int keys) {
 // Launchers (one translation unit per kernel family).  Each returns the
 // hipError_t of its launches; shapes were validated by the dispatcher.
 // Backward stages: Delta = rowsum(dO * O), then the dK/dV and dQ kernels
-// (independent of each other once Delta exists).
-enum { STAGE_DELTA = 0, STAGE_DKDV = 1, STAGE_DQ = 2 };
+// (independent of each other once Delta exists).  STAGE_GRADS (bf16 only) is
+// DKDV and DQ together, in one launch where their workgroups allow it.
+enum { STAGE_DELTA = 0, STAGE_DKDV = 1, STAGE_DQ = 2, STAGE_GRADS = 3 };
 // Soft-target log-softmax loss (fa_lsm_loss_fwd / _bwd), validated by the
 // dispatcher.
 struct LossParams {

@@ -199,22 +199,36 @@ def test_bitwise_determinism(kind):
         assert np.array_equal(a[name], b[name]), name
 
 
-@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 16), (torch.bfloat16, 64), (torch.bfloat16, 128),
-                                     (torch.float32, 64)])
-def test_staged_backward_equals_fa_bwd(dtype, D):
+STAGED = [
+    # dtype, D, B, Hq, Hkv, L, kind
+    (torch.bfloat16, 16, 1, 8, 2, 320, CAUSAL), (torch.bfloat16, 64, 1, 8, 2, 320, CAUSAL),
+    (torch.bfloat16, 128, 1, 8, 2, 320, CAUSAL), (torch.float32, 64, 1, 8, 2, 320, CAUSAL),
+    # 512+ dQ workgroups of 256 rows: fa_bwd runs dK/dV and dQ as one launch
+    (torch.bfloat16, 128, 4, 128, 16, 300, CAUSAL), (torch.bfloat16, 64, 4, 128, 16, 300, TTT),
+    (torch.bfloat16, 32, 4, 128, 16, 300, WINDOW), (torch.bfloat16, 64, 16, 64, 64, 256, CAUSAL),
+]
+
+
+@pytest.mark.parametrize("case", STAGED, ids=[f"{str(c[0])[6:]}_D{c[1]}_B{c[2]}_H{c[3]}_{W.KIND_NAMES[c[6]]}"
+                                               for c in STAGED])
+def test_staged_backward_equals_fa_bwd(case):
     """fa_bwd_stage DELTA, DKDV, DQ in turn writes bitwise what fa_bwd writes
-    (at D >= 32 the dK/dV stage is the split kernel and its reduction)."""
+    (at D >= 32 the dK/dV stage is the split kernel and its reduction; with
+    enough query rows fa_bwd launches the dK/dV and dQ workgroups together)."""
     import flash_attention_fa_amd as fa
-    L = 320
-    q, k, v, do = (x.cuda() for x in inputs(1, 8, 2, L, L, D, dtype, seed=53))
-    say(f"[staged] dtype={dtype} D={D}")
-    o, lse = fa.fa_fwd(q, k, v, mask_kind=CAUSAL)
-    ref = fa.fa_bwd(q, k, v, o, lse, do, mask_kind=CAUSAL)
+    dtype, D, B, Hq, Hkv, L, kind = case
+    Skv = 3 * L if kind == TTT else L
+    win = (50, 7) if kind == WINDOW else None
+    q, k, v, do = (x.cuda() for x in inputs(B, Hq, Hkv, L, Skv, D, dtype, seed=53))
+    say(f"[staged] {case}")
+    kw = dict(mask_kind=kind, window=win)
+    o, lse = fa.fa_fwd(q, k, v, **kw)
+    ref = fa.fa_bwd(q, k, v, o, lse, do, **kw)
     dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
-    ws = torch.empty(fa.fa_bwd_workspace_bytes(q, k, mask_kind=CAUSAL), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(q, k, mask_kind=kind), dtype=torch.uint8, device="cuda")
     # the gradient stages in the opposite order: they are independent once Delta exists
     for stage in (fa.FA_BWD_DELTA, fa.FA_BWD_DQ, fa.FA_BWD_DKDV):
-        fa.fa_bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, mask_kind=CAUSAL)
+        fa.fa_bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, **kw)
     torch.cuda.synchronize()
     for name, a, b in zip(("dQ", "dK", "dV"), ref, (dq, dk, dv)):
         assert torch.equal(a, b), name

@@ -1,5 +1,5 @@
 """GPU parity at the workloads' full sizes, through the same calls the
-benchmark times (fa_fwd, then the Delta, dK/dV and dQ stages of the backward).
+benchmark times (fa_fwd, then fa_bwd).
 
 The fp64 oracle cannot materialise 16K x 16K scores for every head, so each
 case compares what it can compute exactly:
@@ -46,8 +46,7 @@ def run_like_bench(w, q, k, v, do):
     o, lse = fa.fa_fwd(qg, kg, vg, **kw)
     dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
     ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(qg, kg, mask_kind=w.kind)), dtype=torch.uint8, device=dev)
-    for stage in (fa.FA_BWD_DELTA, fa.FA_BWD_DKDV, fa.FA_BWD_DQ):
-        fa.fa_bwd_stage(stage, qg, kg, vg, o, lse, dog, dq, dk, dv, ws, **kw)
+    fa.fa_bwd(qg, kg, vg, o, lse, dog, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
