@@ -161,12 +161,12 @@ size_t row_array_bytes(const Shape& s) {
   return (n + 255) / 256 * 256;
 }
 
-// The dK/dV kernel's partial sums (bf16, D >= 32, when it splits its key
-// blocks, fa::dkdv_split): two halves of float32 dK^T and dV^T,
+// The dK/dV kernel's partial sums (bf16, when it splits its key blocks,
+// fa::dkdv_split): two halves of float32 dK^T and dV^T,
 // [2][2][B, Hkv, keys, D], rounded up to 256 bytes, over the keys the tile
 // kernel owns (all Skv, or under TTT the Sq step-0 keys).
 size_t part_bytes(const Shape& s, int kind) {
-  if (s.dtype != FA_BF16 || s.D < 32) return 0;
+  if (s.dtype != FA_BF16) return 0;
   const int keys = kind == FA_MASK_TTT && s.Sq < s.Skv ? s.Sq : s.Skv;
   if (!fa::dkdv_split(std::max(s.B, 0), std::max(s.Hkv, 0), std::max(keys, 0))) return 0;
   size_t n = (size_t)4 * std::max(s.B, 0) * (size_t)std::max(s.Hkv, 0) * (size_t)std::max(keys, 0) *

@@ -8,9 +8,9 @@
 //   Delta_i = sum_d dO_id O_id                      (delta_kernel)
 //   P_ij    = exp(s q_i.k_j - LSE_i)  on allowed pairs, else 0
 //   dP_ij   = dO_i . v_j,   dS_ij = P_ij (dP_ij - Delta_i)
-//   dV_j    = sum_i P_ij dO_i                        (dkdv_kernel)
-//   dK_j    = s sum_i dS_ij q_i                      (dkdv_kernel)
-//   dQ_i    = s sum_j dS_ij k_j                      (dq_kernel)
+//   dV_j    = sum_i P_ij dO_i                        (dkdv_split_kernel)
+//   dK_j    = s sum_i dS_ij q_i                      (dkdv_split_kernel)
+//   dQ_i    = s sum_j dS_ij k_j                      (dq_dma_kernel)
 // dK/dV are owned by key tiles and dQ by query tiles, so every output element
 // is summed by exactly one workgroup in a fixed order: reruns are bitwise
 // identical.  Keys no query may attend get exact zeros.
@@ -58,236 +58,13 @@ __global__ void __launch_bounds__(256) delta_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ: a workgroup owns NW*QB*32 query rows of one (batch, head) and streams
-// key tiles through LDS (as in the forward).  Transposed scores again: lane =
-// query column, so LSE and Delta are one scalar per lane.  Each key tile is
-// staged three ways: K rows (for S^T = K Q^T), V rows (for dP^T = V dO^T) and
-// K transposed (for dQ^T = K^T dS^T).
-constexpr int DQ_TK = 64;
-
-template <int D>
-struct DqLds {
-  static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = D + 8;
-  static constexpr int KTILE = DQ_TK * KSTR;   // K rows
-  static constexpr int KTT = D * STAGE_ROWS;   // K transposed
-  static constexpr int VTILE = DQ_TK * VSTR;   // V rows
-  static constexpr int BUF = KTILE + KTT + VTILE;
-  static constexpr int BYTES = 2 * BUF * 2;
-};
-
-template <int D, int QB, int NW>
-__global__ void __launch_bounds__(NW * 64, 2)
-dq_kernel(Params p) {
-  constexpr int NT = NW * 64;
-  constexpr int TQ = NW * QB * 32;
-  constexpr int TK = DQ_TK;
-  constexpr int HALF = NT / 2;               // threads staging K; the rest stage V
-  constexpr int UNITS = StageUnit<D>::COUNT;
-  constexpr int PER_T = (UNITS + HALF - 1) / HALF;
-  constexpr int NDB = D >= 32 ? D / 32 : 1;
-  constexpr int NJ = D / 16;
-  using L = DqLds<D>;
-  extern __shared__ __align__(16) unsigned char smem[];
-  bf16* const S0 = reinterpret_cast<bf16*>(smem);  // buffer b at S0 + b * L::BUF
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int l32 = lane & 31, hh = lane >> 5;
-
-  const int nq = (p.Sq + TQ - 1) / TQ;
-  int col, rank;
-  map_block(blockIdx.x, p.B * p.Hq, nq, col, rank);
-  const int b = col / p.Hq, h = col % p.Hq, hk = h / p.G;
-  const int qtile = p.mask.kind == MASK_FULL ? rank : nq - 1 - rank;
-  const MaskB m = resolve_mask(p, b);
-  const int qa = qtile * TQ, qb = min(p.Sq, qa + TQ);
-  const int wa = qa + wave * QB * 32, wb = min(p.Sq, wa + QB * 32);
-
-  const bf16* Qg = static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
-  const bf16* Gg = static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh;
-  const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
-  const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
-  const int64_t rowbase = ((int64_t)b * p.Hq + h) * p.Sq;
-
-  bf16x8 qreg[QB][NJ], greg[QB][NJ];
-  float lse2[QB], dlt[QB];
-#pragma unroll
-  for (int qb_ = 0; qb_ < QB; ++qb_) {
-    const int row = wa + qb_ * 32 + l32;
-    const bool ok = row < p.Sq;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      qreg[qb_][j] = ok ? *reinterpret_cast<const bf16x8*>(Qg + (int64_t)row * p.q.ss + 16 * j + 8 * hh)
-                        : bf16x8{};
-      greg[qb_][j] = ok ? *reinterpret_cast<const bf16x8*>(Gg + (int64_t)row * p.dout.ss + 16 * j + 8 * hh)
-                        : bf16x8{};
-    }
-    lse2[qb_] = ok ? p.lse_in[rowbase + row] * 1.4426950408889634f : 0.f;
-    dlt[qb_] = ok ? p.delta[rowbase + row] : 0.f;
-  }
-
-  f32x16 acc[QB][NDB];
-#pragma unroll
-  for (int qb_ = 0; qb_ < QB; ++qb_)
-#pragma unroll
-    for (int c = 0; c < NDB; ++c) acc[qb_][c] = f32x16{};
-
-  // Stage one key tile: the first half of the threads takes K (stored
-  // row-major and transposed), the second half V (row-major).
-  const bool stage_v = tid >= HALF;
-  const bf16* Sg = stage_v ? Vg : Kg;
-  const int64_t sss = stage_v ? p.v.ss : p.k.ss;
-  i32x4 stg[PER_T][4];
-  auto fetch = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int u = tid % HALF + i * HALF;
-      const StageUnit<D> su(u);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = t * TK + 4 * su.rg + r;
-        stg[i][r] = (u < UNITS && key_valid(m, key))
-                        ? *reinterpret_cast<const i32x4*>(Sg + (int64_t)key * sss + 8 * su.c8)
-                        : i32x4{};
-      }
-    }
-  };
-  auto store = [&](int buf) {
-    bf16* base = S0 + buf * L::BUF;
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int u = tid % HALF + i * HALF;
-      if (u < UNITS) {
-        const StageUnit<D> su(u);
-        if (stage_v) {
-          store_rows4(base + L::KTILE + L::KTT, L::VSTR, su.rg, su.c8, stg[i]);
-        } else {
-          store_rows4(base, L::KSTR, su.rg, su.c8, stg[i]);
-          store_trans4(base + L::KTILE, su.rg, su.c8, stg[i]);
-        }
-      }
-    }
-  };
-
-  TileWalk walk;
-  walk.start(m, qa, qb, TK);
-  int buf = 0;
-  if (walk.valid()) {
-    fetch(walk.t);
-    store(0);
-  }
-  __syncthreads();
-
-  const bool d_lane_ok = D >= 32 || l32 < 16;
-  const int kt_row = d_lane_ok ? l32 : 0;
-
-  while (walk.valid()) {
-    const int t = walk.t;
-    TileWalk nxt = walk;
-    nxt.next(m, qa, qb, TK);
-    if (nxt.valid()) fetch(nxt.t);
-
-    const int k0 = t * TK;
-    const int state = tile_state(m, k0, TK, wa, wb);
-    if (state != TILE_SKIP) {
-      const bf16* Kt = S0 + buf * L::BUF;
-      const bf16* Ktt = Kt + L::KTILE;
-      const bf16* Vt = Ktt + L::KTT;
-      f32x16 s[QB][2], dp[QB][2];
-#pragma unroll
-      for (int qb_ = 0; qb_ < QB; ++qb_)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) { s[qb_][kb] = f32x16{}; dp[qb_][kb] = f32x16{}; }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ak = lds_read8(Kt + (32 * kb + l32) * L::KSTR + 16 * j + 8 * hh);
-          const bf16x8 av = lds_read8(Vt + (32 * kb + l32) * L::VSTR + 16 * j + 8 * hh);
-#pragma unroll
-          for (int qb_ = 0; qb_ < QB; ++qb_) {
-            s[qb_][kb] = mfma32(ak, qreg[qb_][j], s[qb_][kb]);
-            dp[qb_][kb] = mfma32(av, greg[qb_][j], dp[qb_][kb]);
-          }
-        }
-      if (state == TILE_PART) {
-#pragma unroll
-        for (int qb_ = 0; qb_ < QB; ++qb_) {
-          const int qi = wa + qb_ * 32 + l32;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-              s[qb_][kb][i] = allowed(m, qi, key) ? s[qb_][kb][i] : -INFINITY;
-            }
-        }
-      }
-      // dS^T = P^T (dP^T - Delta), rounded to bf16 for the dS K product.
-      bf16x8 dsb[QB][2][2];
-#pragma unroll
-      for (int qb_ = 0; qb_ < QB; ++qb_)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            float e[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int i = 8 * st + u;
-              const float pr = exp2_fast(s[qb_][kb][i] * p.scale_log2 - lse2[qb_]);
-              e[u] = pr * (dp[qb_][kb][i] - dlt[qb_]);
-            }
-            dsb[qb_][kb][st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
-          }
-      // dQ^T += K^T dS^T  (K^T straight from the row-major K tile).
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-          for (int c = 0; c < NDB; ++c) {
-            bf16x8 a = lds_read8(Ktt + tswz(32 * c + kt_row, 32 * kb + 16 * st + 8 * hh));
-            if (!d_lane_ok) a = bf16x8{};
-#pragma unroll
-            for (int qb_ = 0; qb_ < QB; ++qb_) acc[qb_][c] = mfma32(a, dsb[qb_][kb][st], acc[qb_][c]);
-          }
-        }
-    }
-    if (nxt.valid()) store(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    walk = nxt;
-  }
-
-  bf16* Dg = static_cast<bf16*>(const_cast<void*>(p.dq.ptr)) + b * p.dq.sb + h * p.dq.sh;
-#pragma unroll
-  for (int qb_ = 0; qb_ < QB; ++qb_) {
-    const int row = wa + qb_ * 32 + l32;
-    if (row < p.Sq) {
-#pragma unroll
-      for (int c = 0; c < NDB; ++c)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = 32 * c + 8 * g + 4 * hh;
-          if (d < D) {
-            const float sc = p.scale;
-            *reinterpret_cast<bf16x4*>(Dg + (int64_t)row * p.dq.ss + d) =
-                to_bf16x4(acc[qb_][c][4 * g] * sc, acc[qb_][c][4 * g + 1] * sc,
-                          acc[qb_][c][4 * g + 2] * sc, acc[qb_][c][4 * g + 3] * sc);
-          }
-        }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dQ with asynchronous staging (D >= 32): the forward's pipeline with a third
+// dQ with asynchronous staging: the forward's pipeline with a third
 // product.  Key tiles of K and V rows are copied HBM -> LDS into a ring of
 // four XOR-swizzled buffers three tiles ahead; per tile, S^T = K Q^T and
 // dP^T = V dO^T (Q and dO in registers, K and V rows from LDS), dS^T =
 // P^T (dP^T - Delta) with P^T = exp2(scale log2(e) S^T - LSE log2(e)), and
 // dQ^T += K^T dS^T with K^T read transposed from the row-major K tile.
+constexpr int DQ_TK = 64;     // keys per LDS tile
 constexpr int DQ_NBUF = 4;
 
 template <int D>
@@ -312,10 +89,11 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
   constexpr int NINS = TK / RPI;
   constexpr int LPW = (2 * NINS + NW - 1) / NW;
   constexpr bool ALL_COPY = LPW * NW == 2 * NINS;
-  constexpr int NDB = D / 32;
+  // 32-wide d blocks of dQ^T; at D = 16 one block whose rows d >= 16 hold
+  // nothing real (their operands read real columns again and are never written)
+  constexpr int NDB = D >= 32 ? D / 32 : 1;
   constexpr int NJ = D / 16;
   constexpr int ROW16 = 16 * 2 * D;
-  static_assert(D >= 32, "transposing reads need D >= 32");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -383,6 +161,7 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
       for (int c = 0; c < NDB; ++c)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          if (32 * c + 8 * g >= D) continue;   // d = 32c + 8g + 4hh does not exist (D = 16)
           const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(kd + 32 * c + 8 * g);
 #pragma unroll
           for (int u = 0; u < 4; ++u) acc[c][4 * g + u] += ds * (float)k4[u];
@@ -454,7 +233,9 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
 #pragma unroll
   for (int j = 0; j < NJ; ++j) koff[j] = swz_off<D>(l32, 16 * j + 8 * hh);
   const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // (at D = 16 the lanes that would address columns 16..31 address real
+  // columns instead; what they deliver lands in rows d >= 16 only)
+  const int tr_col = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) & (D >= 32 ? 31 : D - 1);
   int toff[2][NDB];
 #pragma unroll
   for (int c = 0; c < NDB; ++c) {
@@ -576,6 +357,7 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * c + 8 * g + 4 * hh;
+        if (32 * c + 8 * g >= D) continue;   // rows d >= D of the block (D = 16)
         const float sc = p.scale;
         *reinterpret_cast<bf16x4*>(Dg + (int64_t)qi * p.dq.ss + d) =
             to_bf16x4(acc[c][4 * g] * sc, acc[c][4 * g + 1] * sc, acc[c][4 * g + 2] * sc, acc[c][4 * g + 3] * sc);
@@ -590,286 +372,7 @@ dq_dma_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV: a workgroup owns NKB*32 keys of one (batch, kv head) and streams
-// query tiles (Q, dO, LSE, Delta) of every query head of the group through
-// LDS, in a fixed order.  Scores in natural orientation, S = Q K^T, so each
-// lane owns one key column; P and dS feed dV^T = dO^T P and dK^T = Q^T dS
-// from registers, with dO^T and Q^T read transposed from the row-major tiles.
-//
-// Two waves share each 32-key block: wave w takes key block w % NKB and the
-// (w / NKB)-th 32-row half of every 64-row query tile, so a SIMD runs two
-// waves and one hides the other's latency.  K^T stays in registers and V^T
-// is read from an LDS copy of the workgroup's V rows.  Each query tile is
-// staged row-major and transposed, so every MFMA operand is one 16-byte LDS
-// read.  At the end the second wave of each pair hands its partial dK/dV to
-// the first through LDS, which adds it to its own (always in that order) and
-// writes the result.  This kernel serves D = 16; wider heads take
-// dkdv_split_kernel.
-constexpr int KV_TQ = 64;
-
-template <int D, int NKB>
-struct KvLds {
-  static constexpr int STR = D + 8;
-  static constexpr int TILE = KV_TQ * STR;                    // Q or dO rows
-  static constexpr int TT = D * STAGE_ROWS;                   // Q or dO transposed
-  // one stage: Q rows, Q^T, dO rows, dO^T (bf16), then LSE and Delta (fp32)
-  static constexpr int STAGE = 2 * (TILE + TT) * 2 + 2 * KV_TQ * 4;
-  static constexpr int VROWS = NKB * 32;
-  static constexpr int VBYTES = VROWS * STR * 2;                // V rows
-  static constexpr int NDB = D >= 32 ? D / 32 : 1;
-  static constexpr int XBYTES = NKB * NDB * 16 * 64 * 4;      // one partial exchange
-  // double-buffer the stage when it fits next to the K/V rows
-  static constexpr int NBUF = 2 * STAGE + VBYTES <= 160 * 1024 ? 2 : 1;
-  static constexpr int MAIN = NBUF * STAGE + VBYTES;
-  static constexpr int BYTES = MAIN > XBYTES ? MAIN : XBYTES;
-};
-
-template <int D, int NKB>
-__global__ void __launch_bounds__(NKB * 2 * 64)
-dkdv_kernel(Params p) {
-  constexpr int NW = 2 * NKB;
-  constexpr int NT = NW * 64;
-  constexpr int TKW = NKB * 32;       // keys per workgroup
-  constexpr int TQ = KV_TQ;
-  constexpr int DC = D / 8;
-  constexpr int HALF = NT / 2;               // threads staging Q; the rest stage dO
-  constexpr int UNITS = StageUnit<D>::COUNT;
-  constexpr int PER_T = (UNITS + HALF - 1) / HALF;
-  constexpr int NDB = D >= 32 ? D / 32 : 1;
-  constexpr int NJ = D / 16;
-  using L = KvLds<D, NKB>;
-  extern __shared__ __align__(16) unsigned char smem[];
-  bf16* Vs = reinterpret_cast<bf16*>(smem + L::NBUF * L::STAGE);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int kblk = wave % NKB, qhalf = wave / NKB;
-
-  const int nkt = (p.Skv + TKW - 1) / TKW;
-  int col, rank;
-  map_block(blockIdx.x, p.B * p.Hkv, nkt, col, rank);
-  const int b = col / p.Hkv, hk = col % p.Hkv;
-  const int ktile = rank;  // key tile 0 sees the most queries under causal masks
-  const MaskB m = resolve_mask(p, b);
-  const int ka = ktile * TKW, kbnd = min(p.Skv, ka + TKW);
-  const int kw = ka + kblk * 32, kwe = min(p.Skv, kw + 32);
-
-  const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
-  const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
-
-  // K^T as the B operand: lane (key = l32, hh) holds K[key][16j + 8hh .. +8].
-  bf16x8 kreg[NJ];
-  {
-    const int key = kw + l32;
-    const bool ok = key_valid(m, key);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      kreg[j] = ok ? *reinterpret_cast<const bf16x8*>(Kg + (int64_t)key * p.k.ss + 16 * j + 8 * hh)
-                   : bf16x8{};
-  }
-  // The workgroup's V rows, zero for keys that are not real.
-  for (int c = tid; c < TKW * DC; c += NT) {
-    const int r = c / DC, c8 = c % DC;
-    const int key = ka + r;
-    const bool ok = key_valid(m, key);
-    const i32x4 val = ok ? *reinterpret_cast<const i32x4*>(Vg + (int64_t)key * p.v.ss + 8 * c8) : i32x4{};
-    lds_write16(Vs + r * L::STR + 8 * c8, val);
-  }
-
-  f32x16 dka[NDB], dva[NDB];
-#pragma unroll
-  for (int c = 0; c < NDB; ++c) { dka[c] = f32x16{}; dva[c] = f32x16{}; }
-
-  int qlo, qhi;
-  query_hull(m, ka, kbnd, qlo, qhi);
-  if (kbnd <= p.mask.frozen) qhi = qlo;   // every key frozen: no steps, zeros written
-  const int t_first = qlo < qhi ? qlo / TQ : 0;
-  const int t_last = qlo < qhi ? (qhi + TQ - 1) / TQ : 0;
-  const int ntile = t_last - t_first;
-  // (query tile, head) pairs: tiles from the last down, the group's heads
-  // inside.  Every workgroup starts at the last query tile and walks down at
-  // the same pace, so the workgroups sharing an XCD read the same Q / dO
-  // tiles at about the same time and its L2 serves them all.
-  const int nsteps = ntile * p.G;
-
-  // Stage layout: [Q rows | Q^T | dO rows | dO^T | LSE | Delta].
-  auto stage_ptr = [&](int buf) { return reinterpret_cast<bf16*>(smem + buf * L::STAGE); };
-  const bool stage_g = tid >= HALF;     // this thread stages dO (else Q)
-  i32x4 stg[PER_T][4];
-  float lst = 0.f, dst = 0.f;
-  auto fetch = [&](int step) {
-    const int h = hk * p.G + step % p.G;
-    const int q0 = (t_last - 1 - step / p.G) * TQ;
-    const bf16* Sg = stage_g ? static_cast<const bf16*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh
-                             : static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
-    const int64_t sss = stage_g ? p.dout.ss : p.q.ss;
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int u = tid % HALF + i * HALF;
-      const StageUnit<D> su(u);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = q0 + 4 * su.rg + r;
-        stg[i][r] = (u < UNITS && row < p.Sq)
-                        ? *reinterpret_cast<const i32x4*>(Sg + (int64_t)row * sss + 8 * su.c8)
-                        : i32x4{};
-      }
-    }
-    if (tid < TQ) {
-      const int row = q0 + tid;
-      const int64_t rb = ((int64_t)b * p.Hq + h) * p.Sq;
-      lst = row < p.Sq ? p.lse_in[rb + row] * 1.4426950408889634f : 0.f;
-      dst = row < p.Sq ? p.delta[rb + row] : 0.f;
-    }
-  };
-  auto store = [&](int buf) {
-    bf16* base = stage_ptr(buf) + (stage_g ? L::TILE + L::TT : 0);
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int u = tid % HALF + i * HALF;
-      if (u < UNITS) {
-        const StageUnit<D> su(u);
-        store_rows4(base, L::STR, su.rg, su.c8, stg[i]);
-        store_trans4(base + L::TILE, su.rg, su.c8, stg[i]);
-      }
-    }
-    float* Ls = reinterpret_cast<float*>(stage_ptr(buf) + 2 * (L::TILE + L::TT));
-    if (tid < TQ) { Ls[tid] = lst; Ls[TQ + tid] = dst; }
-  };
-
-  int buf = 0;
-  if (nsteps > 0) {
-    fetch(0);
-    store(0);
-  }
-  __syncthreads();
-
-  const bool d_lane_ok = D >= 32 || l32 < 16;
-  const int t_row = d_lane_ok ? l32 : 0;
-  const int key = kw + l32;
-  const bf16* Vrow = Vs + (kblk * 32 + l32) * L::STR + 8 * hh;
-
-  for (int step = 0; step < nsteps; ++step) {
-    if (step + 1 < nsteps) fetch(step + 1);
-    const int q0 = (t_last - 1 - step / p.G) * TQ;
-    const bf16* stg0 = stage_ptr(buf);
-    const bf16* Qs = stg0 + 32 * qhalf * L::STR;
-    const bf16* Qt = stg0 + L::TILE;
-    const bf16* Gs = stg0 + L::TILE + L::TT + 32 * qhalf * L::STR;
-    const bf16* Gt = stg0 + 2 * L::TILE + L::TT;
-    const float* Ls = reinterpret_cast<const float*>(stg0 + 2 * (L::TILE + L::TT)) + 32 * qhalf;
-    const float* Ds = Ls + TQ;
-    const int qa = q0 + 32 * qhalf;
-    const int state = rect_state(m, kw, kwe, qa, min(p.Sq, qa + 32));
-    if (state != TILE_SKIP) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const bf16x8 aq = lds_read8(Qs + l32 * L::STR + 16 * j + 8 * hh);
-        const bf16x8 ag = lds_read8(Gs + l32 * L::STR + 16 * j + 8 * hh);
-        const bf16x8 bv = lds_read8(Vrow + 16 * j);
-        s = mfma32(aq, kreg[j], s);
-        dp = mfma32(ag, bv, dp);
-      }
-      // Per-register query rows: q = qa + 8*(i/4) + 4*hh + i%4.
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float pe[8], de[8];
-#pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2) {
-          const int g = 2 * st + g2;
-          const f32x4 l4 = *FA_LDS(const f32x4, Ls + 8 * g + 4 * hh);
-          const f32x4 d4 = *FA_LDS(const f32x4, Ds + 8 * g + 4 * hh);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = 4 * g + u;
-            float sv = s[i];
-            if (state == TILE_PART) {
-              const int qi = qa + 8 * g + 4 * hh + u;
-              sv = allowed(m, qi, key) ? sv : -INFINITY;
-            }
-            const float pr = exp2_fast(sv * p.scale_log2 - l4[u]);
-            pe[4 * g2 + u] = pr;
-            de[4 * g2 + u] = pr * (dp[i] - d4[u]);
-          }
-        }
-        pb[st] = cat8(to_bf16x4(pe[0], pe[1], pe[2], pe[3]), to_bf16x4(pe[4], pe[5], pe[6], pe[7]));
-        dsb[st] = cat8(to_bf16x4(de[0], de[1], de[2], de[3]), to_bf16x4(de[4], de[5], de[6], de[7]));
-      }
-      // dV^T += dO^T P,  dK^T += Q^T dS  (q-contraction, 16 rows per MFMA),
-      // operands from the transposed copies.
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int pos = 32 * qhalf + 16 * st + 8 * hh;
-#pragma unroll
-        for (int c = 0; c < NDB; ++c) {
-          bf16x8 ag = lds_read8(Gt + tswz(32 * c + t_row, pos));
-          bf16x8 aq = lds_read8(Qt + tswz(32 * c + t_row, pos));
-          if (!d_lane_ok) { ag = bf16x8{}; aq = bf16x8{}; }
-          dva[c] = mfma32(ag, pb[st], dva[c]);
-          dka[c] = mfma32(aq, dsb[st], dka[c]);
-        }
-      }
-    }
-    if constexpr (L::NBUF == 2) {
-      if (step + 1 < nsteps) store(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    } else {
-      __syncthreads();
-      if (step + 1 < nsteps) {
-        store(0);
-        __syncthreads();
-      }
-    }
-  }
-
-  // Pair reduction through LDS (the loop's last barrier freed it), then
-  // dK = s * (dK^T)^T, dV = (dV^T)^T; lane (key, hh) holds d = 32c + 8g + 4hh + u.
-  float* X = reinterpret_cast<float*>(smem);
-  bf16* DKg = static_cast<bf16*>(const_cast<void*>(p.dk.ptr)) + b * p.dk.sb + hk * p.dk.sh;
-  bf16* DVg = static_cast<bf16*>(const_cast<void*>(p.dv.ptr)) + b * p.dv.sb + hk * p.dv.sh;
-#pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    f32x16* acc = which == 0 ? dka : dva;
-    if (qhalf == 1) {
-#pragma unroll
-      for (int c = 0; c < NDB; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) X[((kblk * NDB + c) * 16 + i) * 64 + lane] = acc[c][i];
-    }
-    __syncthreads();
-    if (qhalf == 0) {
-#pragma unroll
-      for (int c = 0; c < NDB; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[c][i] += X[((kblk * NDB + c) * 16 + i) * 64 + lane];
-      if (key < p.Skv) {
-        const float sc = which == 0 ? p.scale : 1.0f;
-        if (key < p.mask.frozen) {   // a frozen key: written as exact zeros
-#pragma unroll
-          for (int c = 0; c < NDB; ++c) acc[c] = f32x16{};
-        }
-        bf16* dst_row = (which == 0 ? DKg + (int64_t)key * p.dk.ss : DVg + (int64_t)key * p.dv.ss);
-#pragma unroll
-        for (int c = 0; c < NDB; ++c)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d = 32 * c + 8 * g + 4 * hh;
-            if (d < D)
-              *reinterpret_cast<bf16x4*>(dst_row + d) =
-                  to_bf16x4(acc[c][4 * g] * sc, acc[c][4 * g + 1] * sc, acc[c][4 * g + 2] * sc,
-                            acc[c][4 * g + 3] * sc);
-          }
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dK/dV with asynchronous staging (D >= 32).  A workgroup owns 256 keys of
+// dK/dV with asynchronous staging.  A workgroup owns 256 keys of
 // one (batch, kv head) and one half of their (query tile, head) steps; wave
 // w owns keys 32w .. 32w+31 outright.  Its K rows stay in registers (the B
 // operand of S = Q K^T, natural orientation, a lane per key column); the
@@ -911,15 +414,18 @@ template <int D, int MK, bool SPLIT>
 __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
   using L = KvSplit<D>;
   constexpr int NW = L::NW, TKW = L::TKW, TQ = L::TQ;
-  constexpr int NJ = D / 16, NDB = D / 32;
+  // 32-wide d blocks of dK^T / dV^T; at D = 16 one block whose rows d >= 16
+  // hold nothing real (their operands read real columns again; never written)
+  constexpr int NJ = D / 16, NDB = D >= 32 ? D / 32 : 1;
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;         // rows per copy instruction
   constexpr int QINS = TQ / RPI;        // copy instructions per Q (or dO) tile
-  constexpr int QLPW = 2 * QINS / NW;   // per wave per step
+  // per copying wave per step (at D = 16 the 4 copies take 4 of the 8 waves)
+  constexpr int QLPW = 2 * QINS >= NW ? 2 * QINS / NW : 1;
   constexpr int VINS = TKW / RPI;       // copy instructions for the V rows
   constexpr int VLPW = VINS / NW;
   constexpr int ROW16 = 16 * 2 * D;     // bytes of 16 rows
-  static_assert(D >= 32 && QLPW * NW == 2 * QINS && QINS % QLPW == 0 && VLPW * NW == VINS &&
+  static_assert(D >= 16 && QLPW * NW >= 2 * QINS && QINS % QLPW == 0 && VLPW * NW == VINS &&
                 TKW == kDkdvKeys, "copy split");
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* const Vs = smem + 2 * L::STAGE;
@@ -1012,7 +518,9 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
 #pragma unroll
   for (int x = 0; x < QLPW; ++x) qvoff[x] = 2u * (unsigned)(((cidx0 % QINS + x) * RPI + crow) * (int)sss + schunk[x]);
   const unsigned lds_stage0 = lds_addr_of(smem) + (stage_g ? L::TILE : 0);
+  const bool copier = cidx0 < 2 * QINS;   // this wave issues copies
   auto stage_rows = [&](const StepPos& sp, int buf) __attribute__((always_inline)) {
+    if (!copier) return;
     const bf16* Sg = Sbase + (int64_t)(hk * p.G + sp.hs) * ssh + (int64_t)sp.q0 * sss;
     unsigned char* dst = smem + buf * L::STAGE + (stage_g ? L::TILE : 0);
     const bool whole = sp.q0 + TQ <= p.Sq;   // every row real: no per-lane select
@@ -1060,7 +568,9 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
 #pragma unroll
   for (int j = 0; j < NJ; ++j) roff[j] = swz_off<D>(l32, 16 * j + 8 * hh);
   const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // (at D = 16 the lanes that would address columns 16..31 address real
+  // columns instead; what they deliver lands in rows d >= 16 only)
+  const int tr_col = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) & (D >= 32 ? 31 : D - 1);
   int toff[2][NDB];
 #pragma unroll
   for (int c = 0; c < NDB; ++c) {
@@ -1190,6 +700,7 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = 32 * c + 8 * g + 4 * hh;
+          if (32 * c + 8 * g >= D) continue;   // rows d >= D of the block (D = 16)
           *reinterpret_cast<bf16x4*>(DK + d) = to_bf16x4(dka[c][4 * g] * sc, dka[c][4 * g + 1] * sc,
                                                          dka[c][4 * g + 2] * sc, dka[c][4 * g + 3] * sc);
           *reinterpret_cast<bf16x4*>(DV + d) = to_bf16x4(dva[c][4 * g], dva[c][4 * g + 1], dva[c][4 * g + 2],
@@ -1210,6 +721,7 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * c + 8 * g + 4 * hh;
+        if (32 * c + 8 * g >= D) continue;   // rows d >= D of the block (D = 16)
         *reinterpret_cast<f32x4*>(PK + d) = f32x4{dka[c][4 * g], dka[c][4 * g + 1], dka[c][4 * g + 2], dka[c][4 * g + 3]};
         *reinterpret_cast<f32x4*>(PV + d) = f32x4{dva[c][4 * g], dva[c][4 * g + 1], dva[c][4 * g + 2], dva[c][4 * g + 3]};
       }
@@ -1222,7 +734,7 @@ dkdv_split_kernel(Params p) {
   dkdv_split_body<D, MK, SPLIT>(p, blockIdx.x);
 }
 
-// The two gradient kernels in one launch (D >= 32, the 8-wave dQ): blocks
+// The two gradient kernels in one launch (the 8-wave dQ): blocks
 // [0, nkv) are dkdv_split_kernel's workgroups, blocks [nkv_pad, gridDim) the
 // dQ kernel's (nkv_pad is nkv rounded up to a multiple of 8, so the dQ blocks
 // keep their XCD placement; the blocks in between do nothing).  Each block
@@ -1335,17 +847,6 @@ hipError_t set_lds(K k, int bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int D, int QB, int NW>
-hipError_t launch_dq(const Params& p, hipStream_t stream) {
-  constexpr int TQ = NW * QB * 32;
-  const int64_t nblk = (int64_t)p.B * p.Hq * ((p.Sq + TQ - 1) / TQ);
-  auto k = dq_kernel<D, QB, NW>;
-  hipError_t e = set_lds(k, DqLds<D>::BYTES);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NW * 64), DqLds<D>::BYTES, stream, p);
-  return hipGetLastError();
-}
-
 // After the dK/dV products of the step-0 keys: the reduction of the two
 // halves' partial sums (split blocks) and, under TTT, the later steps' keys.
 template <int D>
@@ -1367,12 +868,12 @@ hipError_t launch_dkdv_rest(const Params& p, bool split, hipStream_t stream) {
 }
 
 // dK/dV and dQ as one grads_kernel launch, when both take 512-thread
-// workgroups (D >= 32 and enough query rows for the 8-wave dQ kernel) and both
-// have work; sets `done`.  Otherwise leaves `done` false and launches nothing.
+// workgroups (enough query rows for the 8-wave dQ kernel) and both have work;
+// sets `done`.  Otherwise leaves `done` false and launches nothing.
 template <int D>
 hipError_t launch_grads(const Params& p, hipStream_t stream, bool& done) {
   done = false;
-  if constexpr (D >= 32) {
+  {
     using LD = KvSplit<D>;
     const int nkeys = walk_keys(p);
     const int64_t ndq = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
@@ -1411,53 +912,36 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if constexpr (D >= 32) {
-    if (stage == STAGE_DKDV) {
-      using LD = KvSplit<D>;
-      const int nkeys = walk_keys(p);
-      const bool split = dkdv_split(p.B, p.Hkv, nkeys);
-      const int64_t nblk = (int64_t)p.B * p.Hkv * (split ? 2 : 1) * ((nkeys + LD::TKW - 1) / LD::TKW);
-      if (nblk > 0) {
-        const bool win = p.mask.kind == MASK_WINDOW;
-        auto k = split ? (win ? dkdv_split_kernel<D, MK_WIN, true> : dkdv_split_kernel<D, MK_FC, true>)
-                       : (win ? dkdv_split_kernel<D, MK_WIN, false> : dkdv_split_kernel<D, MK_FC, false>);
-        if ((e = set_lds(k, LD::BYTES)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(LD::NW * 64), LD::BYTES, stream, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_dkdv_rest<D>(p, split, stream)) != hipSuccess) return e;
-      } else if ((e = launch_dkdv_rest<D>(p, false, stream)) != hipSuccess) {
-        return e;
-      }
-    }
-  } else if (stage == STAGE_DKDV) {
-    constexpr int NKB = 4, TKW = NKB * 32;
-    const int64_t nblk = (int64_t)p.B * p.Hkv * ((p.Skv + TKW - 1) / TKW);
+  if (stage == STAGE_DKDV) {
+    using LD = KvSplit<D>;
+    const int nkeys = walk_keys(p);
+    const bool split = dkdv_split(p.B, p.Hkv, nkeys);
+    const int64_t nblk = (int64_t)p.B * p.Hkv * (split ? 2 : 1) * ((nkeys + LD::TKW - 1) / LD::TKW);
     if (nblk > 0) {
-      auto k = dkdv_kernel<D, NKB>;
-      constexpr int lds = KvLds<D, NKB>::BYTES;
-      if ((e = set_lds(k, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NKB * 2 * 64), lds, stream, p);
+      const bool win = p.mask.kind == MASK_WINDOW;
+      auto k = split ? (win ? dkdv_split_kernel<D, MK_WIN, true> : dkdv_split_kernel<D, MK_FC, true>)
+                     : (win ? dkdv_split_kernel<D, MK_WIN, false> : dkdv_split_kernel<D, MK_FC, false>);
+      if ((e = set_lds(k, LD::BYTES)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(LD::NW * 64), LD::BYTES, stream, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = launch_dkdv_rest<D>(p, split, stream)) != hipSuccess) return e;
+    } else if ((e = launch_dkdv_rest<D>(p, false, stream)) != hipSuccess) {
+      return e;
     }
   }
   if (stage == STAGE_DQ && p.B > 0 && p.Sq > 0) {
     // 8-wave workgroups when there are enough to fill the chip twice over
     const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
-    if constexpr (D >= 32) {
-      const int mk = mask_instance(p.mask.kind);
-      auto k = wg8 >= 512 ? (mk == MK_TTT ? dq_dma_kernel<D, 8, MK_TTT>
-                                          : (mk == MK_WIN ? dq_dma_kernel<D, 8, MK_WIN> : dq_dma_kernel<D, 8, MK_FC>))
-                          : (mk == MK_TTT ? dq_dma_kernel<D, 4, MK_TTT>
-                                          : (mk == MK_WIN ? dq_dma_kernel<D, 4, MK_WIN> : dq_dma_kernel<D, 4, MK_FC>));
-      const int nw = wg8 >= 512 ? 8 : 4;
-      const int64_t nblk = (int64_t)p.B * p.Hq * ((p.Sq + nw * 32 - 1) / (nw * 32));
-      if ((e = set_lds(k, DqDma<D>::BYTES)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(nw * 64), DqDma<D>::BYTES, stream, p);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    } else {
-      if ((e = wg8 >= 512 ? launch_dq<D, 1, 8>(p, stream) : launch_dq<D, 1, 4>(p, stream)) != hipSuccess)
-        return e;
-    }
+    const int mk = mask_instance(p.mask.kind);
+    auto k = wg8 >= 512 ? (mk == MK_TTT ? dq_dma_kernel<D, 8, MK_TTT>
+                                        : (mk == MK_WIN ? dq_dma_kernel<D, 8, MK_WIN> : dq_dma_kernel<D, 8, MK_FC>))
+                        : (mk == MK_TTT ? dq_dma_kernel<D, 4, MK_TTT>
+                                        : (mk == MK_WIN ? dq_dma_kernel<D, 4, MK_WIN> : dq_dma_kernel<D, 4, MK_FC>));
+    const int nw = wg8 >= 512 ? 8 : 4;
+    const int64_t nblk = (int64_t)p.B * p.Hq * ((p.Sq + nw * 32 - 1) / (nw * 32));
+    if ((e = set_lds(k, DqDma<D>::BYTES)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(nw * 64), DqDma<D>::BYTES, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }

@@ -80,9 +80,6 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 x, float c) {
   return c;
 }
 
-__device__ __forceinline__ bf16x8 lds_read8(const bf16* p) {
-  return *FA_LDS(const bf16x8, p);
-}
 __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
   i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(i16x4, p));
   return __builtin_bit_cast(bf16x4, t);
@@ -90,90 +87,12 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
 __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-__device__ __forceinline__ void lds_write16(bf16* p, i32x4 v) { *FA_LDS(i32x4, p) = v; }
-__device__ __forceinline__ void lds_write8(bf16* p, uint2 v) {
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  u32x2 w;
-  w[0] = v.x;
-  w[1] = v.y;
-  *FA_LDS(u32x2, p) = w;
-}
 
 // Four fp32 accumulator values -> 4 bf16 (round to nearest even).
 __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
   bf16x4 r;
   r[0] = (bf16)a; r[1] = (bf16)b; r[2] = (bf16)c; r[3] = (bf16)d;
   return r;
-}
-
-// --------------------------------------------------------------------------
-// Tile staging.  A 64-row tile of a row-major [rows][D] bf16 matrix is moved
-// into LDS in units of 4 rows x 8 columns: each thread loads 4 x 16 bytes and
-// writes a row-major copy and/or a transposed copy ([D][64]) in which, inside
-// every group of 16 rows, bits 2 and 3 of the row index are swapped.  That
-// order makes the 8 values one MFMA k-step needs (two runs of 4 in the 32x32
-// accumulator layout) contiguous, so the transposed operand is a single
-// 16-byte LDS read.
-//
-// The transposed copy is unpadded and XOR-swizzled (tswz): column pair
-// (2p, 2p+1) fills one 256-byte bank line, and the sixteen 16-byte slots of
-// that line are permuted by p mod 16.  Then the MFMA operand reads (16
-// consecutive columns, one 16-byte chunk each) and the 8-byte transposing
-// writes (32 lanes: 4 columns 8 apart x 8 row quads) both touch every bank
-// exactly once per 256 bytes.  The unit -> lane map keeps 16 consecutive
-// lanes on distinct bank slots for the row-major writes.
-
-constexpr int STAGE_ROWS = 64;
-
-// Element offset of (column d, stored row position pos) in a [D][64]
-// transposed tile.
-__device__ __forceinline__ int tswz(int d, int pos) {
-  return (d >> 1) * 128 + 8 * ((((d & 1) << 3) | (pos >> 3)) ^ ((d >> 1) & 15)) + (pos & 7);
-}
-
-__device__ __forceinline__ int tpos(int r) {
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
-template <int D>
-struct StageUnit {
-  static constexpr int COUNT = (STAGE_ROWS / 4) * (D / 8);
-  int rg, c8;  // rows 4*rg .. 4*rg+3, columns 8*c8 .. 8*c8+7
-  __device__ __forceinline__ explicit StageUnit(int u) {
-    const int lam = u & 63, hi = u >> 6;
-    if constexpr (D / 8 >= 4) {
-      rg = 4 * (lam >> 4) + ((lam >> 2) & 3);
-      c8 = (lam & 3) + 4 * hi;
-    } else {
-      rg = lam / (D / 8);
-      c8 = lam % (D / 8);
-    }
-  }
-};
-
-// Transposes a 4 x 8 bf16 block (4 rows of 8) into 8 columns of 4.
-__device__ __forceinline__ void transpose4x8(const i32x4 (&in)[4], uint2 (&out)[8]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const unsigned a0 = in[0][e], a1 = in[1][e], a2 = in[2][e], a3 = in[3][e];
-    out[2 * e].x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-    out[2 * e].y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-    out[2 * e + 1].x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-    out[2 * e + 1].y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-  }
-}
-
-__device__ __forceinline__ void store_rows4(bf16* X, int xstr, int rg, int c8, const i32x4 (&v)[4]) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) lds_write16(X + (4 * rg + r) * xstr + 8 * c8, v[r]);
-}
-
-__device__ __forceinline__ void store_trans4(bf16* Xt, int rg, int c8, const i32x4 (&v)[4]) {
-  uint2 t[8];
-  transpose4x8(v, t);
-  const int pos = tpos(4 * rg);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) lds_write8(Xt + tswz(8 * c8 + e, pos), t[e]);
 }
 
 // --------------------------------------------------------------------------

@@ -37,11 +37,11 @@ struct Params {
   const float* lse_in; // backward input
   float* delta;        // backward workspace: Delta [B, Hq, Sq]
   float* lse2;         // backward workspace: LSE * log2(e) [B, Hq, Sq]
-  float* dkv_part;     // backward workspace (bf16, D >= 32): two halves' float32
+  float* dkv_part;     // backward workspace (bf16): two halves' float32
                        // sums [2][dK^T, dV^T][B, Hkv, Skv, D]
 };
 
-// The bf16 dK/dV kernel (D >= 32) owns 256-key blocks.  With fewer than
+// The bf16 dK/dV kernel owns 256-key blocks.  With fewer than
 // 1024 blocks it splits each block's query steps between two workgroups
 // (so the causal triangle still balances over the chip), which then need
 // float32 partial sums in the workspace and a reduction; with more, every

@@ -204,7 +204,7 @@ fa_status fa_fwd_noalloc(const fa_fwd_args* args, hipStream_t stream);
  * (CS336 "Flash Attention (Triton)", How it works: only O and the
  * logsumexp are kept for the backward).  The bytes: two float32
  * [B, Hq, Sq] arrays (Delta, and LSE in log2 units), each rounded up to 256
- * bytes, and for FA_BF16 with D >= 32 the dK/dV kernel's float32 partial
+ * bytes, and for FA_BF16 the dK/dV kernel's float32 partial
  * sums, four [B, Hkv, Skv, D] arrays (two halves of each key block's query
  * steps, dK and dV; under FA_MASK_TTT only the Sq step-0 keys have them, so
  * Sq replaces Skv), rounded up to 256 bytes; linear in Sq and Skv, never

@@ -249,12 +249,13 @@ def test_workspace_is_linear_in_sequence_length():
     # under TTT only the Sq step-0 keys have partial sums
     ttt = bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=768, D=128, kind=_lib.FA_MASK_TTT)
     assert _lib.lib().fa_bwd_workspace_bytes(ttt) == 2 * 32 * 256 * 4 + 4 * 4 * 256 * 128 * 4
-    # bf16 at D = 32 and 64 holds the partial sums too; D = 16 and fp32 need none
+    # bf16 at every head dim holds the partial sums; fp32 needs none
     assert _lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=64)) == \
         2 * 32 * 256 * 4 + 4 * 4 * 256 * 64 * 4
     assert _lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=32)) == \
         2 * 32 * 256 * 4 + 4 * 4 * 256 * 32 * 4
-    assert _lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=16)) == 2 * 32 * 256 * 4
+    assert _lib.lib().fa_bwd_workspace_bytes(bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=16)) == \
+        2 * 32 * 256 * 4 + 4 * 4 * 256 * 16 * 4
     assert _lib.lib().fa_bwd_workspace_bytes(
         bwd_args(B=1, Hq=32, Hkv=4, Sq=256, Skv=256, D=128, dtype=_lib.FA_F32)) == 2 * 32 * 256 * 4
     sizes = [_lib.lib().fa_fwd_workspace_bytes(fwd_args(B=1, Hq=32, Hkv=4, Sq=s, Skv=s, D=128))

@@ -40,10 +40,10 @@ def test_bf16_gqa_causal(G):
     check_case(q, k, v, do, CAUSAL, "bf16", label=f"bf16 gqa G={G}")
 
 
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("G", [2, 3])
 def test_bf16_gqa_group_split(G, D):
-    # The D >= 32 dK/dV splits each key block's work between two workgroups: by
+    # The dK/dV kernel splits each key block's work between two workgroups: by
     # halves of the group's heads when G is even, by halves of the steps when odd
     q, k, v, do = inputs(2, 2 * G, 2, 300, 300, D, torch.bfloat16, seed=13 + G + D)
     check_case(q, k, v, do, CAUSAL, "bf16", label=f"bf16 gqa split G={G} D={D}")
@@ -213,7 +213,7 @@ STAGED = [
                                                for c in STAGED])
 def test_staged_backward_equals_fa_bwd(case):
     """fa_bwd_stage DELTA, DKDV, DQ in turn writes bitwise what fa_bwd writes
-    (at D >= 32 the dK/dV stage is the split kernel and its reduction; with
+    (the dK/dV stage is the split kernel and its reduction; with
     enough query rows fa_bwd launches the dK/dV and dQ workgroups together)."""
     import flash_attention_fa_amd as fa
     dtype, D, B, Hq, Hkv, L, kind = case
@@ -254,7 +254,7 @@ def test_bf16_many_workgroups(case):
     check_case(q, k, v, do, kind, "bf16", shift=shift, kv_valid=kvv, label=f"bf16 many-WG {name}")
 
 
-@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("D", [16, 32, 64])
 @pytest.mark.parametrize("case", MANY[:3], ids=[c[0] for c in MANY[:3]])
 def test_bf16_many_workgroups_small_head_dim(case, D):
     name, kind, Sq, Skv, shift, kvv = case
@@ -262,7 +262,7 @@ def test_bf16_many_workgroups_small_head_dim(case, D):
     check_case(q, k, v, do, kind, "bf16", shift=shift, kv_valid=kvv, label=f"bf16 many-WG {name} D={D}")
 
 
-# At least 1024 key blocks of 256 (B * Hkv * ceil(keys / 256)): the D >= 32
+# At least 1024 key blocks of 256 (B * Hkv * ceil(keys / 256)): the
 # dK/dV kernel then gives each block to one workgroup, which writes dK and dV
 # itself (no partial sums, no reduction).
 UNSPLIT = [
@@ -271,6 +271,8 @@ UNSPLIT = [
     ("gqa_full_kvvalid_d128", 8, 256, 128, 200, 256, 128, FULL, 0, (256, 255, 130, 1, 64, 200, 7, 99), None),
     ("ttt_d64", 8, 256, 128, 256, 512, 64, TTT, 0, None, None),
     ("window_d32", 16, 64, 64, 256, 256, 32, WINDOW, 2, None, (30, 10)),
+    ("causal_kvvalid_d16", 16, 64, 64, 256, 256, 16, CAUSAL, 1, (256, 255, 130, 1, 64, 200, 7, 99) * 2, None),
+    ("ttt_d16", 8, 256, 128, 256, 512, 16, TTT, 0, None, None),
 ]
 
 
