@@ -479,14 +479,23 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
   if (kbnd <= p.mask.frozen) qhi = qlo;   // every key frozen: no steps, zeros written
   const int t_first = qlo < qhi ? qlo / TQ : 0;
   const int t_last = qlo < qhi ? (qhi + TQ - 1) / TQ : 0;
-  // The block's (query tile, head) steps, tiles from the last down with the
-  // group's heads inside (so the workgroups sharing an XCD read the same
-  // tiles at about the same time).  With an even group each half takes half
-  // of the heads over every tile (each Q/dO tile is then read by one half
-  // only, on one XCD); with an odd one, half of the steps in that order.
-  // Without SPLIT the one workgroup takes them all.
+  // The block's (query tile, head) steps with the group's heads inside, so
+  // the workgroups sharing an XCD read the same tiles at about the same time.
+  // With an even group each half takes half of the heads over every tile
+  // (each Q/dO tile is then read by one half only, on one XCD); with an odd
+  // one, half of the steps in the downward order.  Without SPLIT the one
+  // workgroup takes them all.
+  // Direction.  Under the causal triangle block r has nkt - r tiles of steps
+  // and the blocks of an XCD start in rank order, so the compute unit that
+  // finishes block r (of the first nkt / 2) is the one that next takes
+  // about block nkt - 1 - r.  The first half of the ranks walk from the last
+  // tile down, the second half from their diagonal up: at any moment the
+  // workgroups of an XCD then read one of two tiles, and each Q/dO tile comes
+  // from HBM about twice in all, where a downward walk started at each
+  // workgroup's own time re-fetched it once per late starter.
   const int ntile = t_last - t_first;
   const bool by_head = SPLIT && (p.G & 1) == 0;
+  const bool up = (by_head || !SPLIT) && m.kind == MASK_CAUSAL && 2 * rank >= nkt;   // CAUSAL, TTT
   const int hbeg = by_head ? half * (p.G / 2) : 0;
   const int hend = by_head ? hbeg + p.G / 2 : p.G;
   const int nall = ntile * p.G;
@@ -508,8 +517,9 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
   struct StepPos {
     int hs, q0;   // head slot in the group, first query row of the tile
   };
+  const int qdir = up ? TQ : -TQ;
   auto advance = [&](StepPos& sp) __attribute__((always_inline)) {
-    if (++sp.hs == hend) { sp.hs = hbeg; sp.q0 -= TQ; }
+    if (++sp.hs == hend) { sp.hs = hbeg; sp.q0 += qdir; }
   };
   // Whole tiles (every row below Sq) with a non-negative row stride take the
   // scalar-base form: per-lane byte offsets computed once, no vector
@@ -553,7 +563,7 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
     float* Ls = reinterpret_cast<float*>(smem + buf * L::STAGE + 2 * L::TILE);
     if (tid < TQ) { Ls[tid] = lrow; Ls[TQ + tid] = drow; }
   };
-  StepPos cur{by_head ? hbeg : s0 % p.G, (t_last - 1 - (by_head ? 0 : s0 / p.G)) * TQ};
+  StepPos cur{by_head ? hbeg : s0 % p.G, (up ? t_first : t_last - 1 - (by_head ? 0 : s0 / p.G)) * TQ};
   StepPos nxt = cur;
   if (nsteps > 0) advance(nxt);
   if (nsteps > 0) {
