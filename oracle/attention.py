@@ -26,6 +26,13 @@ Sources, by page and section:
   self-attention and cross-attention.  The page does not define the window;
   WINDOW here is a band of key positions around the query position (see
   ``allowed``).
+* The playbook, section *3. Per-trainer porting checklist*: the fused ops
+  take an additive mask, added to the scores before the softmax and
+  broadcast where it has fewer dimensions.  ``bias`` here is its per-batch,
+  per-key form [B, Skv]: bias[b, j] is added to the scaled score of every
+  query row and head of batch entry b with key j, on top of the mask kind
+  (a key with bias -inf is dropped for that batch entry).  It is an input
+  only: the page's backward produces dQ, dK and dV, nothing for the mask.
 
 Readings taken where the pages are silent:
   * scale defaults to 1/sqrt(D);
@@ -36,7 +43,14 @@ Readings taken where the pages are silent:
   * WINDOW (left, right): key j allowed iff
     i - shift - left <= j <= i - shift + right (and j below kv_valid), so
     (left, 0) is a causal sliding window of left + 1 keys and (w, w) a
-    symmetric band.
+    symmetric band;
+  * the additive mask is taken in its per-(batch, key) form, which keeps the
+    path linear in S (a dense [Sq, Skv] mask is an S x S tensor in memory);
+    its values are real numbers or -inf (the page's F16 mask values are
+    among them); LSE includes it.
+
+With a bias the scores are  S = scale * Q K^T + bias[b]  (the bias row
+broadcast over query rows and heads); everything below uses those scores.
 
 The backward is the gradient of  L = sum(O * dO)  (dO is the upstream
 gradient), derived from the softmax Jacobian:
@@ -96,6 +110,15 @@ def _kv_valid_list(B, Skv, kv_valid):
     return [int(x) for x in np.asarray(kv_valid).reshape(-1)]
 
 
+def _bias_rows(B, Skv, bias):
+    """The per-batch key bias as a float64 [B, Skv] array (zeros if None)."""
+    if bias is None:
+        return np.zeros((B, Skv))
+    b = np.asarray(bias, dtype=np.float64)
+    assert b.shape == (B, Skv), f"bias must be [B, Skv], got {b.shape}"
+    return b
+
+
 def _check_shapes(q, k, v):
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Skv, Dk = k.shape
@@ -127,7 +150,7 @@ def _row_blocks(Sq, rows):
 
 
 def attention_forward(q, k, v, kind=FULL, shift=0, kv_valid=None, scale=None,
-                      heads=None, rows=None, window=None):
+                      heads=None, rows=None, window=None, bias=None):
     """O [B,Hq,Sq,D] and LSE [B,Hq,Sq] in float64.
 
     ``heads`` (a list of query heads) and ``rows`` (a half-open range
@@ -140,6 +163,7 @@ def attention_forward(q, k, v, kind=FULL, shift=0, kv_valid=None, scale=None,
     G = Hq // Hkv
     s = 1.0 / np.sqrt(D) if scale is None or scale <= 0 else float(scale)
     kvv = _kv_valid_list(B, Skv, kv_valid)
+    bias = _bias_rows(B, Skv, bias)
     hs = range(Hq) if heads is None else heads
     O = np.full(q.shape, np.nan)
     LSE = np.full((B, Hq, Sq), np.nan)
@@ -148,7 +172,7 @@ def attention_forward(q, k, v, kind=FULL, shift=0, kv_valid=None, scale=None,
             A = allowed(kind, Sq, Skv, shift, kvv[b], rb, window)
             for h in hs:
                 g = h // G
-                S = s * (q[b, h, rb] @ k[b, g].T)
+                S = s * (q[b, h, rb] @ k[b, g].T) + bias[b][None, :]
                 P, lse = _row_softmax(np.where(A, S, -np.inf))
                 O[b, h, rb] = P @ v[b, g]
                 LSE[b, h, rb] = lse
@@ -156,7 +180,7 @@ def attention_forward(q, k, v, kind=FULL, shift=0, kv_valid=None, scale=None,
 
 
 def attention_backward(q, k, v, do, kind=FULL, shift=0, kv_valid=None,
-                       scale=None, heads=None, rows=None, window=None):
+                       scale=None, heads=None, rows=None, window=None, bias=None):
     """dQ, dK, dV (float64) of L = sum(O * dO), plus Delta [B,Hq,Sq].
 
     P is rebuilt from the scores, exactly as the definition states; dK and dV
@@ -169,6 +193,7 @@ def attention_backward(q, k, v, do, kind=FULL, shift=0, kv_valid=None,
     G = Hq // Hkv
     s = 1.0 / np.sqrt(D) if scale is None or scale <= 0 else float(scale)
     kvv = _kv_valid_list(B, Skv, kv_valid)
+    bias = _bias_rows(B, Skv, bias)
     hs = range(Hq) if heads is None else heads
     dQ = np.full(q.shape, np.nan)
     dK = np.zeros(k.shape)
@@ -179,7 +204,7 @@ def attention_backward(q, k, v, do, kind=FULL, shift=0, kv_valid=None,
             A = allowed(kind, Sq, Skv, shift, kvv[b], rb, window)
             for h in hs:
                 g = h // G
-                S = s * (q[b, h, rb] @ k[b, g].T)
+                S = s * (q[b, h, rb] @ k[b, g].T) + bias[b][None, :]
                 P, _ = _row_softmax(np.where(A, S, -np.inf))
                 dO = do[b, h, rb]
                 dV[b, g] += P.T @ dO
@@ -193,7 +218,7 @@ def attention_backward(q, k, v, do, kind=FULL, shift=0, kv_valid=None,
 
 
 def attention_key_grads(q, k, v, do, keys, kind=FULL, shift=0, kv_valid=None, scale=None,
-                        window=None):
+                        window=None, bias=None):
     """dK, dV (float64) of the keys [keys[0], keys[1]) only, over every query
     row and every head of each group: [B, Hkv, k1 - k0, D] each.
 
@@ -216,6 +241,7 @@ def attention_key_grads(q, k, v, do, keys, kind=FULL, shift=0, kv_valid=None, sc
     G = Hq // Hkv
     s = 1.0 / np.sqrt(D) if scale is None or scale <= 0 else float(scale)
     kvv = _kv_valid_list(B, Skv, kv_valid)
+    bias = _bias_rows(B, Skv, bias)
     k0, k1 = int(keys[0]), int(keys[1])
     dK = np.zeros((B, Hkv, k1 - k0, D))
     dV = np.zeros((B, Hkv, k1 - k0, D))
@@ -231,11 +257,12 @@ def attention_key_grads(q, k, v, do, keys, kind=FULL, shift=0, kv_valid=None, sc
         for g in range(Hkv):
             heads = list(range(g * G, (g + 1) * G))
             O, LSE = attention_forward(q[b:b + 1], k[b:b + 1], v[b:b + 1], kind, shift,
-                                       [kvv[b]], s, heads=heads, rows=(lo, hi), window=window)
+                                       [kvv[b]], s, heads=heads, rows=(lo, hi), window=window,
+                                       bias=bias[b:b + 1])
             for rb in _row_blocks(Sq, (lo, hi)):
                 A = allowed(kind, Sq, Skv, shift, kvv[b], rb, window)[:, k0:k1]
                 for h in heads:
-                    S = s * (q[b, h, rb] @ k[b, g, k0:k1].T)
+                    S = s * (q[b, h, rb] @ k[b, g, k0:k1].T) + bias[b, k0:k1][None, :]
                     P = np.where(A, np.exp(np.where(A, S, 0.0) - LSE[0, h, rb][:, None]), 0.0)
                     dO = do[b, h, rb]
                     dP = dO @ v[b, g, k0:k1].T
@@ -247,9 +274,9 @@ def attention_key_grads(q, k, v, do, keys, kind=FULL, shift=0, kv_valid=None, sc
 
 
 def attention_ref(q, k, v, do, kind=FULL, shift=0, kv_valid=None, scale=None,
-                  heads=None, rows=None, window=None):
+                  heads=None, rows=None, window=None, bias=None):
     """Forward and backward together: dict with O, LSE, dQ, dK, dV, Delta."""
-    O, LSE = attention_forward(q, k, v, kind, shift, kv_valid, scale, heads, rows, window)
+    O, LSE = attention_forward(q, k, v, kind, shift, kv_valid, scale, heads, rows, window, bias)
     dQ, dK, dV, Delta = attention_backward(q, k, v, do, kind, shift, kv_valid,
-                                           scale, heads, rows, window)
+                                           scale, heads, rows, window, bias)
     return dict(O=O, LSE=LSE, dQ=dQ, dK=dK, dV=dV, Delta=Delta)

@@ -477,3 +477,104 @@ def test_key_grads_match_torch_sdpa_autograd(kind, Sq, Skv, shift, kvv, win, key
         assert np.abs(gk).max() > 1e-3 and np.abs(gv).max() > 1e-3
         np.testing.assert_allclose(dK[b], gk, atol=1e-11, err_msg=f"dK b={b}")
         np.testing.assert_allclose(dV[b], gv, atol=1e-11, err_msg=f"dV b={b}")
+
+
+# --------------------------------------------------------------------------
+# The per-batch key bias (the additive mask of the playbook's "3. Per-trainer
+# porting checklist", in its [B, Skv] form): bias[b, j] is added to the
+# scaled score of every row and head of batch entry b with key j.
+
+def _bias(B, Skv, seed, neg_inf_frac=0.15):
+    """Finite biases in [-3, 3] with some -inf entries (never a whole row)."""
+    g = np.random.default_rng(seed)
+    b = g.uniform(-3.0, 3.0, (B, Skv))
+    drop = g.uniform(size=(B, Skv)) < neg_inf_frac
+    drop[:, 0] = False
+    b[drop] = -np.inf
+    return b
+
+
+@pytest.mark.parametrize("kind,Sq,Skv,shift,win", [
+    (FULL, 18, 23, 0, None),
+    (CAUSAL, 20, 20, 0, None),
+    (CAUSAL, 16, 26, -10, None),
+    (WINDOW, 22, 22, 1, (4, 2)),
+])
+def test_bias_neg_inf_tail_equals_kv_valid(kind, Sq, Skv, shift, win):
+    # a bias that is 0 on keys below n and -inf from n on is the padding
+    # mask kv_valid = n: the same allowed pairs with the same scores, so every
+    # output is bitwise the same
+    B, Hq, Hkv, D = 2, 4, 2, 8
+    q, k, v = _rand((B, Hq, Sq, D), 120), _rand((B, Hkv, Skv, D), 121), _rand((B, Hkv, Skv, D), 122)
+    do = _rand((B, Hq, Sq, D), 123)
+    kvv = (Skv - 5, 7)
+    bias = np.zeros((B, Skv))
+    for b in range(B):
+        bias[b, kvv[b]:] = -np.inf
+    a = attention_ref(q, k, v, do, kind, shift, kvv, window=win)
+    c = attention_ref(q, k, v, do, kind, shift, None, window=win, bias=bias)
+    for name in ("O", "LSE", "dQ", "dK", "dV", "Delta"):
+        np.testing.assert_array_equal(a[name], c[name], err_msg=name)
+
+
+@pytest.mark.parametrize("kind", [FULL, CAUSAL, TTT])
+def test_bias_constant_shifts_lse_only(kind):
+    # softmax is unchanged by adding one constant to a row's scores: O and the
+    # gradients stay, LSE moves by the constant
+    B, Hq, Hkv, Sq, D = 2, 4, 2, 12, 8
+    Skv = 3 * Sq if kind == TTT else Sq
+    q, k, v = _rand((B, Hq, Sq, D), 130), _rand((B, Hkv, Skv, D), 131), _rand((B, Hkv, Skv, D), 132)
+    do = _rand((B, Hq, Sq, D), 133)
+    c = np.array([[2.5] * Skv, [-7.25] * Skv])
+    a = attention_ref(q, k, v, do, kind)
+    r = attention_ref(q, k, v, do, kind, bias=c)
+    for name in ("O", "dQ", "dK", "dV", "Delta"):
+        np.testing.assert_allclose(r[name], a[name], atol=1e-12, err_msg=name)
+    np.testing.assert_allclose(r["LSE"], a["LSE"] + c[:, 0][:, None, None], atol=1e-12)
+
+
+@pytest.mark.parametrize("kind,Sq,Skv,shift,win", [
+    (FULL, 17, 29, 0, None),
+    (CAUSAL, 24, 24, 0, None),
+    (CAUSAL, 20, 30, -10, None),
+    (TTT, 12, 36, 0, None),
+    (WINDOW, 22, 22, 1, (4, 2)),
+])
+def test_bias_matches_torch_sdpa_float_mask(kind, Sq, Skv, shift, win):
+    # torch's SDPA with a float attn_mask (the bias where the kind allows the
+    # pair, -inf elsewhere) against the oracle: O, and dQ, dK, dV by autograd
+    B, Hq, Hkv, D = 2, 4, 2, 8
+    q, k, v = _rand((B, Hq, Sq, D), 140), _rand((B, Hkv, Skv, D), 141), _rand((B, Hkv, Skv, D), 142)
+    do = _rand((B, Hq, Sq, D), 143)
+    bias = _bias(B, Skv, 144)
+    r = attention_ref(q, k, v, do, kind, shift, None, window=win, bias=bias)
+    for b in range(B):
+        allow = _torch_mask(kind, Sq, Skv, shift, Skv if kind != TTT else Sq, win)
+        fmask = torch.where(allow, torch.tensor(bias[b])[None, :].expand(Sq, Skv),
+                            torch.tensor(-np.inf, dtype=torch.float64))
+        rows = torch.isfinite(fmask).any(1)   # SDPA gives NaN on rows with no key
+        tq, tk, tv = (torch.tensor(x[b:b + 1], requires_grad=True) for x in (q, k, v))
+        out = torch.nn.functional.scaled_dot_product_attention(
+            tq[:, :, rows], tk, tv, attn_mask=fmask[rows], enable_gqa=True)
+        out.backward(torch.tensor(do[b:b + 1][:, :, rows.numpy()]))
+        np.testing.assert_allclose(r["O"][b][:, rows.numpy()], out.detach().numpy()[0], atol=1e-12)
+        assert np.all(r["O"][b][:, ~rows.numpy()] == 0) and np.all(r["LSE"][b][:, ~rows.numpy()] == 0)
+        np.testing.assert_allclose(r["dQ"][b], tq.grad.numpy()[0], atol=1e-11, err_msg="dQ")
+        np.testing.assert_allclose(r["dK"][b], tk.grad.numpy()[0], atol=1e-11, err_msg="dK")
+        np.testing.assert_allclose(r["dV"][b], tv.grad.numpy()[0], atol=1e-11, err_msg="dV")
+        # LSE: the natural logsumexp of the biased scores over allowed keys
+        S = (q[b] @ np.repeat(k[b], Hq // Hkv, 0).transpose(0, 2, 1)) / np.sqrt(D)
+        L = torch.logsumexp(torch.tensor(S) + fmask[None], dim=-1).numpy()
+        np.testing.assert_allclose(r["LSE"][b][:, rows.numpy()], L[:, rows.numpy()], atol=1e-12)
+
+
+def test_bias_key_grads_match_full_backward():
+    from oracle import attention_key_grads
+    B, Hq, Hkv, Sq, Skv, D = 2, 4, 2, 20, 20, 8
+    q, k, v = _rand((B, Hq, Sq, D), 150), _rand((B, Hkv, Skv, D), 151), _rand((B, Hkv, Skv, D), 152)
+    do = _rand((B, Hq, Sq, D), 153)
+    bias = _bias(B, Skv, 154)
+    r = attention_ref(q, k, v, do, CAUSAL, bias=bias)
+    dK, dV = attention_key_grads(q, k, v, do, (4, 15), CAUSAL, bias=bias)
+    np.testing.assert_allclose(dK, r["dK"][:, :, 4:15], atol=1e-12)
+    np.testing.assert_allclose(dV, r["dV"][:, :, 4:15], atol=1e-12)
