@@ -22,7 +22,10 @@ Mask kinds: ``FULL``, ``CAUSAL`` (key j <= query i - causal_shift),
 plus the key at the query's own position in each later step) and ``WINDOW``
 (``window=(left, right)``: i - causal_shift - left <= j <= i - causal_shift +
 right).  ``kv_valid`` is an optional int32 device tensor [B] of valid key
-counts.
+counts.  ``key_bias`` is an optional float32 device tensor [B, Skv] (unit key
+stride; a stride of 0 over B shares one row) added to the scaled scores of
+every query row and head: an additive mask in per-key form, -inf drops a key.
+It receives no gradient.
 """
 import torch
 
@@ -54,8 +57,18 @@ def _tensor(t):
     return _lib.fa_tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
-def _mask(kind, causal_shift, kv_valid, window=None, frozen_keys=0):
+def _mask(kind, causal_shift, kv_valid, window=None, frozen_keys=0, key_bias=None, shape=None):
     ptr = None
+    bias_ptr, bias_sb = None, 0
+    if key_bias is not None:
+        if key_bias.dtype != torch.float32 or key_bias.dim() != 2:
+            raise FAError(_lib.FA_ERR_INVALID_ARG, "key_bias must be a 2-d float32 tensor [B, Skv]")
+        if shape is not None and tuple(key_bias.shape) != shape:
+            raise FAError(_lib.FA_ERR_INVALID_ARG, f"key_bias has shape {tuple(key_bias.shape)}, expected {shape}")
+        if key_bias.shape[1] > 1 and key_bias.stride(1) != 1:
+            raise FAError(_lib.FA_ERR_INVALID_ARG, "key_bias needs unit stride over keys")
+        bias_ptr = key_bias.data_ptr()
+        bias_sb = key_bias.stride(0) if key_bias.shape[0] > 1 else 0
     if kv_valid is not None:
         if kv_valid.dtype != torch.int32 or not kv_valid.is_contiguous():
             raise FAError(_lib.FA_ERR_INVALID_ARG, "kv_valid must be a contiguous int32 tensor")
@@ -63,7 +76,12 @@ def _mask(kind, causal_shift, kv_valid, window=None, frozen_keys=0):
     if int(kind) == WINDOW and window is None:
         raise FAError(_lib.FA_ERR_INVALID_ARG, "mask_kind WINDOW needs window=(left, right)")
     left, right = (0, 0) if window is None else (int(window[0]), int(window[1]))
-    return _lib.fa_mask_desc(int(kind), int(causal_shift), ptr, left, right, int(frozen_keys))
+    return _lib.fa_mask_desc(int(kind), int(causal_shift), ptr, left, right, int(frozen_keys),
+                             bias_ptr, int(bias_sb))
+
+
+def _bias_shape(q, k):
+    return (int(q.shape[0]), int(k.shape[2]))
 
 
 def _stream(t, stream):
@@ -104,13 +122,16 @@ def _fwd_shape_args(q, k):
     return a
 
 
-def fa_fwd_workspace_bytes(q, k):
-    """Scratch bytes fa_fwd needs for these shapes (bf16: a transposed V, linear in Skv)."""
-    return int(_lib.lib().fa_fwd_workspace_bytes(_fwd_shape_args(q, k)))
+def fa_fwd_workspace_bytes(q, k, *, key_bias=None):
+    """Scratch bytes fa_fwd needs for these shapes (bf16: a transposed V, and
+    with a key bias a scaled copy of it; linear in Skv)."""
+    a = _fwd_shape_args(q, k)
+    a.mask = _mask(FULL, 0, None, None, 0, key_bias, _bias_shape(q, k))
+    return int(_lib.lib().fa_fwd_workspace_bytes(a))
 
 
 def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=None, scale=None,
-           out=None, lse=None, workspace=None, stream=None, frozen_keys=0):
+           out=None, lse=None, workspace=None, stream=None, frozen_keys=0, key_bias=None):
     """Forward attention.  Returns (O [B,Hq,Sq,D] in q's dtype, LSE [B,Hq,Sq] fp32).
 
     ``workspace`` (uint8 device tensor of at least ``fa_fwd_workspace_bytes``
@@ -124,7 +145,7 @@ def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=Non
     a.scale = 0.0 if scale is None else float(scale)
     a.q, a.k, a.v, a.o = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
     a.lse = lse.data_ptr()
-    a.mask = _mask(mask_kind, causal_shift, kv_valid, window, frozen_keys)
+    a.mask = _mask(mask_kind, causal_shift, kv_valid, window, frozen_keys, key_bias, _bias_shape(q, k))
     for t in (k, v, out):
         if t.dtype != q.dtype:
             raise FAError(_lib.FA_ERR_INVALID_ARG, "q, k, v and out must share one dtype")
@@ -137,7 +158,7 @@ def fa_fwd(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=Non
 
 
 def fa_fwd_noalloc(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=None, scale=None,
-                   out=None, lse=None, stream=None, frozen_keys=0):
+                   out=None, lse=None, stream=None, frozen_keys=0, key_bias=None):
     """fa_fwd without a workspace argument: the library's static device
     scratch holds the transposed V (for callers that cannot allocate, e.g.
     under graph capture; pass ``out`` and ``lse`` there, since allocating
@@ -152,7 +173,7 @@ def fa_fwd_noalloc(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, wi
     a.scale = 0.0 if scale is None else float(scale)
     a.q, a.k, a.v, a.o = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
     a.lse = lse.data_ptr()
-    a.mask = _mask(mask_kind, causal_shift, kv_valid, window, frozen_keys)
+    a.mask = _mask(mask_kind, causal_shift, kv_valid, window, frozen_keys, key_bias, _bias_shape(q, k))
     for t in (k, v, out):
         if t.dtype != q.dtype:
             raise FAError(_lib.FA_ERR_INVALID_ARG, "q, k, v and out must share one dtype")
@@ -161,7 +182,7 @@ def fa_fwd_noalloc(q, k, v, *, mask_kind=FULL, causal_shift=0, kv_valid=None, wi
 
 
 def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window=None,
-              frozen_keys=0):
+              frozen_keys=0, key_bias=None):
     B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
     a = _lib.fa_bwd_args()
     a.dtype = _dtype_code(q)
@@ -171,22 +192,22 @@ def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_val
     a.lse = None if lse is None else lse.data_ptr()
     if dq is not None:
         a.dq, a.dk, a.dv = _tensor(dq), _tensor(dk), _tensor(dv)
-    a.mask = _mask(mask_kind, causal_shift, kv_valid, window, frozen_keys)
+    a.mask = _mask(mask_kind, causal_shift, kv_valid, window, frozen_keys, key_bias, _bias_shape(q, k))
     return a
 
 
-def fa_bwd_workspace_bytes(q, k, *, mask_kind=FULL):
-    """Scratch bytes fa_bwd needs for these shapes (linear in Sq)."""
+def fa_bwd_workspace_bytes(q, k, *, mask_kind=FULL, key_bias=None):
+    """Scratch bytes fa_bwd needs for these shapes (linear in Sq and Skv)."""
     a = _lib.fa_bwd_args()
     B, Hq, Hkv, Sq, Skv, D = _shape(q, k)
     a.dtype = _dtype_code(q)
     a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
-    a.mask = _lib.fa_mask_desc(int(mask_kind), 0, None, 0, 0, 0)
+    a.mask = _mask(mask_kind, 0, None, (0, 0), 0, key_bias, _bias_shape(q, k))
     return int(_lib.lib().fa_bwd_workspace_bytes(a))
 
 
 def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=None, window=None,
-           scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None, frozen_keys=0):
+           scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None, frozen_keys=0, key_bias=None):
     """Backward attention.  Returns (dQ, dK, dV) in q's dtype."""
     if dq is None:
         dq = torch.empty_like(q, memory_format=torch.contiguous_format)
@@ -195,7 +216,7 @@ def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=No
     if dv is None:
         dv = torch.empty_like(v, memory_format=torch.contiguous_format)
     a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window,
-                  frozen_keys)
+                  frozen_keys, key_bias)
     need = int(_lib.lib().fa_bwd_workspace_bytes(a))
     if workspace is None:
         workspace = _scratch(need, q.device, stream)
@@ -206,14 +227,15 @@ def fa_bwd(q, k, v, o, lse, dout, *, mask_kind=FULL, causal_shift=0, kv_valid=No
 
 
 def fa_bwd_stage(stage, q, k, v, o, lse, dout, dq, dk, dv, workspace, *, mask_kind=FULL,
-                 causal_shift=0, kv_valid=None, window=None, scale=None, stream=None, frozen_keys=0):
+                 causal_shift=0, kv_valid=None, window=None, scale=None, stream=None, frozen_keys=0,
+                 key_bias=None):
     """One stage (FA_BWD_DELTA, FA_BWD_DKDV or FA_BWD_DQ) of ``fa_bwd``.
 
     The caller provides the outputs and the workspace; DKDV and DQ read the
-    Delta that a DELTA stage left in ``workspace``.
+    Delta (and scaled key bias) that a DELTA stage left in ``workspace``.
     """
     a = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, mask_kind, causal_shift, kv_valid, scale, window,
-                  frozen_keys)
+                  frozen_keys, key_bias)
     _lib.check(_lib.lib().fa_bwd_stage(a, int(stage), workspace.data_ptr(),
                                        workspace.numel() * workspace.element_size(),
                                        _stream(q, stream)))
@@ -225,34 +247,37 @@ def fa_last_error():
 
 class _Attention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, mask_kind, causal_shift, kv_valid, scale, window, frozen_keys):
+    def forward(ctx, q, k, v, mask_kind, causal_shift, kv_valid, scale, window, frozen_keys, key_bias):
         o, lse = fa_fwd(q, k, v, mask_kind=mask_kind, causal_shift=causal_shift,
-                        kv_valid=kv_valid, window=window, scale=scale)
+                        kv_valid=kv_valid, window=window, scale=scale, key_bias=key_bias)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.cfg = (mask_kind, causal_shift, kv_valid, scale, window, frozen_keys)
+        ctx.cfg = (mask_kind, causal_shift, kv_valid, scale, window, frozen_keys, key_bias)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        mask_kind, causal_shift, kv_valid, scale, window, frozen_keys = ctx.cfg
+        mask_kind, causal_shift, kv_valid, scale, window, frozen_keys, key_bias = ctx.cfg
         if do.stride(-1) != 1:
             do = do.contiguous()
         dq, dk, dv = fa_bwd(q, k, v, o, lse, do, mask_kind=mask_kind, causal_shift=causal_shift,
-                            kv_valid=kv_valid, window=window, scale=scale, frozen_keys=frozen_keys)
-        return dq, dk, dv, None, None, None, None, None, None
+                            kv_valid=kv_valid, window=window, scale=scale, frozen_keys=frozen_keys,
+                            key_bias=key_bias)
+        return dq, dk, dv, None, None, None, None, None, None, None
 
 
 def attention(q, k, v, mask_kind=FULL, causal_shift=0, kv_valid=None, scale=None, window=None,
-              frozen_keys=0):
+              frozen_keys=0, key_bias=None):
     """Fused attention O = softmax(scale q k^T + mask) v, differentiable.
 
     ``scale`` defaults to 1/sqrt(D); ``window`` = (left, right) for WINDOW.
     A negative ``causal_shift`` -P with CAUSAL shows every query a P-key
     prefix; ``frozen_keys`` = P then leaves the prefix's dK, dV at zero
-    without computing them.  Saves only O and LSE for the backward.
+    without computing them.  ``key_bias`` [B, Skv] (float32) is added to the
+    scaled scores; it gets no gradient.  Saves only O and LSE for the backward.
     """
-    return _Attention.apply(q, k, v, mask_kind, causal_shift, kv_valid, scale, window, frozen_keys)
+    return _Attention.apply(q, k, v, mask_kind, causal_shift, kv_valid, scale, window, frozen_keys,
+                            key_bias)
 
 
 # ---- soft-target log-softmax loss (fa_lsm_loss_fwd / fa_lsm_loss_bwd) -------

@@ -44,7 +44,8 @@ class fa_tensor(ctypes.Structure):
 class fa_mask_desc(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("causal_shift", ctypes.c_int32),
                 ("kv_valid", ctypes.c_void_p), ("window_left", ctypes.c_int32),
-                ("window_right", ctypes.c_int32), ("frozen_keys", ctypes.c_int32)]
+                ("window_right", ctypes.c_int32), ("frozen_keys", ctypes.c_int32),
+                ("key_bias", ctypes.c_void_p), ("key_bias_stride_b", ctypes.c_int64)]
 
 
 _SHAPE = [("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("Hq", ctypes.c_int32),

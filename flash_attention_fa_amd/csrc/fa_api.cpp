@@ -82,6 +82,14 @@ fa_status check_shape(const Shape& s, const fa_mask_desc& m) {
     return fail(FA_ERR_INVALID_ARG, "negative causal_shift %d with the TTT mask", m.causal_shift);
   if (m.frozen_keys < 0)
     return fail(FA_ERR_INVALID_ARG, "negative frozen_keys %d", m.frozen_keys);
+  if (m.key_bias && s.B > 0 && s.Skv > 0) {
+    if (reinterpret_cast<uintptr_t>(m.key_bias) % 4 != 0)
+      return fail(FA_ERR_ALIGNMENT, "key_bias: pointer is not 4-byte aligned");
+    if (m.key_bias_stride_b < 0)
+      return fail(FA_ERR_INVALID_ARG, "key_bias_stride_b %lld is negative", (long long)m.key_bias_stride_b);
+    if (m.key_bias_stride_b > (int64_t(1) << 40))
+      return fail(FA_ERR_UNSUPPORTED, "key_bias_stride_b %lld is too large", (long long)m.key_bias_stride_b);
+  }
   if (m.kind == FA_MASK_TTT) {
     if (s.Sq <= 0 && s.Skv != 0)
       return fail(FA_ERR_INVALID_ARG, "TTT mask needs Sq > 0 (Sq is the step length)");
@@ -153,6 +161,15 @@ void fill_common(fa::Params& p, const Shape& s, float scale, const fa_mask_desc&
   p.mask.wl = m.kind == FA_MASK_WINDOW ? m.window_left : 0;
   p.mask.wr = m.kind == FA_MASK_WINDOW ? m.window_right : 0;
   p.mask.frozen = m.frozen_keys;
+  p.mask.bias = s.B > 0 && s.Skv > 0 ? m.key_bias : nullptr;
+  p.mask.bias_sb = m.key_bias_stride_b;
+}
+
+// The bytes the key bias spans (empty without one).
+Range bias_span(const Shape& s, const fa_mask_desc& m) {
+  if (!m.key_bias || s.B <= 0 || s.Skv <= 0) return Range{0, 0, true};
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(m.key_bias);
+  return Range{lo, lo + ((uintptr_t)(s.B - 1) * (uintptr_t)m.key_bias_stride_b + (uintptr_t)s.Skv) * 4, false};
 }
 
 // One float32 [B, Hq, Sq] array, rounded up to 256 bytes.
@@ -174,20 +191,35 @@ size_t part_bytes(const Shape& s, int kind) {
   return (n + 255) / 256 * 256;
 }
 
-// Backward workspace: Delta, then LSE * log2(e) (both [B, Hq, Sq] float32),
-// then the dK/dV partial sums.
-size_t delta_bytes(const Shape& s, int kind) { return 2 * row_array_bytes(s) + part_bytes(s, kind); }
-
-// Forward workspace (bf16 only): V^T, bfloat16 [B, Hkv, D, vt_keys(s)].
+// Keys per row of the forward's V^T and of the scaled key-bias copy: Skv
+// rounded up to a whole key tile.
 int64_t vt_keys(const Shape& s) {
   return ((int64_t)std::max(s.Skv, 0) + fa::kVtTile - 1) / fa::kVtTile * fa::kVtTile;
 }
-size_t fwd_ws_bytes(const Shape& s) {
+
+// The key bias divided by the scale (bf16 kernels, with a key bias):
+// float32 [B, vt_keys(s)], rounded up to 256 bytes.
+size_t bias_copy_bytes(const Shape& s, const fa_mask_desc& m) {
+  if (s.dtype != FA_BF16 || !m.key_bias || s.B <= 0 || s.Skv <= 0) return 0;
+  size_t n = (size_t)s.B * (size_t)vt_keys(s) * 4;
+  return (n + 255) / 256 * 256;
+}
+
+// Backward workspace: Delta, then LSE * log2(e) (both [B, Hq, Sq] float32),
+// then the dK/dV partial sums, then the scaled key bias.
+size_t delta_bytes(const Shape& s, const fa_mask_desc& m) {
+  return 2 * row_array_bytes(s) + part_bytes(s, m.kind) + bias_copy_bytes(s, m);
+}
+
+// Forward workspace (bf16 only): V^T, bfloat16 [B, Hkv, D, vt_keys(s)], then
+// the scaled key bias.
+size_t vt_bytes(const Shape& s) {
   if (s.dtype != FA_BF16) return 0;
   size_t n = (size_t)std::max(s.B, 0) * (size_t)std::max(s.Hkv, 0) * (size_t)std::max(s.D, 0) *
              (size_t)vt_keys(s) * 2;
   return (n + 255) / 256 * 256;
 }
+size_t fwd_ws_bytes(const Shape& s, const fa_mask_desc& m) { return vt_bytes(s) + bias_copy_bytes(s, m); }
 
 // A caller workspace of `need` bytes: present, large enough, 256-byte aligned.
 fa_status check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -255,11 +287,12 @@ fa_status fwd_run(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t s
            reinterpret_cast<uintptr_t>(a->lse) + (size_t)s.B * s.Hq * s.Sq * 4, !rows};
   if (s.dtype == FA_BF16 && vt_keys(s) >= (int64_t(1) << 24))
     return fail(FA_ERR_UNSUPPORTED, "Skv=%d is too large (limit 2^24 - 64)", s.Skv);
-  const size_t need = fwd_ws_bytes(s);
+  const size_t need = fwd_ws_bytes(s, a->mask);
   if (static_ws) {
     if (need > ws_bytes)
       return fail(FA_ERR_UNSUPPORTED,
-                  "fa_fwd_noalloc: these shapes need %zu bytes of scratch (B*Hkv*D*Skv rounded up, bf16); "
+                  "fa_fwd_noalloc: these shapes need %zu bytes of scratch (B*Hkv*D*Skv rounded up, bf16, "
+                  "plus B*Skv floats with a key bias); "
                   "its static scratch holds %zu; call fa_fwd with a workspace instead", need, ws_bytes);
   } else if ((st = check_ws(ws, ws_bytes, need))) {
     return st;
@@ -274,6 +307,9 @@ fa_status fwd_run(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t s
   if (overlap(ro, rl)) return fail(FA_ERR_ALIAS, "o overlaps lse");
   if (overlap(rw, ro)) return fail(FA_ERR_ALIAS, "workspace overlaps o");
   if (overlap(rw, rl)) return fail(FA_ERR_ALIAS, "workspace overlaps lse");
+  const Range rb = bias_span(s, a->mask);
+  if (overlap(rb, ro) || overlap(rb, rl) || overlap(rb, rw))
+    return fail(FA_ERR_ALIAS, "key_bias overlaps o, lse or the workspace");
   if (a->mask.kv_valid && reinterpret_cast<uintptr_t>(a->mask.kv_valid) % 4 != 0)
     return fail(FA_ERR_ALIGNMENT, "kv_valid: pointer is not 4-byte aligned");
   if (!rows) return FA_OK;  // nothing to compute
@@ -286,6 +322,7 @@ fa_status fwd_run(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t s
   p.lse = a->lse;
   p.vt = ws;
   p.vt_ss = vt_keys(s);
+  p.bias_s = bias_copy_bytes(s, a->mask) ? reinterpret_cast<float*>(static_cast<char*>(ws) + vt_bytes(s)) : nullptr;
   hipError_t e = s.dtype == FA_BF16 ? fa::launch_fwd_bf16(p, stream) : fa::launch_fwd_f32(p, stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "%s launch failed: %s", fn, hipGetErrorString(e));
   return FA_OK;
@@ -300,7 +337,7 @@ const char* fa_last_error(void) { return g_error.c_str(); }
 size_t fa_fwd_workspace_bytes(const fa_fwd_args* a) {
   if (!a) return 0;
   Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
-  return fwd_ws_bytes(s);
+  return fwd_ws_bytes(s, a->mask);
 }
 
 fa_status fa_fwd(const fa_fwd_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -314,7 +351,7 @@ fa_status fa_fwd_noalloc(const fa_fwd_args* a, hipStream_t stream) {
 size_t fa_bwd_workspace_bytes(const fa_bwd_args* a) {
   if (!a) return 0;
   Shape s{a->dtype, a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->D};
-  return delta_bytes(s, a->mask.kind);
+  return delta_bytes(s, a->mask);
 }
 
 // Validates a backward call and launches the requested stages in order.
@@ -337,7 +374,7 @@ static fa_status bwd_run(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStr
   if (rows && a->lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse: NULL pointer");
   if (rows && reinterpret_cast<uintptr_t>(a->lse) % 4 != 0)
     return fail(FA_ERR_ALIGNMENT, "lse: pointer is not 4-byte aligned");
-  const size_t need = delta_bytes(s, a->mask.kind);
+  const size_t need = delta_bytes(s, a->mask);
   if ((st = check_ws(ws, ws_bytes, need))) return st;
   if (a->mask.kv_valid && reinterpret_cast<uintptr_t>(a->mask.kv_valid) % 4 != 0)
     return fail(FA_ERR_ALIGNMENT, "kv_valid: pointer is not 4-byte aligned");
@@ -347,13 +384,13 @@ static fa_status bwd_run(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStr
                  span(a->dout, s.B, s.Hq, s.Sq, s.D, eb),
                  {reinterpret_cast<uintptr_t>(a->lse),
                   reinterpret_cast<uintptr_t>(a->lse) + (size_t)s.B * s.Hq * s.Sq * 4, !rows},
-                 {0, 0, true}};
+                 bias_span(s, a->mask)};
   Range out[4] = {span(a->dq, s.B, s.Hq, s.Sq, s.D, eb), span(a->dk, s.B, s.Hkv, s.Skv, s.D, eb),
                   span(a->dv, s.B, s.Hkv, s.Skv, s.D, eb),
                   {reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + need, need == 0}};
   const char* out_names[4] = {"dq", "dk", "dv", "workspace"};
   for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
+    for (int j = 0; j < 7; ++j)
       if (overlap(out[i], in[j])) return fail(FA_ERR_ALIAS, "%s overlaps an input tensor", out_names[i]);
     for (int j = i + 1; j < 4; ++j)
       if (overlap(out[i], out[j]))
@@ -372,6 +409,10 @@ static fa_status bwd_run(const fa_bwd_args* a, void* ws, size_t ws_bytes, hipStr
   p.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + row_array_bytes(s));
   p.dkv_part = part_bytes(s, a->mask.kind) ? reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * row_array_bytes(s))
                                             : nullptr;
+  p.vt_ss = vt_keys(s);   // the row length of the scaled key-bias copy
+  p.bias_s = bias_copy_bytes(s, a->mask)
+                 ? reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * row_array_bytes(s) + part_bytes(s, a->mask.kind))
+                 : nullptr;
   // The whole backward in bf16 runs the two gradient stages as one
   // (fa::STAGE_GRADS): the same workgroups, bitwise the same results.
   const bool whole = first_stage == fa::STAGE_DELTA && last_stage == fa::STAGE_DQ && s.dtype == FA_BF16;

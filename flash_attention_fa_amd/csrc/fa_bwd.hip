@@ -16,6 +16,8 @@
 // identical.  Keys no query may attend get exact zeros.
 #include <climits>
 
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace fa {
@@ -67,18 +69,22 @@ __global__ void __launch_bounds__(256) delta_kernel(Params p) {
 constexpr int DQ_TK = 64;     // keys per LDS tile
 constexpr int DQ_NBUF = 4;
 
+// With a key bias, DQ_NBUF 1 KB slots follow: each tile's 64 scaled bias
+// values (256 bytes; the copy instruction that brings them writes 1 KB).
 template <int D>
 struct DqDma {
   static constexpr int TILE = DQ_TK * D * 2;   // K or V rows of one tile
   static constexpr int BUF = 2 * TILE;
   static constexpr int BYTES = DQ_NBUF * BUF;
+  static constexpr int BIAS_BASE = BYTES;
+  static constexpr int BIAS_BYTES = DQ_NBUF * 1024;
 };
 
 // MK: the mask-kind instance.  As in the forward, the MK_TTT tile loop walks
 // the step-0 keys, which the causal mask describes, and adds the single key
 // s*L + i of each later step s to row i's dQ with vector arithmetic
 // (ttt_fold).
-template <int D, int NW, int MK>
+template <int D, int NW, int MK, bool BIAS>
 __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
   constexpr bool TTT = MK == MK_TTT;
   using L = DqDma<D>;
@@ -116,6 +122,9 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
   const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
   const bf16* Vg = static_cast<const bf16*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
   const int64_t rowbase = ((int64_t)b * p.Hq + h) * p.Sq;
+  // BIAS: the scaled key bias of this batch entry, [vt_ss]
+  constexpr bool has_bias = BIAS;
+  const float* Bsg = BIAS ? p.bias_s + (int64_t)b * p.vt_ss : nullptr;
 
   // Q^T and dO^T as B operands; LSE (log2 units) and Delta one per lane.
   bf16x8 qreg[NJ], greg[NJ];
@@ -154,7 +163,7 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
       }
       sd = half_swap_sum(sd);
       pd = half_swap_sum(pd);
-      const float pr = rok ? exp2_fast(sd * p.scale_log2 - l2) : 0.f;
+      const float pr = rok ? exp2_fast((sd + (has_bias ? Bsg[j] : 0.f)) * p.scale_log2 - l2) : 0.f;
       const float ds = pr * (pd - dlt);
       const bf16* kd = kr + 4 * hh;
 #pragma unroll
@@ -200,9 +209,14 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
 #pragma unroll
   for (int x = 0; x < LPW; ++x) voff[x] = 2u * (unsigned)(rstep[x] + rbase + cofs[x]);
   const bool soff_ok = xss >= 0;
+  // With a key bias the last wave also copies the tile's 64 scaled bias
+  // values (lanes 16..63 repeat lanes 0..15; the slot is 1 KB).
+  const bool bias_wave = has_bias && wave == NW - 1;
   auto copy_tile = [&](int t, int k) __attribute__((always_inline)) {
     const int tb = t * TK;
     const unsigned lbuf = lds0 + k * L::BUF;
+    if (bias_wave)
+      lds_dma16_at(Bsg + (t >= 0 ? tb : 0) + 4 * (lane & 15), lds0 + L::BIAS_BASE + k * 1024);
     if (soff_ok && t >= 0 && tb + TK <= m.kvv) {
       const bf16* sbase = Xg + (int64_t)tb * xss;
 #pragma unroll
@@ -224,9 +238,12 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
       }
     }
   };
-  const int my_ins = ALL_COPY ? LPW : (wave * LPW < 2 * NINS ? LPW : 0);
+  const int my_ins = (ALL_COPY ? LPW : (wave * LPW < 2 * NINS ? LPW : 0)) + (bias_wave ? 1 : 0);
   auto wait_copies = [&]() __attribute__((always_inline)) {
-    if (my_ins == LPW) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
+    if (my_ins == LPW) wait_vmcnt<LPW>();
+    else if (my_ins == LPW + 1) wait_vmcnt<LPW + 1>();
+    else if (my_ins == 1) wait_vmcnt<1>();
+    else wait_vmcnt<0>();
   };
 
   int koff[NJ];
@@ -280,10 +297,21 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // dP^T accumulates onto -Delta (the lane's row), so it comes out as
-        // dP^T - Delta.
-        f32x16 s = f32x16{}, dp;
+        // dP^T - Delta; S^T onto the scaled bias of each register's key
+        // (32 kb + 8 (i / 4) + 4 hh + i % 4 of the tile), or zero.
+        f32x16 s, dp;
 #pragma unroll
         for (int i = 0; i < 16; ++i) dp[i] = -dlt;
+        if (has_bias) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 b4 = *FA_LDS(const f32x4, smem + L::BIAS_BASE + k * 1024 + 4 * (32 * kb + 8 * g + 4 * hh));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s[4 * g + u] = b4[u];
+          }
+        } else {
+          s = f32x16{};
+        }
         auto opread = [&](int n) __attribute__((always_inline)) {
           return *FA_LDS(const bf16x8, ((n & 1) ? Vt : Kt) + 2 * kb * ROW16 + koff[n >> 1]);
         };
@@ -365,10 +393,10 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
   }
 }
 
-template <int D, int NW, int MK>
+template <int D, int NW, int MK, bool BIAS>
 __global__ void __launch_bounds__(NW * 64, 2)
 dq_dma_kernel(Params p) {
-  dq_dma_body<D, NW, MK>(p, blockIdx.x);
+  dq_dma_body<D, NW, MK, BIAS>(p, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -410,7 +438,7 @@ struct KvSplit {
 // workgroups per key block, each writing float32 partial sums (see
 // dkdv_split); without it one workgroup takes every step of its block and
 // writes dK, dV.
-template <int D, int MK, bool SPLIT>
+template <int D, int MK, bool SPLIT, bool BIAS>
 __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
   using L = KvSplit<D>;
   constexpr int NW = L::NW, TKW = L::TKW, TQ = L::TQ;
@@ -593,6 +621,10 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
 #pragma unroll
   for (int c = 0; c < NDB; ++c) { dka[c] = f32x16{}; dva[c] = f32x16{}; }
 
+  // BIAS: S starts from the scaled bias of this lane's key (the same for
+  // every query row); otherwise from zero.
+  const float kbias = BIAS && key < nkeys ? p.bias_s[(int64_t)b * p.vt_ss + key] : 0.f;
+
   // Rows from qfull on see every key of this wave's block (CAUSAL / FULL):
   // their tiles need no mask and no classification.
   int qfull = INT_MAX;
@@ -624,7 +656,13 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
     if (state != TILE_SKIP) {
       // dP accumulates onto -Delta of each register's row (q = qa + 8*(i/4) +
       // 4*hh + i%4), so it comes out as dP - Delta.
-      f32x16 s = f32x16{}, dp;
+      f32x16 s, dp;
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = kbias;
+      } else {
+        s = f32x16{};
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 d4 = *FA_LDS(const f32x4, Ds + 32 * h + 8 * g + 4 * hh);
@@ -738,10 +776,10 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
   }
 }
 
-template <int D, int MK, bool SPLIT>
+template <int D, int MK, bool SPLIT, bool BIAS>
 __global__ void __launch_bounds__(512)
 dkdv_split_kernel(Params p) {
-  dkdv_split_body<D, MK, SPLIT>(p, blockIdx.x);
+  dkdv_split_body<D, MK, SPLIT, BIAS>(p, blockIdx.x);
 }
 
 // The two gradient kernels in one launch (the 8-wave dQ): blocks
@@ -752,15 +790,15 @@ dkdv_split_kernel(Params p) {
 // bitwise those of the two launches in turn; as the dK/dV workgroups drain,
 // dQ workgroups take over their compute units instead of leaving them idle
 // until the dK/dV launch ends.
-template <int D, int MKKV, bool SPLIT, int MKQ>
+template <int D, int MKKV, bool SPLIT, int MKQ, bool BIAS>
 __global__ void __launch_bounds__(512, 2)
 grads_kernel(Params p, int nkv, int nkv_pad) {
   const int bid = blockIdx.x;
   if (bid < nkv_pad) {
-    if (bid < nkv) dkdv_split_body<D, MKKV, SPLIT>(p, bid);
+    if (bid < nkv) dkdv_split_body<D, MKKV, SPLIT, BIAS>(p, bid);
     return;
   }
-  dq_dma_body<D, 8, MKQ>(p, bid - nkv_pad);
+  dq_dma_body<D, 8, MKQ, BIAS>(p, bid - nkv_pad);
 }
 
 // dK = scale * (half 0 + half 1), dV = half 0 + half 1, rounded to bf16; 8
@@ -817,6 +855,7 @@ __global__ void __launch_bounds__(256) ttt_dkdv_kernel(Params p) {
   const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.v.ptr) + b * p.v.sb +
                                                      hk * p.v.sh + (int64_t)j * p.v.ss + 8 * sub);
   float dk[8] = {}, dv[8] = {};
+  const float kbias = p.bias_s ? p.bias_s[(int64_t)b * p.vt_ss + j] : 0.f;
   if (r < m.kvv) {
     for (int h = 0; h < p.G; ++h) {
       const int hq = hk * p.G + h;
@@ -831,7 +870,7 @@ __global__ void __launch_bounds__(256) ttt_dkdv_kernel(Params p) {
         sd += __shfl_xor(sd, o, LPK);
         pd += __shfl_xor(pd, o, LPK);
       }
-      const float pr = exp2_fast(sd * p.scale_log2 - p.lse2[row]);
+      const float pr = exp2_fast((sd + kbias) * p.scale_log2 - p.lse2[row]);
       const float ds = pr * (pd - p.delta[row]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -893,10 +932,15 @@ hipError_t launch_grads(const Params& p, hipStream_t stream, bool& done) {
     const int64_t nkv_pad = (nkv + 7) / 8 * 8;
     if (nkv_pad + ndq > INT_MAX) return hipSuccess;
     const int mk = mask_instance(p.mask.kind);
-    auto k = mk == MK_WIN ? (split ? grads_kernel<D, MK_WIN, true, MK_WIN> : grads_kernel<D, MK_WIN, false, MK_WIN>)
-           : mk == MK_TTT ? (split ? grads_kernel<D, MK_FC, true, MK_TTT> : grads_kernel<D, MK_FC, false, MK_TTT>)
-                          : (split ? grads_kernel<D, MK_FC, true, MK_FC> : grads_kernel<D, MK_FC, false, MK_FC>);
-    const int lds = LD::BYTES > DqDma<D>::BYTES ? LD::BYTES : DqDma<D>::BYTES;
+    auto pick = [&](auto bc) {
+      constexpr bool BI = decltype(bc)::value;
+      return mk == MK_WIN ? (split ? grads_kernel<D, MK_WIN, true, MK_WIN, BI> : grads_kernel<D, MK_WIN, false, MK_WIN, BI>)
+           : mk == MK_TTT ? (split ? grads_kernel<D, MK_FC, true, MK_TTT, BI> : grads_kernel<D, MK_FC, false, MK_TTT, BI>)
+                          : (split ? grads_kernel<D, MK_FC, true, MK_FC, BI> : grads_kernel<D, MK_FC, false, MK_FC, BI>);
+    };
+    auto k = p.bias_s ? pick(std::true_type{}) : pick(std::false_type{});
+    const int lq = DqDma<D>::BYTES + (p.bias_s ? DqDma<D>::BIAS_BYTES : 0);
+    const int lds = LD::BYTES > lq ? LD::BYTES : lq;
     hipError_t e;
     if ((e = set_lds(k, lds)) != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3((unsigned)(nkv_pad + ndq)), dim3(512), lds, stream, p, (int)nkv, (int)nkv_pad);
@@ -922,6 +966,8 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // the scaled key bias the dK/dV and dQ stages start their scores from
+  if (stage == STAGE_DELTA && (e = launch_bias_scale(p, stream)) != hipSuccess) return e;
   if (stage == STAGE_DKDV) {
     using LD = KvSplit<D>;
     const int nkeys = walk_keys(p);
@@ -929,8 +975,12 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     const int64_t nblk = (int64_t)p.B * p.Hkv * (split ? 2 : 1) * ((nkeys + LD::TKW - 1) / LD::TKW);
     if (nblk > 0) {
       const bool win = p.mask.kind == MASK_WINDOW;
-      auto k = split ? (win ? dkdv_split_kernel<D, MK_WIN, true> : dkdv_split_kernel<D, MK_FC, true>)
-                     : (win ? dkdv_split_kernel<D, MK_WIN, false> : dkdv_split_kernel<D, MK_FC, false>);
+      auto pick = [&](auto bc) {
+        constexpr bool BI = decltype(bc)::value;
+        return split ? (win ? dkdv_split_kernel<D, MK_WIN, true, BI> : dkdv_split_kernel<D, MK_FC, true, BI>)
+                     : (win ? dkdv_split_kernel<D, MK_WIN, false, BI> : dkdv_split_kernel<D, MK_FC, false, BI>);
+      };
+      auto k = p.bias_s ? pick(std::true_type{}) : pick(std::false_type{});
       if ((e = set_lds(k, LD::BYTES)) != hipSuccess) return e;
       hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(LD::NW * 64), LD::BYTES, stream, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -943,14 +993,19 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     // 8-wave workgroups when there are enough to fill the chip twice over
     const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
     const int mk = mask_instance(p.mask.kind);
-    auto k = wg8 >= 512 ? (mk == MK_TTT ? dq_dma_kernel<D, 8, MK_TTT>
-                                        : (mk == MK_WIN ? dq_dma_kernel<D, 8, MK_WIN> : dq_dma_kernel<D, 8, MK_FC>))
-                        : (mk == MK_TTT ? dq_dma_kernel<D, 4, MK_TTT>
-                                        : (mk == MK_WIN ? dq_dma_kernel<D, 4, MK_WIN> : dq_dma_kernel<D, 4, MK_FC>));
+    auto pick = [&](auto bc) {
+      constexpr bool BI = decltype(bc)::value;
+      return wg8 >= 512 ? (mk == MK_TTT ? dq_dma_kernel<D, 8, MK_TTT, BI>
+                                        : (mk == MK_WIN ? dq_dma_kernel<D, 8, MK_WIN, BI> : dq_dma_kernel<D, 8, MK_FC, BI>))
+                        : (mk == MK_TTT ? dq_dma_kernel<D, 4, MK_TTT, BI>
+                                        : (mk == MK_WIN ? dq_dma_kernel<D, 4, MK_WIN, BI> : dq_dma_kernel<D, 4, MK_FC, BI>));
+    };
+    auto k = p.bias_s ? pick(std::true_type{}) : pick(std::false_type{});
     const int nw = wg8 >= 512 ? 8 : 4;
     const int64_t nblk = (int64_t)p.B * p.Hq * ((p.Sq + nw * 32 - 1) / (nw * 32));
-    if ((e = set_lds(k, DqDma<D>::BYTES)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(nw * 64), DqDma<D>::BYTES, stream, p);
+    const int lds = DqDma<D>::BYTES + (p.bias_s ? DqDma<D>::BIAS_BYTES : 0);
+    if ((e = set_lds(k, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(nw * 64), lds, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -35,6 +35,7 @@ enum { MASK_FULL = 0, MASK_CAUSAL = 1, MASK_TTT = 2, MASK_WINDOW = 3 };
 enum { TILE_SKIP = 0, TILE_FULL = 1, TILE_PART = 2 };
 
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
 // Running max starts here instead of -inf so exp2(x - m) never sees
 // (-inf) - (-inf); any finite score exceeds it and triggers a rescale.
 constexpr float kMaxInit = -1.0e30f;
@@ -473,6 +474,27 @@ hipError_t launch_transpose_keys(const Params& p, const Tensor& src, void* dst, 
   const unsigned grid = (unsigned)(nblk < (1 << 20) ? nblk : (1 << 20));
   hipLaunchKernelGGL(transpose_keys_kernel<D>, dim3(grid), dim3(256), 0, s, p, src, static_cast<bf16*>(dst),
                      dst_ss, ntile, nblk);
+  return hipGetLastError();
+}
+
+// The key bias divided by the scale, float32 [B, vt_ss] with zeros past Skv:
+// the value a score's matrix-core accumulation starts from, so the scaled
+// score comes out as scale * (q.k + bias / scale) = scale q.k + bias.
+template <int Unused = 0>
+__global__ void __launch_bounds__(256) bias_scale_kernel(Params p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t b = i / p.vt_ss, j = i % p.vt_ss;
+    p.bias_s[i] = j < p.Skv ? p.mask.bias[b * p.mask.bias_sb + j] / p.scale : 0.f;
+  }
+}
+
+inline hipError_t launch_bias_scale(const Params& p, hipStream_t s) {
+  if (p.mask.bias == nullptr || p.bias_s == nullptr) return hipSuccess;
+  const int64_t n = (int64_t)p.B * p.vt_ss;
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(bias_scale_kernel<0>, dim3((unsigned)(blocks < (1 << 16) ? blocks : (1 << 16))), dim3(256), 0,
+                     s, p, n);
   return hipGetLastError();
 }
 

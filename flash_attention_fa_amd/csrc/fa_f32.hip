@@ -47,6 +47,7 @@ __global__ void __launch_bounds__(F_ROWS) fwd_f32_kernel(Params p) {
   const float* Kg = static_cast<const float*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
   const float* Vg = static_cast<const float*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh;
   load_rows<D>(Qs, Qg, p.q.ss, qa, F_ROWS, p.Sq, &m, false);
+  const float* Bg = p.mask.bias ? p.mask.bias + (int64_t)b * p.mask.bias_sb : nullptr;
 
   float o[D];
 #pragma unroll
@@ -68,7 +69,7 @@ __global__ void __launch_bounds__(F_ROWS) fwd_f32_kernel(Params p) {
 #pragma unroll
       for (int d = 0; d < D; ++d) dot = fmaf(Qs[threadIdx.x * D + d], Ks[j * D + d], dot);
       const bool ok = allowed(m, i, k0 + j) && k0 + j < p.Skv;
-      sc[j] = ok ? dot * p.scale_log2 : -INFINITY;
+      sc[j] = ok ? dot * p.scale_log2 + (Bg ? Bg[k0 + j] * kLog2e : 0.f) : -INFINITY;
       mt = fmaxf(mt, sc[j]);
     }
     const float mn = fmaxf(mrun, mt);
@@ -133,6 +134,7 @@ __global__ void __launch_bounds__(F_ROWS) dq_f32_kernel(Params p) {
   load_rows<D>(Qs, Qg, p.q.ss, qa, F_ROWS, p.Sq, &m, false);
   load_rows<D>(Gs, Gg, p.dout.ss, qa, F_ROWS, p.Sq, &m, false);
   const int64_t rb = ((int64_t)b * p.Hq + h) * p.Sq;
+  const float* Bg = p.mask.bias ? p.mask.bias + (int64_t)b * p.mask.bias_sb : nullptr;
   float lse2 = 0.f, delta = 0.f;
   if (i < p.Sq) {
     lse2 = p.lse_in[rb + i] * 1.4426950408889634f;
@@ -157,7 +159,7 @@ __global__ void __launch_bounds__(F_ROWS) dq_f32_kernel(Params p) {
         s = fmaf(Qs[threadIdx.x * D + d], Ks[j * D + d], s);
         dp = fmaf(Gs[threadIdx.x * D + d], Vs[j * D + d], dp);
       }
-      const float pr = exp2_fast(s * p.scale_log2 - lse2);
+      const float pr = exp2_fast(s * p.scale_log2 + (Bg ? Bg[k0 + j] * kLog2e : 0.f) - lse2);
       const float ds = pr * (dp - delta);
 #pragma unroll
       for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, Ks[j * D + d], dq[d]);
@@ -197,6 +199,8 @@ __global__ void __launch_bounds__(F_ROWS) dkdv_f32_kernel(Params p) {
   int qlo, qhi;
   query_hull(m, ka, kbnd, qlo, qhi);
   const bool real = j < p.Skv && key_valid(m, j);
+  // this thread's key bias in log2 units (0 without one)
+  const float kb2 = real && p.mask.bias ? p.mask.bias[(int64_t)b * p.mask.bias_sb + j] * kLog2e : 0.f;
   for (int hq = 0; hq < p.G; ++hq) {
     const int h = hk * p.G + hq;
     const float* Qg = static_cast<const float*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
@@ -222,7 +226,7 @@ __global__ void __launch_bounds__(F_ROWS) dkdv_f32_kernel(Params p) {
           s = fmaf(Qs[r * D + d], Ks[threadIdx.x * D + d], s);
           dp = fmaf(Gs[r * D + d], Vs[threadIdx.x * D + d], dp);
         }
-        const float pr = exp2_fast(s * p.scale_log2 - Ls[r]);
+        const float pr = exp2_fast(s * p.scale_log2 + kb2 - Ls[r]);
         const float ds = pr * (dp - Ds[r]);
 #pragma unroll
         for (int d = 0; d < D; ++d) {

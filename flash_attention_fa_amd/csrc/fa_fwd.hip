@@ -39,6 +39,7 @@
 // of tile i+1 (partial tiles only) closes the iteration.  One barrier per
 // tile, which waits only for the copies of tile i+2.
 #include <algorithm>
+#include <type_traits>
 
 #include "fa_device.h"
 
@@ -55,11 +56,15 @@ constexpr float kSumLimit = 4096.0f;
 // LDS: the NBUF K tiles (64 swizzled rows of D), then the NBUF V^T tiles (D
 // swizzled rows of 64 keys), so every operand address of a ring buffer is a
 // lane constant plus an immediate below 64 KB.
+// With a key bias, NBUF 1 KB slots follow: the tile's 64 scaled bias values
+// (256 bytes; the copy instruction that brings them writes 1 KB).
 template <int D>
 struct FwdLds {
   static constexpr int TILE_BYTES = TK * D * 2;          // one K or V^T tile
   static constexpr int VT_BASE = NBUF * TILE_BYTES;
   static constexpr int BYTES = 2 * NBUF * TILE_BYTES;
+  static constexpr int BIAS_BASE = BYTES;
+  static constexpr int BIAS_BYTES = NBUF * 1024;
 };
 
 template <int K>
@@ -74,7 +79,7 @@ struct Buf {
 // of a 64-key tile per step that holds one key per row, each lane folds its
 // row's keys into the running max, normaliser and O before the tile loop
 // (ttt_fold).
-template <int D, int NW, int MK>
+template <int D, int NW, int MK, bool BIAS>
 __global__ void __launch_bounds__(NW * 64, 2)
 fwd_kernel(Params p) {
   constexpr bool TTT = MK == MK_TTT;
@@ -109,6 +114,9 @@ fwd_kernel(Params p) {
   const bf16* Qg = static_cast<const bf16*>(p.q.ptr) + b * p.q.sb + h * p.q.sh;
   const bf16* Kg = static_cast<const bf16*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh;
   const bf16* VTg = static_cast<const bf16*>(p.vt) + (int64_t)(b * p.Hkv + hk) * D * p.vt_ss;
+  // BIAS: the scaled key bias of this batch entry, [vt_ss]
+  constexpr bool has_bias = BIAS;
+  const float* Bsg = BIAS ? p.bias_s + (int64_t)b * p.vt_ss : nullptr;
 
   // Q^T as the B operand: lane (q = l32, half hh) holds Q[q][16j + 8hh .. +8].
   bf16x8 qreg[NJ];
@@ -143,7 +151,7 @@ fwd_kernel(Params p) {
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) dot = dot_bf16x8(qreg[jj], *reinterpret_cast<const bf16x8*>(kr + 16 * jj), dot);
       dot = half_swap_sum(dot);
-      const float x = rok ? dot * p.scale_log2 : -INFINITY;
+      const float x = rok ? (dot + (has_bias ? Bsg[j] : 0.f)) * p.scale_log2 : -INFINITY;
       const float mn = fmaxf(mrun, x);
       const float alpha = exp2_fast(mrun - mn);
       const float pr = exp2_fast(x - mn);
@@ -203,9 +211,14 @@ fwd_kernel(Params p) {
 #pragma unroll
   for (int x = 0; x < LPW; ++x) voff[x] = 2u * (unsigned)(rstep[x] + rbase + cofs[x]);
   const bool soff_ok = p.k.ss >= 0;
+  // With a key bias the last wave also copies the tile's 64 scaled bias
+  // values (lanes 16..63 repeat lanes 0..15; the slot is 1 KB).
+  const bool bias_wave = has_bias && wave == NW - 1;
   auto copy_tiles = [&](int t, int k) __attribute__((always_inline)) {
     const int tb = t * TK;
     const unsigned lbuf = lds0 + k * L::TILE_BYTES;
+    if (bias_wave)
+      lds_dma16_at(Bsg + (t >= 0 ? tb : 0) + 4 * (lane & 15), lds0 + L::BIAS_BASE + k * 1024);
     if (soff_ok && t >= 0 && tb + TK <= m.kvv) {
       const bf16* sbase = wk ? Kg + (int64_t)tb * p.k.ss : VTg + tb;
 #pragma unroll
@@ -228,9 +241,30 @@ fwd_kernel(Params p) {
     }
   };
   // Waits until this wave's copies of all but the newest tile have landed.
-  const int my_ins = ALL_COPY ? LPW : (wave * LPW < 2 * NINS ? LPW : 0);
+  const int my_ins = (ALL_COPY ? LPW : (wave * LPW < 2 * NINS ? LPW : 0)) + (bias_wave ? 1 : 0);
   auto wait_copies = [&]() __attribute__((always_inline)) {
-    if (my_ins == LPW) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
+    if (my_ins == LPW) wait_vmcnt<LPW>();
+    else if (my_ins == LPW + 1) wait_vmcnt<LPW + 1>();
+    else if (my_ins == 1) wait_vmcnt<1>();
+    else wait_vmcnt<0>();
+  };
+  // Where the scores of the tile in buffer k start: the scaled bias of their
+  // keys (register i of key block kb holds key 32 kb + 8 (i / 4) + 4 hh +
+  // i % 4 of the tile), or zero.
+  auto score_init = [&](int k, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    if (has_bias) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 b4 = *FA_LDS(const f32x4, smem + L::BIAS_BASE + k * 1024 + 4 * (32 * kb + 8 * g + 4 * hh));
+#pragma unroll
+          for (int u = 0; u < 4; ++u) s[kb][4 * g + u] = b4[u];
+        }
+    } else {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+    }
   };
 
   // Lane-constant byte offsets into a tile: the swizzle of a row depends only
@@ -251,8 +285,7 @@ fwd_kernel(Params p) {
   // S^T of the tile in buffer k: 2 key blocks of 32.
   auto qk = [&](auto kc, f32x16 (&s)[2]) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+    score_init(k, s);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -312,8 +345,7 @@ fwd_kernel(Params p) {
   auto qk_softmax = [&](auto kc, f32x16 (&s)[2], const f32x16 (&sp)[2], bf16x8 (&pb)[2][2])
       __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+    score_init(k, s);
     float e[2][2][8];
     float ls = 0.f;
     // K operands are read PF products ahead of their use.
@@ -456,12 +488,18 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   const int nq = (p.Sq + TQ - 1) / TQ;
   const int64_t nblk = (int64_t)p.B * p.Hq * nq;
   if (nblk == 0) return hipSuccess;
-  // V^T of the keys the tile walk reads
+  // V^T of the keys the tile walk reads, and the scaled key bias
   hipError_t e = launch_transpose_keys<D>(p, p.v, p.vt, p.vt_ss, stream);
   if (e != hipSuccess) return e;
-  const int lds = FwdLds<D>::BYTES;
+  if ((e = launch_bias_scale(p, stream)) != hipSuccess) return e;
+  const int lds = FwdLds<D>::BYTES + (p.bias_s ? FwdLds<D>::BIAS_BYTES : 0);
   const int mk = mask_instance(p.mask.kind);
-  auto k = mk == MK_TTT ? fwd_kernel<D, NW, MK_TTT> : (mk == MK_WIN ? fwd_kernel<D, NW, MK_WIN> : fwd_kernel<D, NW, MK_FC>);
+  auto pick = [&](auto bc) {
+    constexpr bool BI = decltype(bc)::value;
+    return mk == MK_TTT ? fwd_kernel<D, NW, MK_TTT, BI>
+                        : (mk == MK_WIN ? fwd_kernel<D, NW, MK_WIN, BI> : fwd_kernel<D, NW, MK_FC, BI>);
+  };
+  auto k = p.bias_s ? pick(std::true_type{}) : pick(std::false_type{});
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(NW * 64), lds, stream, p);

@@ -17,6 +17,8 @@ struct Mask {
   const int* kv_valid; // device [B] or nullptr
   int wl, wr;          // WINDOW: keys allowed before / after the (shifted) diagonal
   int frozen;          // keys below it get dK = dV = 0, not computed
+  const float* bias;   // key bias [B, Skv] (row stride bias_sb) or nullptr
+  int64_t bias_sb;
 };
 
 // Keys per V^T tile of the forward workspace (the forward's key tile).
@@ -39,6 +41,9 @@ struct Params {
   float* lse2;         // backward workspace: LSE * log2(e) [B, Hq, Sq]
   float* dkv_part;     // backward workspace (bf16): two halves' float32
                        // sums [2][dK^T, dV^T][B, Hkv, Skv, D]
+  float* bias_s;       // workspace (bf16, with a key bias): bias / scale,
+                       // [B, vt_ss], zero past Skv; written by the pre-pass
+                       // (forward) or the Delta stage (backward)
 };
 
 // The bf16 dK/dV kernel owns 256-key blocks.  With fewer than

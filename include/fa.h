@@ -132,6 +132,21 @@ typedef struct {
                                 whose K/V are not trained): the backward writes
                                 dK = dV = 0 there and does not compute them; the
                                 forward and dQ are unchanged.  0 = none */
+  const float* key_bias;     /* device float32 [B, Skv] or NULL: an additive mask
+                                in per-key form (the ggml playbook, "3. Per-trainer
+                                porting checklist": the fused ops take an additive
+                                mask, broadcast where it has fewer dimensions).
+                                key_bias[b * key_bias_stride_b + j] is added to the
+                                scaled score of key j for every query row and head
+                                of batch entry b, on top of the mask kind (a key
+                                still needs the kind's permission); LSE includes
+                                it.  Values are finite or -inf (-inf drops the key
+                                for that batch entry); +inf and NaN give undefined
+                                results.  An input only: the backward computes no
+                                gradient for it.  4-byte aligned; the caller owns
+                                it and must pass the same bias to fa_bwd. */
+  int64_t key_bias_stride_b; /* >= 0, elements between batch rows of key_bias
+                                (0: one row for every batch entry) */
 } fa_mask_desc;
 
 /* Forward arguments: the shapes, the softmax scale (1/sqrt(d_k) by default,
@@ -173,7 +188,10 @@ typedef struct {
  * transposed copy of V, bfloat16 [B, Hkv, D, Skv rounded up to 64], rounded
  * up to 256 bytes (the PV product, O^T = V^T P^T of CS336 "Flash Attention
  * (Triton)", contracts over keys; stored key-minor, V^T feeds the matrix
- * cores with plain 16-byte reads).  FA_F32: 0.  Linear in Skv, never S x S.
+ * cores with plain 16-byte reads).  With a key_bias, FA_BF16 adds float32
+ * [B, Skv rounded up to 64] (the bias divided by the scale, which the matrix
+ * cores take as the initial value of each score), rounded up to 256 bytes.
+ * FA_F32: 0.  Linear in Skv, never S x S.  Depends on args->mask.key_bias.
  * Returns 0 when args is NULL. */
 size_t fa_fwd_workspace_bytes(const fa_fwd_args* args);
 
@@ -207,8 +225,10 @@ fa_status fa_fwd_noalloc(const fa_fwd_args* args, hipStream_t stream);
  * bytes, and for FA_BF16 the dK/dV kernel's float32 partial
  * sums, four [B, Hkv, Skv, D] arrays (two halves of each key block's query
  * steps, dK and dV; under FA_MASK_TTT only the Sq step-0 keys have them, so
- * Sq replaces Skv), rounded up to 256 bytes; linear in Sq and Skv, never
- * S x S.  Depends on args->mask.kind.  Returns 0 when args is NULL. */
+ * Sq replaces Skv), rounded up to 256 bytes, and with a key_bias a float32
+ * [B, Skv rounded up to 64] copy of it divided by the scale, rounded up to
+ * 256 bytes; linear in Sq and Skv, never S x S.  Depends on args->mask.kind
+ * and args->mask.key_bias.  Returns 0 when args is NULL. */
 size_t fa_bwd_workspace_bytes(const fa_bwd_args* args);
 
 /* Backward: writes dQ, dK, dV; bitwise identical on every rerun (fixed

@@ -18,6 +18,7 @@ import pytest
 from flash_attention_fa_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HERE = os.path.dirname(os.path.abspath(__file__))
 BASE = 1 << 32          # fake device addresses: 16-byte aligned, far apart
 GAP = 1 << 28
 
@@ -36,17 +37,41 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def _c_layout(structs):
+    """sizeof and offsetof of every field, as gcc lays out include/fa.h."""
+    import shutil
+    import subprocess
+    import tempfile
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    root = os.path.dirname(HERE)
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "fa.h"', 'int main(void) {']
+    for name, fields in structs.items():
+        lines.append(f'  printf("{name} sizeof %zu\\n", sizeof({name}));')
+        for f in fields:
+            lines.append(f'  printf("{name} {f} %zu\\n", offsetof({name}, {f}));')
+    lines += ['  return 0;', '}']
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "layout.c"), os.path.join(d, "layout")
+        with open(src, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        subprocess.run([gcc, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"),
+                        "-I", "/opt/rocm/include", src, "-o", exe], check=True, capture_output=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    return {tuple(l.split()[:2]): int(l.split()[2]) for l in out.splitlines()}
+
+
 def test_struct_layout_matches_header():
-    # offsets a C compiler gives the structs of fa.h on x86-64
-    assert ctypes.sizeof(_lib.fa_tensor) == 32
-    assert ctypes.sizeof(_lib.fa_mask_desc) == 32
-    assert _lib.fa_mask_desc.frozen_keys.offset == 24
-    assert _lib.fa_mask_desc.kv_valid.offset == 8 and _lib.fa_mask_desc.window_right.offset == 20
-    assert _lib.fa_fwd_args.q.offset == 32
-    assert _lib.fa_fwd_args.lse.offset == 32 + 4 * 32
-    assert _lib.fa_fwd_args.mask.offset == 32 + 4 * 32 + 8
-    assert _lib.fa_bwd_args.lse.offset == 32 + 5 * 32
-    assert _lib.fa_bwd_args.mask.offset == 32 + 5 * 32 + 8 + 3 * 32
+    # every ctypes mirror against the layout gcc gives the structs of fa.h
+    structs = {"fa_tensor": _lib.fa_tensor, "fa_mask_desc": _lib.fa_mask_desc,
+               "fa_fwd_args": _lib.fa_fwd_args, "fa_bwd_args": _lib.fa_bwd_args,
+               "fa_lsm_loss_args": _lib.fa_lsm_loss_args}
+    c = _c_layout({n: [f[0] for f in t._fields_] for n, t in structs.items()})
+    for n, t in structs.items():
+        assert c[(n, "sizeof")] == ctypes.sizeof(t), n
+        for f in t._fields_:
+            assert c[(n, f[0])] == getattr(t, f[0]).offset, (n, f[0])
 
 
 def _t(slot, B, H, S, D, eb=2, strides=None):
@@ -322,3 +347,81 @@ def test_noalloc_valid_request_without_device_fails_cleanly():
     # fp32 needs no scratch at any size: never refused for its size
     st, msg = fwd_noalloc(fwd_args(B=1, Hq=32, Hkv=4, Sq=64, Skv=65600, D=128, kind=0, dtype=_lib.FA_F32))
     assert st == _lib.FA_ERR_HIP, msg
+
+
+# ---- the key bias (fa_mask_desc.key_bias) ----------------------------------
+
+BIAS = BASE + 10 * GAP
+
+
+def test_key_bias_validation():
+    for make, call in ((fwd_args, fwd), (bwd_args, bwd)):
+        a = make()
+        a.mask.key_bias = BIAS + 2                # not 4-byte aligned
+        st, msg = call(a, ws_bytes=1 << 26)
+        assert st == _lib.FA_ERR_ALIGNMENT and "key_bias" in msg
+        a = make()
+        a.mask.key_bias, a.mask.key_bias_stride_b = BIAS, -64
+        st, msg = call(a, ws_bytes=1 << 26)
+        assert st == _lib.FA_ERR_INVALID_ARG and "key_bias_stride_b" in msg
+    # the bias is an input: no output or workspace may overlap it
+    a = fwd_args()
+    a.mask.key_bias = a.o.data + 256
+    st, msg = fwd(a)
+    assert st == _lib.FA_ERR_ALIAS and "key_bias" in msg
+    a = fwd_args()
+    a.mask.key_bias = a.lse
+    st, msg = fwd(a)
+    assert st == _lib.FA_ERR_ALIAS and "key_bias" in msg
+    a = bwd_args()
+    a.mask.key_bias = a.dk.data
+    st, msg = bwd(a, ws_bytes=1 << 26)
+    assert st == _lib.FA_ERR_ALIAS and "dk" in msg
+    a = bwd_args()
+    a.mask.key_bias = WS + 64                 # inside the workspace
+    st, msg = bwd(a, ws_bytes=1 << 26)
+    assert st == _lib.FA_ERR_ALIAS and "workspace" in msg
+    # empty shapes never read the bias: any pointer passes the bias checks
+    a = fwd_args(B=0)
+    a.mask.key_bias = BIAS + 2
+    assert fwd(a)[0] == _lib.FA_OK
+
+
+def test_key_bias_workspace_bytes():
+    # bf16: the scaled bias copy, float32 [B, Skv rounded up to 64], rounded up
+    # to 256 bytes, after the forward's V^T and after the backward's arrays
+    for B, Skv in ((1, 64), (2, 100), (3, 1)):
+        a = fwd_args(B=B, Skv=Skv)
+        base = _lib.lib().fa_fwd_workspace_bytes(a)
+        a.mask.key_bias = BIAS
+        extra = (B * ((Skv + 63) // 64 * 64) * 4 + 255) // 256 * 256
+        assert _lib.lib().fa_fwd_workspace_bytes(a) == base + extra
+        b = bwd_args(B=B, Skv=Skv)
+        base = _lib.lib().fa_bwd_workspace_bytes(b)
+        b.mask.key_bias = BIAS
+        assert _lib.lib().fa_bwd_workspace_bytes(b) == base + extra
+    # fp32 reads the caller's bias as is: no extra scratch
+    for make, f in ((fwd_args, _lib.lib().fa_fwd_workspace_bytes), (bwd_args, _lib.lib().fa_bwd_workspace_bytes)):
+        a = make(dtype=_lib.FA_F32)
+        base = f(a)
+        a.mask.key_bias = BIAS
+        assert f(a) == base
+    # a workspace sized without the bias is too small with it
+    a = fwd_args()
+    need = _lib.lib().fa_fwd_workspace_bytes(a)
+    a.mask.key_bias = BIAS
+    st, msg = fwd(a, ws_bytes=need)
+    assert st == _lib.FA_ERR_INVALID_ARG and "workspace too small" in msg
+
+
+@no_device
+def test_key_bias_valid_request_without_device_fails_cleanly():
+    for dtype in (_lib.FA_BF16, _lib.FA_F32):
+        a = fwd_args(dtype=dtype)
+        a.mask.key_bias, a.mask.key_bias_stride_b = BIAS, 0
+        st, msg = fwd(a, ws_bytes=1 << 26)
+        assert st == _lib.FA_ERR_HIP
+        b = bwd_args(dtype=dtype)
+        b.mask.key_bias, b.mask.key_bias_stride_b = BIAS, 64
+        st, msg = bwd(b, ws_bytes=1 << 26)
+        assert st == _lib.FA_ERR_HIP

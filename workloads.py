@@ -177,6 +177,17 @@ def make_stress_inputs(recipe, B, Hq, Hkv, Sq, Skv, D, seed=0, spikes=(), level=
     return tuple(x.to(dtype) for x in (q, k, v, do))
 
 
+def make_key_bias(B, Skv, seed=0, lo=-3.0, hi=3.0, neg_inf_frac=0.15, device="cpu"):
+    """A per-batch key bias [B, Skv] float32: uniform in [lo, hi) with a
+    fraction of the keys at -inf (dropped), key 0 always finite."""
+    g = torch.Generator().manual_seed(seed)
+    b = torch.rand(B, Skv, generator=g) * (hi - lo) + lo
+    drop = torch.rand(B, Skv, generator=g) < neg_inf_frac
+    drop[:, 0] = False
+    b[drop] = float("-inf")
+    return b.to(device)
+
+
 # ---- soft-target log-softmax loss workloads ---------------------------------
 # The (B, T, V) configurations of the SpecForge page's loss benchmark (section
 # "In-place Gradient Calculation").  Recipe: a generator on ``device`` seeded
