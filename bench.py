@@ -213,7 +213,7 @@ def cpu_baseline(w, q, k, v, do, nheads):
 
 
 def dkdv_label(w):
-    if w.dtype == "bf16" and w.D >= 32:
+    if w.dtype == "bf16":
         return "dK/dV stage (fa_bwd_stage FA_BWD_DKDV: dkdv_split_kernel + dkdv_reduce_kernel)"
     return "dK/dV stage (fa_bwd_stage FA_BWD_DKDV: one kernel)"
 
