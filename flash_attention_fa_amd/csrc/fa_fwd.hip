@@ -506,12 +506,17 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// 8-wave workgroups (256 query rows) when there are enough of them to fill
-// the chip twice over, 4-wave ones (128 rows) for small problems.
+// D = 128: 8-wave workgroups (256 query rows) when there are enough of them
+// to fill the chip twice over, 4-wave ones (128 rows) for small problems.
+// D <= 64: always 4-wave workgroups.  Their LDS ring (64 KB or less) lets two
+// share a compute unit, so while one waits at its per-tile barrier the
+// other's waves keep the SIMDs busy (an 8-wave workgroup's barrier stalls all
+// of a compute unit's waves at once); at D = 128 one 4-wave workgroup's ring
+// (128 KB) fills the LDS and leaves each SIMD a single wave.
 template <int D>
 hipError_t launch_d(const Params& p, hipStream_t s) {
   const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
-  if (wg8 >= 512) return launch<D, 8>(p, s);
+  if (D >= 128 && wg8 >= 512) return launch<D, 8>(p, s);
   return launch<D, 4>(p, s);
 }
 
