@@ -423,9 +423,11 @@ dq_dma_kernel(Params p) {
 // two halves, always half 0 + half 1, so reruns are bitwise identical.
 // With more blocks one workgroup takes every step of its block and writes
 // dK and dV directly.
+// D <= 64: 4-wave workgroups of 128 keys (two share a compute unit, so one's
+// per-step barrier does not idle all of its waves); D = 128: 8 waves, 256 keys.
 template <int D>
 struct KvSplit {
-  static constexpr int NW = 8;
+  static constexpr int NW = D <= 64 ? 4 : 8;
   static constexpr int TKW = NW * 32;                  // keys per workgroup
   static constexpr int TQ = 64;                        // query rows per step (two 32-row sub-tiles)
   static constexpr int TILE = TQ * D * 2;              // one Q or dO tile (bytes)
@@ -454,7 +456,7 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
   constexpr int VLPW = VINS / NW;
   constexpr int ROW16 = 16 * 2 * D;     // bytes of 16 rows
   static_assert(D >= 16 && QLPW * NW >= 2 * QINS && QINS % QLPW == 0 && VLPW * NW == VINS &&
-                TKW == kDkdvKeys, "copy split");
+                kDkdvKeys % TKW == 0, "copy split");
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* const Vs = smem + 2 * L::STAGE;
 
@@ -777,12 +779,13 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
 }
 
 template <int D, int MK, bool SPLIT, bool BIAS>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(KvSplit<D>::NW * 64, 2)
 dkdv_split_kernel(Params p) {
   dkdv_split_body<D, MK, SPLIT, BIAS>(p, blockIdx.x);
 }
 
-// The two gradient kernels in one launch (the 8-wave dQ): blocks
+// The two gradient kernels in one launch (dQ with the dK/dV kernel's wave
+// count): blocks
 // [0, nkv) are dkdv_split_kernel's workgroups, blocks [nkv_pad, gridDim) the
 // dQ kernel's (nkv_pad is nkv rounded up to a multiple of 8, so the dQ blocks
 // keep their XCD placement; the blocks in between do nothing).  Each block
@@ -791,14 +794,14 @@ dkdv_split_kernel(Params p) {
 // dQ workgroups take over their compute units instead of leaving them idle
 // until the dK/dV launch ends.
 template <int D, int MKKV, bool SPLIT, int MKQ, bool BIAS>
-__global__ void __launch_bounds__(512, 2)
+__global__ void __launch_bounds__(KvSplit<D>::NW * 64, 2)
 grads_kernel(Params p, int nkv, int nkv_pad) {
   const int bid = blockIdx.x;
   if (bid < nkv_pad) {
     if (bid < nkv) dkdv_split_body<D, MKKV, SPLIT, BIAS>(p, bid);
     return;
   }
-  dq_dma_body<D, 8, MKQ, BIAS>(p, bid - nkv_pad);
+  dq_dma_body<D, KvSplit<D>::NW, MKQ, BIAS>(p, bid - nkv_pad);
 }
 
 // dK = scale * (half 0 + half 1), dV = half 0 + half 1, rounded to bf16; 8
@@ -916,19 +919,26 @@ hipError_t launch_dkdv_rest(const Params& p, bool split, hipStream_t stream) {
   return hipSuccess;
 }
 
-// dK/dV and dQ as one grads_kernel launch, when both take 512-thread
-// workgroups (enough query rows for the 8-wave dQ kernel) and both have work;
-// sets `done`.  Otherwise leaves `done` false and launches nothing.
+// dK/dV and dQ as one grads_kernel launch (workgroups of the dK/dV kernel's
+// size: 8 waves at D = 128, 4 at D <= 64, where only split key blocks take
+// it), when there are enough query rows for 8-wave dQ workgroups and both
+// have work; sets `done`.  Otherwise leaves `done` false and launches
+// nothing.
 template <int D>
 hipError_t launch_grads(const Params& p, hipStream_t stream, bool& done) {
   done = false;
   {
     using LD = KvSplit<D>;
     const int nkeys = walk_keys(p);
-    const int64_t ndq = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
+    const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
+    const int64_t ndq = (int64_t)p.B * p.Hq * ((p.Sq + LD::NW * 32 - 1) / (LD::NW * 32));
     const bool split = dkdv_split(p.B, p.Hkv, nkeys);
     const int64_t nkv = (int64_t)p.B * p.Hkv * (split ? 2 : 1) * ((nkeys + LD::TKW - 1) / LD::TKW);
-    if (ndq < 512 || nkv == 0) return hipSuccess;
+    if (wg8 < 512 || nkv == 0) return hipSuccess;
+    // D <= 64: only split key blocks (few of them, long dK/dV tails) gain from
+    // sharing the launch with dQ; with many blocks the 8-wave dQ launched on
+    // its own is faster than the 4-wave dQ the merged launch would take
+    if (D <= 64 && !split) return hipSuccess;
     const int64_t nkv_pad = (nkv + 7) / 8 * 8;
     if (nkv_pad + ndq > INT_MAX) return hipSuccess;
     const int mk = mask_instance(p.mask.kind);
@@ -943,7 +953,7 @@ hipError_t launch_grads(const Params& p, hipStream_t stream, bool& done) {
     const int lds = LD::BYTES > lq ? LD::BYTES : lq;
     hipError_t e;
     if ((e = set_lds(k, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3((unsigned)(nkv_pad + ndq)), dim3(512), lds, stream, p, (int)nkv, (int)nkv_pad);
+    hipLaunchKernelGGL(k, dim3((unsigned)(nkv_pad + ndq)), dim3(LD::NW * 64), lds, stream, p, (int)nkv, (int)nkv_pad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     done = true;
     return launch_dkdv_rest<D>(p, split, stream);
@@ -991,6 +1001,8 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
   }
   if (stage == STAGE_DQ && p.B > 0 && p.Sq > 0) {
     // 8-wave workgroups when there are enough to fill the chip twice over
+    // (each wave's rows get the same arithmetic in either size, so the
+    // one-launch backward's dQ blocks, 4-wave at D <= 64, match bitwise)
     const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
     const int mk = mask_instance(p.mask.kind);
     auto pick = [&](auto bc) {
