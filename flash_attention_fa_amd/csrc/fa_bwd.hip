@@ -400,9 +400,9 @@ dq_dma_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV with asynchronous staging.  A workgroup owns 256 keys of
-// one (batch, kv head) and one half of their (query tile, head) steps; wave
-// w owns keys 32w .. 32w+31 outright.  Its K rows stay in registers (the B
+// dK/dV with asynchronous staging.  A workgroup owns NW * 32 keys (256 at
+// D = 128, 128 at D <= 64) of one (batch, kv head) and one half of their
+// (query tile, head) steps; wave w owns keys 32w .. 32w+31 outright.  Its K rows stay in registers (the B
 // operand of S = Q K^T, natural orientation, a lane per key column); the
 // workgroup's V rows sit in LDS.  Each step stages one 64-row query tile of
 // one head (Q, dO, LSE*log2(e), Delta), worked through as two 32-row
@@ -413,9 +413,10 @@ dq_dma_kernel(Params p) {
 // tiles with transposing LDS reads.  Rows past Sq are copied from the tile's
 // first row (finite) and masked.
 //
-// 256 keys per workgroup let each staged query row serve twice the matrix
-// work of a 128-key block (the copies into LDS are the kernel's costliest
-// non-matrix work).  With fewer than 1024 such blocks (dkdv_split), each
+// At D = 128, 256 keys per workgroup let each staged query row serve twice
+// the matrix work of a 128-key block (the copies into LDS are the kernel's
+// costliest non-matrix work).  With fewer than 1024 blocks of 256 keys
+// (dkdv_split, whatever the workgroup's own size), each
 // block's steps are split between two workgroups, which keeps enough
 // workgroups to balance the causal triangle (the halves are the two halves
 // of the group's heads, or of the steps when the group is odd); each half
@@ -450,7 +451,8 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;         // rows per copy instruction
   constexpr int QINS = TQ / RPI;        // copy instructions per Q (or dO) tile
-  // per copying wave per step (at D = 16 the 4 copies take 4 of the 8 waves)
+  // per copying wave per step (at D = 16 with 8 waves the 4 copies would take
+  // 4 of them)
   constexpr int QLPW = 2 * QINS >= NW ? 2 * QINS / NW : 1;
   constexpr int VINS = TKW / RPI;       // copy instructions for the V rows
   constexpr int VLPW = VINS / NW;

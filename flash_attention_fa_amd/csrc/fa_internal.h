@@ -46,11 +46,12 @@ struct Params {
                        // (forward) or the Delta stage (backward)
 };
 
-// The bf16 dK/dV kernel owns 256-key blocks.  With fewer than
-// 1024 blocks it splits each block's query steps between two workgroups
+// The bf16 dK/dV kernel's split decision counts 256-key blocks (its
+// workgroups own 256 keys at D = 128, 128 at D <= 64).  With fewer than 1024
+// such blocks it splits each workgroup's query steps between two workgroups
 // (so the causal triangle still balances over the chip), which then need
-// float32 partial sums in the workspace and a reduction; with more, every
-// workgroup takes all steps of its block and writes dK, dV itself.
+// float32 partial sums (per key) in the workspace and a reduction; with more,
+// every workgroup takes all steps of its block and writes dK, dV itself.
 constexpr int kDkdvKeys = 256;
 inline bool dkdv_split(int B, int Hkv, int keys) {
   const int64_t nkt = ((int64_t)keys + kDkdvKeys - 1) / kDkdvKeys;
