@@ -1002,10 +1002,15 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
     }
   }
   if (stage == STAGE_DQ && p.B > 0 && p.Sq > 0) {
-    // 8-wave workgroups when there are enough to fill the chip twice over
-    // (each wave's rows get the same arithmetic in either size, so the
-    // one-launch backward's dQ blocks, 4-wave at D <= 64, match bitwise)
-    const int64_t wg8 = (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
+    // 8-wave workgroups when there are enough to fill the chip twice over,
+    // except at D <= 64 under a causal, TTT or window mask: there workgroups
+    // carry unequal work and 4-wave ones (two per compute unit, as in the
+    // forward) balance it better; under FULL every workgroup is alike and
+    // the 8-wave one was faster.  Each wave's rows get the same arithmetic in
+    // either size, so results do not depend on it (the one-launch backward's
+    // dQ blocks take the dK/dV kernel's size).
+    const bool small = D <= 64 && p.mask.kind != MASK_FULL;
+    const int64_t wg8 = small ? 0 : (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
     const int mk = mask_instance(p.mask.kind);
     auto pick = [&](auto bc) {
       constexpr bool BI = decltype(bc)::value;
