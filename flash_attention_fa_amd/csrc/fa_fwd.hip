@@ -31,13 +31,15 @@
 // recomputed.  LDS addresses are lane constants plus immediates: the loop is
 // unrolled over the four ring buffers.
 //
-// Pipeline.  Four LDS buffers hold tiles i .. i+3.  K and V^T rows are copied
-// HBM -> LDS asynchronously (no registers, no vector instructions) three tiles
-// ahead; iteration i issues the QK^T products of tile i+1, then the
+// Pipeline.  Iteration i issues the QK^T products of tile i+1, then the
 // exponentials of tile i (independent of those products, so the matrix cores
 // and the vector ALUs work at once), then the PV products of tile i; the mask
-// of tile i+1 (partial tiles only) closes the iteration.  One barrier per
-// tile, which waits only for the copies of tile i+2.
+// of tile i+1 (partial tiles only) closes the iteration.  K and V^T rows are
+// copied HBM -> LDS asynchronously (no registers, no vector instructions)
+// into a ring of four K and four V^T buffers.  Iterations go in pairs with
+// one barrier per pair: the first of a pair copies what the next pair reads
+// (K rows of tiles i+3, i+4, V^T rows of i+2, i+3: K runs a tile ahead of
+// V^T because QK^T does), into buffers the previous pair finished with.
 #include <algorithm>
 #include <type_traits>
 
@@ -211,14 +213,9 @@ fwd_kernel(Params p) {
 #pragma unroll
   for (int x = 0; x < LPW; ++x) voff[x] = 2u * (unsigned)(rstep[x] + rbase + cofs[x]);
   const bool soff_ok = p.k.ss >= 0;
-  // With a key bias the last wave also copies the tile's 64 scaled bias
-  // values (lanes 16..63 repeat lanes 0..15; the slot is 1 KB).
-  const bool bias_wave = has_bias && wave == NW - 1;
   auto copy_tiles = [&](int t, int k) __attribute__((always_inline)) {
     const int tb = t * TK;
     const unsigned lbuf = lds0 + k * L::TILE_BYTES;
-    if (bias_wave)
-      lds_dma16_at(Bsg + (t >= 0 ? tb : 0) + 4 * (lane & 15), lds0 + L::BIAS_BASE + k * 1024);
     if (soff_ok && t >= 0 && tb + TK <= m.kvv) {
       const bf16* sbase = wk ? Kg + (int64_t)tb * p.k.ss : VTg + tb;
 #pragma unroll
@@ -240,13 +237,11 @@ fwd_kernel(Params p) {
       }
     }
   };
-  // Waits until this wave's copies of all but the newest tile have landed.
-  const int my_ins = (ALL_COPY ? LPW : (wave * LPW < 2 * NINS ? LPW : 0)) + (bias_wave ? 1 : 0);
-  auto wait_copies = [&]() __attribute__((always_inline)) {
-    if (my_ins == LPW) wait_vmcnt<LPW>();
-    else if (my_ins == LPW + 1) wait_vmcnt<LPW + 1>();
-    else if (my_ins == 1) wait_vmcnt<1>();
-    else wait_vmcnt<0>();
+  // With a key bias the last wave also copies each tile's 64 scaled bias
+  // values into slot k (lanes 16..63 repeat lanes 0..15; the slot is 1 KB).
+  const bool bias_wave = has_bias && wave == NW - 1;
+  auto copy_bias = [&](int t, int k) __attribute__((always_inline)) {
+    if (bias_wave) lds_dma16_at(Bsg + (t >= 0 ? t * TK : 0) + 4 * (lane & 15), lds0 + L::BIAS_BASE + k * 1024);
   };
   // Where the scores of the tile in buffer k start: the scaled bias of their
   // keys (register i of key block kb holds key 32 kb + 8 (i / 4) + 4 hh +
@@ -420,23 +415,39 @@ fwd_kernel(Params p) {
   segment_tiles(m, 0, qa, qb, TK, t, tend);
   auto tile_or_none = [&](int u) __attribute__((always_inline)) { return u < tend ? u : -1; };
 
+  // Ring buffers: tile t of the walk sits in buffer (t - t0) mod 4.  K rows
+  // (and the bias) are read one iteration before V^T rows (QK^T of tile i+1
+  // runs with PV of tile i), so they are copied one tile further ahead.
   f32x16 scur[2], snxt[2];
   if (t < tend) {
-    copy_tiles(t, 0);
-    copy_tiles(tile_or_none(t + 1), 1);
-    copy_tiles(tile_or_none(t + 2), 2);
-    wait_copies();
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {   // K rows of tiles t .. t+2, V^T rows of t, t+1
+      if (wk || u < 2) copy_tiles(tile_or_none(t + u), u);
+      copy_bias(tile_or_none(t + u), u);
+    }
+    wait_vmcnt<0>();
   }
   barrier_lds();
   if (t < tend) {
     qk(Buf<0>{}, scur);
     mask(t, scur);
   }
+  barrier_lds();   // the first pair's copies refill K buffer 0
 
   // One iteration with tile i in buffer k; false when the walk has ended.
+  // Iterations go in pairs with one barrier per pair: the first of a pair
+  // issues the copies the next pair reads (K rows and bias of tiles i+3,
+  // i+4, V^T rows of i+2, i+3, into the buffers the previous pair finished
+  // with), the second waits for them and closes the pair with the barrier.
   auto step = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    copy_tiles(tile_or_none(t + 3), (k + 3) & (NBUF - 1));
+    if constexpr ((k & 1) == 0) {
+      const int a = wk ? 3 : 2;
+      copy_tiles(tile_or_none(t + a), (k + a) & (NBUF - 1));
+      copy_tiles(tile_or_none(t + a + 1), (k + a + 1) & (NBUF - 1));
+      copy_bias(tile_or_none(t + 3), (k + 3) & (NBUF - 1));
+      copy_bias(tile_or_none(t + 4), k);
+    }
     // QK^T of tile i+1 (its buffer may hold a stale tile at the end: unused)
     // with the exponentials of tile i spread between its products (they are
     // independent: matrix cores and vector ALUs overlap).
@@ -449,8 +460,10 @@ fwd_kernel(Params p) {
     lsum += ls;
     pv(kc, pb);
     if (t + 1 < tend) mask(t + 1, snxt);
-    wait_copies();
-    barrier_lds();
+    if constexpr ((k & 1) == 1) {
+      wait_vmcnt<0>();
+      barrier_lds();
+    }
     scur[0] = snxt[0];
     scur[1] = snxt[1];
     return ++t < tend;
