@@ -39,10 +39,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Running max starts here instead of -inf so exp2(x - m) never sees
 // (-inf) - (-inf); any finite score exceeds it and triggers a rescale.
 constexpr float kMaxInit = -1.0e30f;
-// Rescale the accumulators only when a row max grows by more than this many
-// powers of two; the stale max keeps every exp2 argument <= kRescaleSlack, so
-// P stays <= 2^8 and the final O / l, LSE are unchanged.
-constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -26,10 +26,13 @@
 // (scale and running max), the exp2, half a bf16 pack and half a two-way dot
 // product that sums the packed P for the normaliser (so l sums exactly the P
 // the PV product uses).  No per-tile row max is taken: P is computed against
-// the running max and only when some row's tile sum exceeds kSumLimit (which
-// bounds every P in it) is the true max taken, O^T and l rescaled and P
-// recomputed.  LDS addresses are lane constants plus immediates: the loop is
-// unrolled over the four ring buffers.
+// a reference kSlack above a stale row max and saturated at 1 (the exp2's
+// clamp bit, no extra instruction), so it is bounded before anything is
+// checked and the PV products follow the exponentials in one stretch of code.
+// Only when some row's tile sum reaches 1 (which any saturated P forces) is
+// the true max taken, after the PV products, and the tile corrected (fixup).
+// LDS addresses are lane constants plus immediates: the loop is unrolled over
+// the four ring buffers.
 //
 // Pipeline.  Iteration i issues the QK^T products of tile i+1, then the
 // exponentials of tile i (independent of those products, so the matrix cores
@@ -51,9 +54,23 @@ namespace {
 constexpr int TK = 64;    // keys per LDS tile
 static_assert(TK == kVtTile, "the V^T workspace is laid out in forward key tiles");
 constexpr int NBUF = 4;   // tiles in flight in LDS
-// A tile's per-row sum of P above this bound triggers the running-max refresh
-// (every P of the row is below it, so nothing overflows before the check).
+// The running max is lazy: P = exp2(x - mref), x the scaled score in log2
+// units, against a reference mref that moves only when a tile's P grows too
+// large.  At D >= 64 (LATE) mref sits kSlack above a row max and P saturates
+// at 1: every P is bounded before anything is checked, the PV products run
+// first, and a row whose P could have saturated (lane's tile sum >= 1) is
+// corrected afterwards (fixup); the common 2^-kSlack factor of P cancels in
+// O = acc / l and returns in the LSE through mref.  At D <= 32 mref is a row
+// max and a lane's tile sum above kSumLimit = 2^kSlack (which bounds every P
+// in it) rescales O and l and recomputes P before the PV products (refresh):
+// the late correction keeps the scores live through the PV products, which
+// at these D costs a wave per SIMD.
+constexpr float kSlack = 12.0f;
 constexpr float kSumLimit = 4096.0f;
+
+__device__ __forceinline__ float exp2_sat(float x) {
+  return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x), 0.0f, 1.0f);
+}
 
 // LDS: the NBUF K tiles (64 swizzled rows of D), then the NBUF V^T tiles (D
 // swizzled rows of 64 keys), so every operand address of a ring buffer is a
@@ -85,6 +102,8 @@ template <int D, int NW, int MK, bool BIAS>
 __global__ void __launch_bounds__(NW * 64, 2)
 fwd_kernel(Params p) {
   constexpr bool TTT = MK == MK_TTT;
+  constexpr bool LATE = D >= 64;
+  constexpr float SLACK = LATE ? kSlack : 0.0f;
   constexpr int TQ = NW * 32;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;              // rows per 1 KB copy instruction
@@ -135,8 +154,9 @@ fwd_kernel(Params p) {
 
   if constexpr (TTT) {
     // ttt_fold: key s*L + i of each later step s, one per row, with the exact
-    // running max (no lazy bound here), before the tile loop (the order of
-    // the keys does not change the result).  The score's two lane halves each
+    // running max (plus the tile loop's slack) and no lazy bound,
+    // before the tile loop (the order of the keys does not change the
+    // result).  The score's two lane halves each
     // hold half of q_i.k (the d of qreg), summed across the halves; O^T
     // takes p * V row in the lane's own d positions.  Rows that are not real
     // or not below kv_valid take score -inf, which leaves O, l and the max
@@ -154,7 +174,7 @@ fwd_kernel(Params p) {
       for (int jj = 0; jj < NJ; ++jj) dot = dot_bf16x8(qreg[jj], *reinterpret_cast<const bf16x8*>(kr + 16 * jj), dot);
       dot = half_swap_sum(dot);
       const float x = rok ? (dot + (has_bias ? Bsg[j] : 0.f)) * p.scale_log2 : -INFINITY;
-      const float mn = fmaxf(mrun, x);
+      const float mn = fmaxf(mrun, x + SLACK);
       const float alpha = exp2_fast(mrun - mn);
       const float pr = exp2_fast(x - mn);
       mrun = mn;
@@ -319,22 +339,6 @@ fwd_kernel(Params p) {
       if (n + PF < NOP) sched_group(SCHED_DS_READ, 1);
     }
   };
-  // P of a tile against the running max, rounded to bf16, and its row sum
-  // over the rounded values (two-way dot products with ones).
-  auto softmax = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float e[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) e[u] = exp2_fast(s[kb][8 * st + u] * p.scale_log2 - mrun);
-        pb[kb][st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
-        ls = sum_bf16x8(pb[kb][st], ls);
-      }
-    return ls;
-  };
   // qk() and softmax() interleaved in program order: after product n come
   // the exponentials of score registers 2n and 2n+1 of the other tile.
   auto qk_softmax = [&](auto kc, f32x16 (&s)[2], const f32x16 (&sp)[2], bf16x8 (&pb)[2][2])
@@ -360,7 +364,8 @@ fwd_kernel(Params p) {
       for (int x = 0; x < 32 / (2 * NJ); ++x) {
         const int idx = n * (32 / (2 * NJ)) + x;   // 0..31: (kb', st', u)
         const int kb2 = idx >> 4, st2 = (idx >> 3) & 1, u = idx & 7;
-        e[kb2][st2][u] = exp2_fast(sp[kb2][8 * st2 + u] * p.scale_log2 - mrun);
+        const float arg = sp[kb2][8 * st2 + u] * p.scale_log2 - mrun;
+        e[kb2][st2][u] = LATE ? exp2_sat(arg) : exp2_fast(arg);
         if (u == 7) {
           pb[kb2][st2] = cat8(to_bf16x4(e[kb2][st2][0], e[kb2][st2][1], e[kb2][st2][2], e[kb2][st2][3]),
                               to_bf16x4(e[kb2][st2][4], e[kb2][st2][5], e[kb2][st2][6], e[kb2][st2][7]));
@@ -370,16 +375,35 @@ fwd_kernel(Params p) {
     }
     return ls;
   };
-  // Running-max refresh from a tile's scores (rare): O^T and l move to the
-  // new max.
-  auto refresh = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
+  // !LATE: P of a tile against the running max, rounded to bf16, and its row
+  // sum over the rounded values (two-way dot products with ones).
+  auto softmax = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) e[u] = exp2_fast(s[kb][8 * st + u] * p.scale_log2 - mrun);
+        pb[kb][st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
+        ls = sum_bf16x8(pb[kb][st], ls);
+      }
+    return ls;
+  };
+  // Row max of a tile's scores, in log2 units (both lane halves).
+  auto tile_max = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
     float mx = s[0][0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    mx = half_swap_max(mx) * p.scale_log2;
-    const float mn = fmaxf(mrun, mx);
+    return half_swap_max(mx) * p.scale_log2;
+  };
+  // !LATE: running-max refresh from a tile's scores (rare): O^T and l move
+  // to the new max.
+  auto refresh = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
+    const float mn = fmaxf(mrun, tile_max(s));
     const float alpha = exp2_fast(mrun - mn);
     mrun = mn;
     lsum *= alpha;
@@ -387,6 +411,38 @@ fwd_kernel(Params p) {
     for (int c = 0; c < NDB; ++c)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[c][i] *= alpha;
+  };
+  // LATE: correction of a tile whose P may have saturated (rare: a row max
+  // that grew by more than kSlack, or a row with no allowed key before),
+  // after its PV products ran with Ps = min(1, exp2(x - mref)).  With mn = max(mref, row
+  // max + kSlack) and alpha = exp2(mref - mn): O^T and l are scaled by alpha,
+  // then the difference D = exp2(x - mn) - alpha * Ps goes through the PV
+  // product and into l, so the tile's weights become exp2(x - mn) (up to
+  // rounding) and l sums the same weights O^T holds.
+  auto fixup = [&](auto kc, const f32x16 (&s)[2], const bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+    const float mn = fmaxf(mrun, tile_max(s) + kSlack);
+    const float alpha = exp2_fast(mrun - mn);
+    lsum *= alpha;
+#pragma unroll
+    for (int c = 0; c < NDB; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[c][i] *= alpha;
+    bf16x8 db[2][2];
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float d[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          d[u] = exp2_fast(s[kb][8 * st + u] * p.scale_log2 - mn) - alpha * (float)pb[kb][st][u];
+        db[kb][st] = cat8(to_bf16x4(d[0], d[1], d[2], d[3]), to_bf16x4(d[4], d[5], d[6], d[7]));
+        ls = sum_bf16x8(db[kb][st], ls);
+      }
+    lsum += ls;
+    mrun = mn;
+    pv(kc, db);
   };
   // Mask of tile t (partial and skipped tiles only).
   // Tiles below full_end hold only keys every row of this wave may attend
@@ -431,6 +487,19 @@ fwd_kernel(Params p) {
   if (t < tend) {
     qk(Buf<0>{}, scur);
     mask(t, scur);
+    // The reference starts at (slack above) the first tile's row max, so only
+    // a later jump of the max needs a correction.  (After the TTT fold O^T and
+    // l already hold weights against the old reference.)
+    const float mn = fmaxf(mrun, tile_max(scur) + SLACK);
+    if constexpr (TTT) {
+      const float alpha = exp2_fast(mrun - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int c = 0; c < NDB; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[c][i] *= alpha;
+    }
+    mrun = mn;
   }
   barrier_lds();   // the first pair's copies refill K buffer 0
 
@@ -453,12 +522,19 @@ fwd_kernel(Params p) {
     // independent: matrix cores and vector ALUs overlap).
     bf16x8 pb[2][2];
     float ls = qk_softmax(Buf<(k + 1) & (NBUF - 1)>{}, snxt, scur, pb);
-    if (__any(!(ls <= kSumLimit))) {
-      refresh(scur);
-      ls = softmax(scur, pb);
+    if constexpr (LATE) {
+      lsum += ls;
+      pv(kc, pb);
+      // A P of 1 (saturated) makes its lane's sum at least 1.
+      if (__any(!(ls < 1.0f))) fixup(kc, scur, pb);
+    } else {
+      if (__any(!(ls <= kSumLimit))) {
+        refresh(scur);
+        ls = softmax(scur, pb);
+      }
+      lsum += ls;
+      pv(kc, pb);
     }
-    lsum += ls;
-    pv(kc, pb);
     if (t + 1 < tend) mask(t + 1, snxt);
     if constexpr ((k & 1) == 1) {
       wait_vmcnt<0>();

@@ -1,23 +1,34 @@
 """GPU parity on inputs that make the bf16 forward rescale live accumulators.
 
-The forward keeps a lazy running max per query row: P of a key tile is taken
-against the stored max m, and only when some lane's sum of P over its 32
-keys of the tile exceeds 4096 (= 2^12, so that no P can overflow first) does
-the wave take the true tile max, rescale O and l by alpha = exp(m_old - m_new)
-and recompute P.  This is the online-softmax update of CS336 "Flash Attention
-(Triton)" (How it works: the running max m and normaliser l, with the
-accumulated output rescaled when m grows).  With N(0, 1) inputs no tile after
-the first ever passes that bound, so the rescale of accumulators that already
-hold values is reached only by inputs built for it: the ``spike`` recipe of
-``workloads.make_stress_inputs`` (flat scores, then eight keys about 7 units
-higher in one lane half of one key tile, with the mean of V flipped on them).
+The forward keeps a lazy running max per query row (the online-softmax
+update of CS336 "Flash Attention (Triton)", How it works: the running max m
+and normaliser l, with the accumulated output rescaled when m grows).  P of a
+key tile is taken against a stored reference, and only when some lane's sum
+of P over its 32 keys of the tile passes a bound does the wave take the true
+tile max and rescale O and l.  Two forms, by head dim:
+
+- D <= 32: the reference is a row max, the bound 4096 (= 2^12, so no P can
+  overflow first); O and l are rescaled and P recomputed before the PV
+  products.
+- D >= 64: the reference is 2^12 above a row max and P saturates at 1, so
+  the bound is a lane sum of 1; the PV products run first and the tile is
+  corrected after them (O, l scaled by alpha = exp(m_old - m_new), then
+  the difference between the new and the used P goes through the PV
+  product).
+
+With N(0, 1) inputs no tile after the first ever passes either bound, so the
+rescale of accumulators that already hold values is reached only by inputs
+built for it: the ``spike`` recipe of ``workloads.make_stress_inputs`` (flat
+scores, then eight keys about 7 units higher in one lane half of one key
+tile, with the mean of V flipped on them).
 
 Before any GPU call, ``guaranteed_live_refreshes`` proves from the inputs
 alone (fp64, on the CPU) that the branch is reached: the lazy max is never
 above the true running max M of the keys a row has seen, so a lane whose
 half-tile sum of exp(s - M) exceeds 4096 (with 5 % slack for rounding)
-certainly triggers the refresh, and with M finite the row's accumulators are
-live.  The test also requires that these rows carry at least 20 % of their
+certainly triggers the refresh (at D >= 64 its sum of min(1, exp(s - m -
+ln 4096)) with m <= M is then at least 1), and with M finite the row's
+accumulators are live.  The test also requires that these rows carry at least 20 % of their
 softmax mass in the rescaled accumulators and that V's mean differs in sign
 between the keys before and at the spike, so a mistake in the rescale moves
 O by a large fraction of max|O| and cannot pass the 2e-2 bar.
@@ -120,7 +131,7 @@ CASES = [
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_bf16_rescale_four_wave(case, D):
     """4-wave forward (128 query rows per workgroup: few workgroups), GQA."""
