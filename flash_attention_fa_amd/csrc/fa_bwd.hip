@@ -62,22 +62,27 @@ __global__ void __launch_bounds__(256) delta_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // dQ with asynchronous staging: the forward's pipeline with a third
 // product.  Key tiles of K and V rows are copied HBM -> LDS into a ring of
-// four XOR-swizzled buffers three tiles ahead; per tile, S^T = K Q^T and
+// four XOR-swizzled buffers three tiles ahead (three buffers, two ahead, at
+// D = 64); per tile, S^T = K Q^T and
 // dP^T = V dO^T (Q and dO in registers, K and V rows from LDS), dS^T =
 // P^T (dP^T - Delta) with P^T = exp2(scale log2(e) S^T - LSE log2(e)), and
 // dQ^T += K^T dS^T with K^T read transposed from the row-major K tile.
 constexpr int DQ_TK = 64;     // keys per LDS tile
-constexpr int DQ_NBUF = 4;
 
-// With a key bias, DQ_NBUF 1 KB slots follow: each tile's 64 scaled bias
-// values (256 bytes; the copy instruction that brings them writes 1 KB).
+// The ring holds NBUF tiles, copied NBUF - 1 tiles ahead: four, except at
+// D = 64, where three (48 KB) let three 4-wave workgroups share a compute
+// unit (the kernel's 166 registers allow three waves per SIMD; a 64 KB ring
+// allowed two workgroups).  With a key bias, NBUF 1 KB slots follow: each
+// tile's 64 scaled bias values (256 bytes; the copy instruction that brings
+// them writes 1 KB).
 template <int D>
 struct DqDma {
+  static constexpr int NBUF = D == 64 ? 3 : 4;   // tiles in the ring
   static constexpr int TILE = DQ_TK * D * 2;   // K or V rows of one tile
   static constexpr int BUF = 2 * TILE;
-  static constexpr int BYTES = DQ_NBUF * BUF;
+  static constexpr int BYTES = NBUF * BUF;
   static constexpr int BIAS_BASE = BYTES;
-  static constexpr int BIAS_BYTES = DQ_NBUF * 1024;
+  static constexpr int BIAS_BYTES = NBUF * 1024;
 };
 
 // MK: the mask-kind instance.  As in the forward, the MK_TTT tile loop walks
@@ -268,17 +273,18 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
   int t, tend;
   segment_tiles(m, 0, qa, qb, TK, t, tend);
   auto tile_or_none = [&](int u) __attribute__((always_inline)) { return u < tend ? u : -1; };
+  constexpr int NB = L::NBUF;
   if (t < tend) {
     copy_tile(t, 0);
     copy_tile(tile_or_none(t + 1), 1);
-    copy_tile(tile_or_none(t + 2), 2);
+    if constexpr (NB == 4) copy_tile(tile_or_none(t + 2), 2);
     wait_copies();
   }
   barrier_lds();
 
   auto step = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    copy_tile(tile_or_none(t + 3), (k + 3) % DQ_NBUF);
+    copy_tile(tile_or_none(t + NB - 1), (k + NB - 1) % NB);
     const int k0 = t * TK;
     const int state = t < full_end ? TILE_FULL : tile_state(m, k0, TK, wa, wb);
     if (state != TILE_SKIP) {
@@ -373,7 +379,12 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
     return ++t < tend;
   };
   if (t < tend) {
-    while (step(Buf<0>{}) && step(Buf<1>{}) && step(Buf<2>{}) && step(Buf<3>{})) {
+    if constexpr (NB == 4) {
+      while (step(Buf<0>{}) && step(Buf<1>{}) && step(Buf<2>{}) && step(Buf<3>{})) {
+      }
+    } else {
+      while (step(Buf<0>{}) && step(Buf<1>{}) && step(Buf<2>{})) {
+      }
     }
   }
   wait_vmcnt<0>();   // copies of tiles past the end
@@ -780,8 +791,11 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
   }
 }
 
+// At D = 64 (without a key bias) the kernel fits 170 registers, so three
+// waves share a SIMD: three 4-wave workgroups (49 KB of LDS each) per compute
+// unit.  With a bias the extra registers would spill there.
 template <int D, int MK, bool SPLIT, bool BIAS>
-__global__ void __launch_bounds__(KvSplit<D>::NW * 64, 2)
+__global__ void __launch_bounds__(KvSplit<D>::NW * 64, D == 64 && !BIAS ? 3 : 2)
 dkdv_split_kernel(Params p) {
   dkdv_split_body<D, MK, SPLIT, BIAS>(p, blockIdx.x);
 }
@@ -1003,13 +1017,15 @@ hipError_t launch_stage(const Params& p, int stage, hipStream_t stream) {
   }
   if (stage == STAGE_DQ && p.B > 0 && p.Sq > 0) {
     // 8-wave workgroups when there are enough to fill the chip twice over,
-    // except at D <= 64 under a causal, TTT or window mask: there workgroups
-    // carry unequal work and 4-wave ones (two per compute unit, as in the
-    // forward) balance it better; under FULL every workgroup is alike and
-    // the 8-wave one was faster.  Each wave's rows get the same arithmetic in
-    // either size, so results do not depend on it (the one-launch backward's
-    // dQ blocks take the dK/dV kernel's size).
-    const bool small = D <= 64 && p.mask.kind != MASK_FULL;
+    // except at D = 64, and at D <= 32 under a causal, TTT or window mask:
+    // there workgroups carry unequal work and 4-wave ones (several per
+    // compute unit, as in the forward) balance it better; at D = 64 three of
+    // them share a compute unit (the 48 KB ring), under FULL too.  At D <= 32
+    // under FULL every workgroup is alike and the 8-wave one was faster.
+    // Each wave's rows get the same arithmetic in either size, so results do
+    // not depend on it (the one-launch backward's dQ blocks take the dK/dV
+    // kernel's size).
+    const bool small = D == 64 || (D <= 32 && p.mask.kind != MASK_FULL);
     const int64_t wg8 = small ? 0 : (int64_t)p.B * p.Hq * ((p.Sq + 255) / 256);
     const int mk = mask_instance(p.mask.kind);
     auto pick = [&](auto bc) {
