@@ -11,7 +11,10 @@ Prints one JSON line: the metric, the per-step time, fwd / bwd / fwd+bwd
 TFLOP/s and their fraction of the 2516.6 TFLOP/s dense bf16 peak, the time of
 each kernel, the roofline of the dominant kernel (the dK/dV stage), the peak
 device memory, and the fp64 oracle timed on a bounded sample of the same
-workload on the host CPU.  The timed step is fa_fwd then fa_bwd, as a caller
+workload on the host CPU, and (``platform_gemm``) a dense bf16 GEMM through
+the vendor BLAS timed on the same box after the steps: the practical rate of
+the matrix cores there, which the kernels' fractions can be read against.
+The timed step is fa_fwd then fa_bwd, as a caller
 runs them (fa_bwd launches Delta, then dK/dV and dQ as one kernel where the
 shapes allow); the per-kernel times come from further steps, outside the
 timed ones, that launch the backward's three stages one by one
@@ -181,6 +184,31 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n}), flush=True)
     return 0
+
+
+def gemm_reference(dev, n=8192, reps=20, rounds=3):
+    """A dense n^3 bf16 GEMM through the vendor BLAS (torch.matmul, hipBLASLt on
+    ROCm) on this machine: the practical dense-MFMA rate the attention kernels'
+    fraction of the peak can be read against.  Context only; no part of the
+    attention path uses it."""
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev, generator=g)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev, generator=g)
+    for _ in range(5):
+        c = a @ b
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    ms = float(np.median(times))
+    del a, b, c
+    return ms, 2.0 * n ** 3 / (ms * 1e-3) / 1e12
 
 
 def find_workload(name):
@@ -509,6 +537,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=2,
                     help="query heads of batch 0 the oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the vendor-BLAS bf16 GEMM timed for context after the steps")
     ap.add_argument("--sweep", action="store_true",
                     help="time every named workload, one JSON line each, and exit")
     ap.add_argument("--loss", action="store_true",
@@ -595,6 +625,17 @@ def main():
         "runs": runs_summary(r, f_fwd, f_bwd, tf),
         "clock": clock_summary(r["clock"], value),
     }
+    if not a.no_gemm_reference:
+        g_ms, g_tf = gemm_reference(dev)
+        out["platform_gemm"] = {
+            "what": "8192^3 bf16 GEMM through the vendor BLAS (torch.matmul) on this box, timed after "
+                    "the attention steps (median of 3 runs of 20): the practical dense-MFMA rate, "
+                    "context only",
+            "ms": round(g_ms, 4), "tflops": round(g_tf, 1),
+            "pct_of_peak": round(100 * g_tf / PEAK_BF16_TFLOPS, 2),
+            "fwd_over_gemm": round(tf(f_fwd, fwd_med) / g_tf, 3),
+            "dkdv_over_gemm": round(dkdv_tf / g_tf, 3),
+            "step_over_gemm": round(value / g_tf, 3)}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, a.cpu_heads)
     print(json.dumps(out), flush=True)
