@@ -186,7 +186,7 @@ def copy_calibration():
     return 0
 
 
-def gemm_reference(dev, n=8192, reps=20, rounds=3):
+def gemm_reference(dev, n=8192, reps=60, rounds=5):
     """A dense n^3 bf16 GEMM through the vendor BLAS (torch.matmul, hipBLASLt on
     ROCm) on this machine: the practical dense-MFMA rate the attention kernels'
     fraction of the peak can be read against.  Context only; no part of the
@@ -629,7 +629,7 @@ def main():
         g_ms, g_tf = gemm_reference(dev)
         out["platform_gemm"] = {
             "what": "8192^3 bf16 GEMM through the vendor BLAS (torch.matmul) on this box, timed after "
-                    "the attention steps (median of 3 runs of 20): the practical dense-MFMA rate, "
+                    "the attention steps (median of 5 runs of 60): the practical dense-MFMA rate, "
                     "context only",
             "ms": round(g_ms, 4), "tflops": round(g_tf, 1),
             "pct_of_peak": round(100 * g_tf / PEAK_BF16_TFLOPS, 2),
