@@ -98,8 +98,11 @@ struct Buf {
 // of a 64-key tile per step that holds one key per row, each lane folds its
 // row's keys into the running max, normaliser and O before the tile loop
 // (ttt_fold).
+// At D = 16 (4-wave workgroups, no key bias) the kernel is bounded to 128
+// registers, so four waves share a SIMD; at D = 32 the same bound would
+// spill many registers.
 template <int D, int NW, int MK, bool BIAS>
-__global__ void __launch_bounds__(NW * 64, 2)
+__global__ void __launch_bounds__(NW * 64, D == 16 && NW == 4 && !BIAS ? 4 : 2)
 fwd_kernel(Params p) {
   constexpr bool TTT = MK == MK_TTT;
   constexpr bool LATE = D >= 64;
