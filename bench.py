@@ -534,7 +534,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=W.HEADLINE.name)
-    ap.add_argument("--cpu-heads", type=int, default=2,
+    ap.add_argument("--cpu-heads", type=int, default=3,
                     help="query heads of batch 0 the oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-reference", action="store_true",
