@@ -435,8 +435,9 @@ dq_dma_kernel(Params p) {
 // two halves, always half 0 + half 1, so reruns are bitwise identical.
 // With more blocks one workgroup takes every step of its block and writes
 // dK and dV directly.
-// D <= 64: 4-wave workgroups of 128 keys (two share a compute unit, so one's
-// per-step barrier does not idle all of its waves); D = 128: 8 waves, 256 keys.
+// D <= 64: 4-wave workgroups of 128 keys (two or more share a compute unit,
+// so one's per-step barrier does not idle all of its waves; three at D = 64,
+// see dkdv_split_kernel); D = 128: 8 waves, 256 keys.
 template <int D>
 struct KvSplit {
   static constexpr int NW = D <= 64 ? 4 : 8;
