@@ -302,10 +302,11 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
       constexpr int PF = 3;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // Raised issue priority while this wave forms S, dP and dS: its
-        // exponentials issue ahead of the other wave's vector work while
-        // that wave's dQ products keep the matrix cores busy.
-        __builtin_amdgcn_s_setprio(1);
+        // At D >= 64, raised issue priority while this wave forms S, dP and
+        // dS: its exponentials issue ahead of the other wave's vector work
+        // while that wave's dQ products keep the matrix cores busy (at
+        // D <= 32 it was slower).
+        if constexpr (D >= 64) __builtin_amdgcn_s_setprio(1);
         // dP^T accumulates onto -Delta (the lane's row), so it comes out as
         // dP^T - Delta; S^T onto the scaled bias of each register's key
         // (32 kb + 8 (i / 4) + 4 hh + i % 4 of the tile), or zero.
@@ -370,7 +371,7 @@ __device__ __forceinline__ void dq_dma_body(const Params& p, int bid) {
           }
           dsb[st] = cat8(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]));
         }
-        __builtin_amdgcn_s_setprio(0);
+        if constexpr (D >= 64) __builtin_amdgcn_s_setprio(0);
         // dQ^T += K^T dS^T, K^T read transposed from the K rows.
 #pragma unroll
         for (int n = 0; n < NDQ; ++n) {
@@ -675,10 +676,10 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
       if (state == TILE_FULL && qa + 32 > p.Sq) state = TILE_PART;   // rows past Sq
     }
     if (state != TILE_SKIP) {
-      // At D <= 64 (vector work per score as at D = 128, half the products)
-      // the wave raises its issue priority while it forms S, dP, P and dS,
-      // as the forward and dQ kernels do; at D = 128 that was slower.
-      if constexpr (D <= 64) __builtin_amdgcn_s_setprio(1);
+      // At D = 64 the wave raises its issue priority while it forms S, dP,
+      // P and dS, as the forward and dQ kernels do; at D = 128 and at
+      // D <= 32 that was slower.
+      if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
       // dP accumulates onto -Delta of each register's row (q = qa + 8*(i/4) +
       // 4*hh + i%4), so it comes out as dP - Delta.
       f32x16 s, dp;
@@ -728,7 +729,7 @@ __device__ __forceinline__ void dkdv_split_body(const Params& p, int bid) {
         pb[st] = cat8(to_bf16x4(pe[0], pe[1], pe[2], pe[3]), to_bf16x4(pe[4], pe[5], pe[6], pe[7]));
         dsb[st] = cat8(to_bf16x4(de[0], de[1], de[2], de[3]), to_bf16x4(de[4], de[5], de[6], de[7]));
       }
-      if constexpr (D <= 64) __builtin_amdgcn_s_setprio(0);
+      if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
       // dV^T += dO^T P,  dK^T += Q^T dS: A operands read transposed from the
       // row-major tiles (rows 16 st + (4 hh + r) and + 8, the order the score
       // registers hold the rows in).

@@ -523,13 +523,15 @@ fwd_kernel(Params p) {
     // QK^T of tile i+1 (its buffer may hold a stale tile at the end: unused)
     // with the exponentials of tile i spread between its products (they are
     // independent: matrix cores and vector ALUs overlap).
-    // The wave raises its issue priority for this phase: its exponentials
-    // then issue ahead of the other wave's vector work while that wave's
-    // PV products keep the matrix cores busy.
+    // At D = 128 the wave raises its issue priority for this phase: its
+    // exponentials then issue ahead of the other wave's vector work while
+    // that wave's PV products keep the matrix cores busy.  (At D <= 64,
+    // where the vector work per tile is as large as the matrix work, it was
+    // slower.)
     bf16x8 pb[2][2];
-    __builtin_amdgcn_s_setprio(1);
+    if constexpr (D == 128) __builtin_amdgcn_s_setprio(1);
     float ls = qk_softmax(Buf<(k + 1) & (NBUF - 1)>{}, snxt, scur, pb);
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (D == 128) __builtin_amdgcn_s_setprio(0);
     if constexpr (LATE) {
       lsum += ls;
       pv(kc, pb);
