@@ -10,7 +10,7 @@
 // O and LSE ever reach HBM (ggml flash-attn-training playbook, section 1).
 //
 // Work split.  A workgroup owns NW*32 query rows of one (batch, head); each
-// wave owns one block of 32 rows, two waves per SIMD.  Keys stream through
+// wave owns one block of 32 rows, two or more waves per SIMD.  Keys stream through
 // LDS in tiles of 64.  Scores are computed transposed, S^T = K Q^T, so each
 // lane owns one query column and 32 keys of it: the softmax scale, running
 // max and normaliser are one scalar per lane.  O^T = V^T P^T takes P straight
