@@ -626,7 +626,12 @@ def main():
         "clock": clock_summary(r["clock"], value),
     }
     if not a.no_gemm_reference:
-        g_ms, g_tf = gemm_reference(dev)
+        try:
+            g_ms, g_tf = gemm_reference(dev)
+        except Exception as e:   # context only: never lose the bench line over it
+            g_ms, g_tf = None, None
+            out["platform_gemm"] = {"error": f"{type(e).__name__}: {e}"}
+    if not a.no_gemm_reference and g_tf:
         out["platform_gemm"] = {
             "what": "8192^3 bf16 GEMM through the vendor BLAS (torch.matmul) on this box, timed after "
                     "the attention steps (median of 5 runs of 60): the practical dense-MFMA rate, "
